@@ -1,0 +1,209 @@
+"""Benchmark of the striped paged-attention hot path on one MI355X.
+
+One step = every stripe's partial (cp_paged_attn_partial over all P stripes, plus cp_own_token_attn for the mixed
+workload) followed by cp_lse_merge, over one batch whose inputs are already resident in HBM. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b] [--no-cpu-baseline]
+
+The default workload is the Llama-3-8B-shaped GQA decode (32 q heads, 8 kv heads, head dim 128, page 16, P = 4
+stripes, batch 64, context lengths uniform in [1024, 8192], bf16 with fp32 accumulation). `value` is KV GB/s:
+algorithmic KV bytes (every context token's K and V read once) per second of wall-clock step time.
+
+`roofline` describes the dominant kernel (the partial): algorithmic bytes per launch over its average duration,
+measured with HIP events on the stream it runs on, against the 8 TB/s HBM peak. `traffic` is the measured HBM
+traffic per launch from rocprofv3 counters, scaled by the counter/bytes ratio of a plain copy kernel (see
+``--copy-calibration`` and the profiles directory); it is only filled in when the counters were taken on the current
+kernel build.
+
+`cpu_baseline` is the float64 CPU oracle timed on host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# Counter-derived HBM traffic per partial launch for the default workload, from the rocprofv3 PMC runs recorded in
+# profiles/ (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel factor). Keyed by the kernel source hash it was
+# taken on; ignored (traffic = null) when the kernel source has changed since.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_llama8b.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "cp_slot_map_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "longctx", "mla", "mixed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for the counter scale factor) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the float64 oracle (stripe partials + exact merge per row) on a bounded sample of the workload's rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    order = list(np.argsort(wl.ctx_len))
+    rows = [order[0], order[-1]] + [b for b in np.random.default_rng(0).permutation(wl.batch).tolist()
+                                    if b not in (order[0], order[-1])]
+    spent, kv_bytes, tokens, done = 0.0, 0, 0, []
+    per_token = wl.kv_bytes() / max(1, int(wl.ctx_len.astype(np.int64).sum()))
+    for b in rows:
+        rv = workloads.row_values(wl, int(b), "cuda")
+        q, k, v = rv.q.cpu(), rv.k_ctx.cpu(), rv.v_ctx.cpu()
+        kn = rv.k_new.cpu() if rv.k_new is not None else None
+        vn = rv.v_new.cpu() if rv.v_new is not None else None
+        del rv
+        t0 = time.perf_counter()
+        oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn)
+        spent += time.perf_counter() - t0
+        kv_bytes += int(wl.ctx_len[b]) * per_token
+        tokens += int(wl.new_len[b])
+        done.append(int(b))
+        if spent >= budget_s:
+            break
+    torch.cuda.synchronize()
+    return {
+        "value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": f"{len(done)} of {wl.batch} rows (shortest and longest included), {int(kv_bytes / per_token)} "
+                  f"context tokens, float64 numpy, {spent:.1f} s; query tokens/s {tokens / spent:.2f}",
+        "query_tokens_per_s": round(tokens / spent, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the whole striped path on a single MI355X "
+              f"(all P stripes resident); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads
+    from cp_slot_map_amd import pool
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    torch.cuda.set_device(0)
+    wl = workloads.make(args.workload)
+    batch = pool.build_batch(wl, "cuda", fill=0.0)
+    plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        plan.partial()
+        plan.own_token()
+        ev[i][1].record()
+        plan.combine()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+
+    ms_per_step = wall * 1e3 / K
+    kv_bytes = wl.kv_bytes()
+    qtok = wl.num_tokens
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    part_avg = float(np.mean(part_ms))
+    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_RECORD):
+        rec = json.load(open(TRAFFIC_RECORD))
+        if rec.get("kernel_hash") == kernel_source_hash() and rec.get("workload") == wl.name:
+            traffic = rec.get("bytes_per_launch")
+
+    flops = None
+    if wl.kind == "gqa":
+        flops = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64)) * wl.num_q_heads * 2 * (
+            wl.head_dim + wl.head_dim_v)
+    result = {
+        "metric": "striped paged-attention decode: KV GB/s (% of HBM peak) and query tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "page_size": wl.page_size, "partners": wl.partners,
+                   "ctx_tokens": int(wl.ctx_len.astype(np.int64).sum()), "query_tokens": qtok, "seed": wl.seed,
+                   "kv_bytes": kv_bytes},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "query_tokens_per_s": round(qtok / (ms_per_step * 1e-3), 1),
+        "kernel_ms": {"partial_avg": round(part_avg, 5), "partial_min": round(float(np.min(part_ms)), 5),
+                      "merge_avg": round(float(np.mean(merge_ms)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "cp_paged_attn_partial (gqa_decode_bf16_kernel)",
+                     "bytes_per_launch": kv_bytes},
+    }
+    if flops:
+        result["tflops_partial"] = round(flops / (part_avg * 1e-3) / 1e12, 3)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,322 @@
+"""PyTorch-facing binding of libcpattn: shape/dtype checks and argument marshalling only.
+
+Every computation runs in the HIP library; torch provides device memory and the current stream. Tensors must live on
+the GPU. Layouts follow include/cpattn.h:
+
+* GQA pools are 5-D tensors indexed [stripe, page, slot, kv_head, dim] (any strides, dim contiguous). The usual
+  storage is head-major inside a page, [P, num_pages, Hkv, pp, D], passed as ``pool.transpose(2, 3)``.
+* MLA pools are 4-D [stripe, page, slot, 576].
+* Partials are [S, T, Hq, Dv] fp32 with lse [S, T, Hq] fp32 (natural log).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import CPATTN_BF16, CPATTN_F32, CPATTN_GQA, CPATTN_MLA, MAX_PARTIALS, PagedArgs, OwnArgs, MergeArgs
+
+__all__ = ["slot_map", "slot_map_rank", "kv_write", "paged_attn_partial", "paged_attn_workspace_size",
+           "own_token_attn", "lse_merge", "debug_gather_stripe", "version"]
+
+
+def _lib_handle():
+    return _lib.load()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return CPATTN_F32
+    if dt == torch.bfloat16:
+        return CPATTN_BF16
+    raise TypeError(f"unsupported dtype {dt}; expected float32 or bfloat16")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("cpattn tensors must live on the GPU")
+
+
+def version():
+    return _lib_handle().cpattn_version().decode()
+
+
+def slot_map(logical_slot: torch.Tensor, page_size: int, partners: int, stream=None):
+    """(partner int32, physical slot int64) for each logical slot (int64; < 0 = padding -> -1, -1)."""
+    lib = _lib_handle()
+    _need_cuda(logical_slot)
+    s = logical_slot.to(torch.int64).contiguous()
+    partner = torch.empty(s.shape, dtype=torch.int32, device=s.device)
+    phys = torch.empty(s.shape, dtype=torch.int64, device=s.device)
+    _lib.check(lib.cp_slot_map(_ptr(s), s.numel(), int(page_size), int(partners), _ptr(partner), _ptr(phys),
+                               _stream(stream)))
+    return partner, phys
+
+
+def slot_map_rank(logical_slot: torch.Tensor, page_size: int, partners: int, rank: int, sink_slot: int, stream=None):
+    """Per-rank write slot: physical slot if `rank` owns the token, else `sink_slot`; -1 for padding."""
+    lib = _lib_handle()
+    _need_cuda(logical_slot)
+    s = logical_slot.to(torch.int64).contiguous()
+    out = torch.empty(s.shape, dtype=torch.int64, device=s.device)
+    _lib.check(lib.cp_slot_map_rank(_ptr(s), s.numel(), int(page_size), int(partners), int(rank), int(sink_slot),
+                                    _ptr(out), _stream(stream)))
+    return out
+
+
+def _pool_strides(pool, kind):
+    if kind == "mla":
+        if pool.dim() != 4 or pool.stride(3) != 1:
+            raise ValueError("MLA pool must be [stripe, page, slot, 576] with a contiguous last dim")
+        return pool.stride(0), pool.stride(1), pool.stride(2), 0
+    if pool.dim() != 5 or pool.stride(4) != 1:
+        raise ValueError("GQA pool must be [stripe, page, slot, kv_head, dim] with a contiguous last dim")
+    return pool.stride(0), pool.stride(1), pool.stride(2), pool.stride(3)
+
+
+def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partners: int, *, kind="gqa",
+             stripe_begin=0, stripe_count=None, sink_slot=-1, stream=None):
+    """Write rows k_src [n, Hkv, D] (v_src [n, Hkv, Dv] or None) into the stripe pools through the slot map."""
+    lib = _lib_handle()
+    _need_cuda(logical_slot, k_src, v_src, k_pool, v_pool)
+    s = logical_slot.to(torch.int64).contiguous()
+    if kind == "mla":
+        k_src = k_src.reshape(k_src.shape[0], 1, -1)
+    if k_src.stride(-1) != 1 or (v_src is not None and v_src.stride(-1) != 1):
+        raise ValueError("source rows must have a contiguous last dim")
+    if v_src is not None and (v_src.stride(0) != k_src.stride(0) or v_src.stride(1) != k_src.stride(1)):
+        v_src = v_src.contiguous()
+        k_src = k_src.contiguous()
+    ss, sp, sl, sh = _pool_strides(k_pool, kind)
+    if v_pool is not None and _pool_strides(v_pool, kind) != (ss, sp, sl, sh):
+        raise ValueError("K and V pools must share strides")
+    P = int(partners)
+    sc = P - stripe_begin if stripe_count is None else int(stripe_count)
+    hkv = k_src.shape[1]
+    _lib.check(lib.cp_kv_write(_ptr(s), s.numel(), _ptr(k_src), _ptr(v_src), k_src.stride(0), k_src.stride(1),
+                               _dtype_code(k_src.dtype), hkv, k_src.shape[2],
+                               0 if v_src is None else v_src.shape[2], _ptr(k_pool),
+                               _ptr(v_pool if v_pool is not None else k_pool), ss, sp, sl, sh, int(page_size), P,
+                               k_pool.shape[1], int(stripe_begin), sc, int(sink_slot), _stream(stream)))
+
+
+def _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale, kind,
+                stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens):
+    a = PagedArgs()
+    a.kind = CPATTN_MLA if kind == "mla" else CPATTN_GQA
+    a.dtype = _dtype_code(q.dtype)
+    if k_pool.dtype != q.dtype:
+        raise TypeError("q and the pools must share a dtype")
+    a.num_rows = ctx_len.numel()
+    a.num_tokens = num_tokens
+    a.num_partners = int(partners)
+    a.stripe_begin = int(stripe_begin)
+    a.stripe_count = int(stripe_count)
+    a.page_size = int(page_size)
+    a.num_pages = k_pool.shape[1]
+    a.num_q_heads = q.shape[1]
+    if kind == "mla":
+        a.num_kv_heads = 1
+        a.head_dim = k_pool.shape[3]
+        a.head_dim_v = 512
+    else:
+        a.num_kv_heads = k_pool.shape[3]
+        a.head_dim = k_pool.shape[4]
+        a.head_dim_v = v_pool.shape[4]
+    a.scale = float(scale)
+    a.max_ctx_len = int(max_ctx_len)
+    a.max_row_tokens = int(max_row_tokens)
+    a.max_pages = block_table.shape[1]
+    a.q_row_start = q_row_start.data_ptr()
+    a.ctx_len = ctx_len.data_ptr()
+    a.block_table = block_table.data_ptr()
+    a.bt_stride = block_table.stride(0)
+    a.q = q.data_ptr()
+    a.q_stride_token, a.q_stride_head = q.stride(0), q.stride(1)
+    a.k_pool = k_pool.data_ptr()
+    a.v_pool = v_pool.data_ptr()
+    a.kv_stride_stripe, a.kv_stride_page, a.kv_stride_slot, a.kv_stride_head = _pool_strides(k_pool, kind)
+    if out is not None:
+        a.out = out.data_ptr()
+        a.out_stride_stripe, a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1), out.stride(2)
+        a.lse = lse.data_ptr()
+        a.lse_stride_stripe, a.lse_stride_token = lse.stride(0), lse.stride(1)
+    return a
+
+
+class _Workspace:
+    """Per-device zero-initialised scratch for split chunks; grown on demand, kept for reuse."""
+
+    def __init__(self):
+        self.buf = {}
+
+    def get(self, device, nbytes):
+        if nbytes <= 0:
+            return None
+        cur = self.buf.get(device)
+        if cur is None or cur.numel() < nbytes:
+            cur = torch.zeros(int(nbytes), dtype=torch.uint8, device=device)
+            self.buf[device] = cur
+        return cur
+
+
+_WS = _Workspace()
+
+
+def _check_int32_dev(*ts):
+    for t in ts:
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("row offsets, lengths and block tables must be contiguous int32 tensors")
+
+
+def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
+                              kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens):
+    lib = _lib_handle()
+    sc = int(partners) - stripe_begin if stripe_count is None else stripe_count
+    a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
+                    scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
+                    max_row_tokens=max_row_tokens, out=None, lse=None, num_tokens=q.shape[0])
+    n = C.c_int64(0)
+    _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
+    return int(n.value)
+
+
+def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
+                       kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len=None, max_row_tokens=None,
+                       out=None, lse=None, workspace=None, stream=None):
+    """Per-stripe partials (out [S, T, Hq, Dv] fp32, lse [S, T, Hq] fp32) of attention over the striped pool.
+
+    q [T, Hq, D]; q_row_start int32 [B + 1]; ctx_len int32 [B]; block_table int32 [B, max_pages]. ``max_ctx_len``
+    and ``max_row_tokens`` are host upper bounds (read from the device with a sync when omitted).
+    """
+    lib = _lib_handle()
+    _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
+    _check_int32_dev(q_row_start, ctx_len, block_table)
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [T, Hq, D] with a contiguous last dim")
+    if kind == "mla" and v_pool is None:
+        v_pool = k_pool
+    sc = int(partners) - stripe_begin if stripe_count is None else int(stripe_count)
+    T, Hq = q.shape[0], q.shape[1]
+    Dv = 512 if kind == "mla" else v_pool.shape[4]
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_len.max().item()) if ctx_len.numel() else 0
+    if max_row_tokens is None:
+        max_row_tokens = int((q_row_start[1:] - q_row_start[:-1]).max().item()) if ctx_len.numel() else 0
+    if out is None:
+        out = torch.empty((sc, T, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((sc, T, Hq), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or lse.dtype != torch.float32 or out.stride(3) != 1 or lse.stride(2) != 1:
+        raise ValueError("out/lse must be fp32 with contiguous last dims")
+    a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
+                    scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
+                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T)
+    n = C.c_int64(0)
+    _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
+    if n.value > 0:
+        ws = workspace if workspace is not None else _WS.get(q.device, n.value)
+        if ws.numel() * ws.element_size() < n.value:
+            raise ValueError(f"workspace too small: {n.value} bytes needed")
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _lib.check(lib.cp_paged_attn_partial(C.byref(a), _stream(stream)))
+    return out, lse
+
+
+def own_token_attn(q, k, v, cu_seqlens, *, scale, num_rows=None, max_row_tokens=None, out=None, lse=None,
+                   stream=None):
+    """Causal attention of each row's in-step queries over its in-step K/V: out [T, Hq, D] fp32, lse [T, Hq]."""
+    lib = _lib_handle()
+    _need_cuda(q, k, v, cu_seqlens, out, lse)
+    _check_int32_dev(cu_seqlens)
+    if q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1 or k.stride() != v.stride():
+        raise ValueError("q/k/v need contiguous last dims and k, v the same strides")
+    T, Hq, D = q.shape
+    B = cu_seqlens.numel() - 1 if num_rows is None else int(num_rows)
+    if max_row_tokens is None:
+        max_row_tokens = int((cu_seqlens[1:B + 1] - cu_seqlens[:B]).max().item()) if B > 0 else 0
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    a = OwnArgs()
+    a.dtype = _dtype_code(q.dtype)
+    a.num_rows = B
+    a.bucket_tokens = T
+    a.num_q_heads = Hq
+    a.num_kv_heads = k.shape[1]
+    a.head_dim = D
+    a.scale = float(scale)
+    a.max_row_tokens = int(max_row_tokens)
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.q = q.data_ptr()
+    a.q_stride_token, a.q_stride_head = q.stride(0), q.stride(1)
+    a.k, a.v = k.data_ptr(), v.data_ptr()
+    a.kv_stride_token, a.kv_stride_head = k.stride(0), k.stride(1)
+    a.out = out.data_ptr()
+    a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1)
+    a.lse = lse.data_ptr()
+    a.lse_stride_token = lse.stride(0)
+    _lib.check(lib.cp_own_token_attn(C.byref(a), _stream(stream)))
+    return out, lse
+
+
+def lse_merge(outs, lses, *, out_dtype=torch.float32, out=None, lse_out=None, token_count=None, stream=None):
+    """Exact LSE merge of N partials: outs is a list of [T, H, Dv] fp32, lses a list of [T, H] fp32."""
+    lib = _lib_handle()
+    n = len(outs)
+    if n != len(lses) or not 1 <= n <= MAX_PARTIALS:
+        raise ValueError(f"need 1..{MAX_PARTIALS} partials with matching lses")
+    T, H, Dv = outs[0].shape
+    _need_cuda(*outs, *lses, out, lse_out, token_count)
+    if out is None:
+        out = torch.empty((T, H, Dv), dtype=out_dtype, device=outs[0].device)
+    if lse_out is None:
+        lse_out = torch.empty((T, H), dtype=torch.float32, device=outs[0].device)
+    a = MergeArgs()
+    a.num_partials, a.num_tokens, a.num_heads, a.head_dim_v = n, T, H, Dv
+    a.out_dtype = _dtype_code(out.dtype)
+    a.token_count = token_count.data_ptr() if token_count is not None else None
+    for i, (o, l) in enumerate(zip(outs, lses)):
+        if o.dtype != torch.float32 or l.dtype != torch.float32 or o.stride(2) != 1 or tuple(o.shape) != (T, H, Dv):
+            raise ValueError("partials must be fp32 [T, H, Dv] with a contiguous last dim")
+        a.part_out[i] = o.data_ptr()
+        a.part_lse[i] = l.data_ptr()
+        a.part_out_stride_token[i], a.part_out_stride_head[i] = o.stride(0), o.stride(1)
+        a.part_lse_stride_token[i], a.part_lse_stride_head[i] = l.stride(0), l.stride(1)
+    a.out = out.data_ptr()
+    a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1)
+    a.lse_out = lse_out.data_ptr()
+    a.lse_out_stride_token = lse_out.stride(0)
+    _lib.check(lib.cp_lse_merge(C.byref(a), _stream(stream)))
+    return out, lse_out
+
+
+def debug_gather_stripe(k_pool, block_table_row, ctx_len: int, page_size: int, partners: int, r: int, *,
+                        kind="gqa", stream=None):
+    """Stripe r's keys of one row in local order, read with the kernels' own addressing: [Lr, Hkv, D]."""
+    lib = _lib_handle()
+    _need_cuda(k_pool, block_table_row)
+    _check_int32_dev(block_table_row)
+    ss, sp, sl, sh = _pool_strides(k_pool, kind)
+    hkv = 1 if kind == "mla" else k_pool.shape[3]
+    D = k_pool.shape[-1]
+    P = int(partners)
+    Lr = max(0, -(-(int(ctx_len) - r) // P))
+    dst = torch.empty((Lr, hkv, D), dtype=k_pool.dtype, device=k_pool.device)
+    _lib.check(lib.cp_debug_gather_stripe(_ptr(k_pool), _dtype_code(k_pool.dtype), ss, sp, sl, sh, k_pool.shape[1],
+                                          _ptr(block_table_row), int(ctx_len), int(page_size), P, int(r), hkv, D,
+                                          _ptr(dst), _stream(stream)))
+    return dst

@@ -1,0 +1,137 @@
+// Entry points of libcpattn: host-side validation and kernel dispatch. Nothing is enqueued unless every check that
+// can be made on the host passes; device-resident values are clamped inside the kernels.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace cpattn {
+
+static thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int32_t check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CPATTN_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return CPATTN_OK;
+}
+
+static bool negative_stride(const cp_paged_args& a) {
+    return a.q_stride_token < 0 || a.q_stride_head < 0 || a.kv_stride_stripe < 0 || a.kv_stride_page < 0 ||
+           a.kv_stride_slot < 0 || a.kv_stride_head < 0 || a.out_stride_stripe < 0 || a.out_stride_token < 0 ||
+           a.out_stride_head < 0 || a.lse_stride_stripe < 0 || a.lse_stride_token < 0 || a.bt_stride < 0;
+}
+
+// Validate cp_paged_args; on success fill the pool geometry.
+static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
+    if (!pa) return fail(CPATTN_EINVAL, "cp_paged_attn_partial: args is null");
+    const cp_paged_args& a = *pa;
+    if (a.kind != CPATTN_GQA && a.kind != CPATTN_MLA) return fail(CPATTN_EINVAL, "kind = %d unknown", a.kind);
+    if (a.dtype != CPATTN_F32 && a.dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype = %d unknown", a.dtype);
+    if (a.num_rows < 0 || a.num_tokens < 0 || a.max_ctx_len < 0 || a.max_row_tokens < 0 || a.max_pages < 0)
+        return fail(CPATTN_EINVAL, "negative size");
+    if (a.num_partners < 1 || a.num_partners > 16)
+        return fail(CPATTN_EINVAL, "num_partners = %d outside [1, 16]", a.num_partners);
+    if (a.page_size < 1 || a.page_size % a.num_partners)
+        return fail(CPATTN_EINVAL, "num_partners = %d must divide page_size = %d", a.num_partners, a.page_size);
+    if (a.stripe_count < 1 || a.stripe_begin < 0 || a.stripe_begin + a.stripe_count > a.num_partners)
+        return fail(CPATTN_EINVAL, "stripes [%d, %d) outside [0, %d)", a.stripe_begin, a.stripe_begin + a.stripe_count,
+                    a.num_partners);
+    if (a.num_pages < 1) return fail(CPATTN_EINVAL, "num_pages = %d must be >= 1 (page 0 is the sink)", a.num_pages);
+    if (a.num_q_heads < 1 || a.num_kv_heads < 1 || a.num_q_heads % a.num_kv_heads)
+        return fail(CPATTN_EINVAL, "num_q_heads = %d must be a positive multiple of num_kv_heads = %d", a.num_q_heads,
+                    a.num_kv_heads);
+    if (a.bt_stride < a.max_pages) return fail(CPATTN_EINVAL, "bt_stride < max_pages");
+    if (negative_stride(a)) return fail(CPATTN_EINVAL, "negative stride");
+    if (int64_t(a.max_pages) * a.page_size > (int64_t(1) << 31) - 1)
+        return fail(CPATTN_EINVAL, "max_pages * page_size overflows int32");
+    if (a.kind == CPATTN_MLA) {
+        if (a.num_kv_heads != 1) return fail(CPATTN_EINVAL, "MLA needs num_kv_heads = 1 (one latent head)");
+        if (a.v_pool != a.k_pool) return fail(CPATTN_EINVAL, "MLA reads values from the latent rows: v_pool != k_pool");
+        if (a.dtype != CPATTN_BF16 || a.head_dim != 576 || a.head_dim_v != 512)
+            return fail(CPATTN_EUNSUPPORTED, "MLA is built for bf16 with head_dim 576, head_dim_v 512");
+    } else {
+        if (a.head_dim != a.head_dim_v || (a.head_dim != 64 && a.head_dim != 128))
+            return fail(CPATTN_EUNSUPPORTED, "GQA is built for head_dim = head_dim_v in {64, 128} (got %d, %d)",
+                        a.head_dim, a.head_dim_v);
+    }
+    if (a.num_tokens > 0 && (!a.out || !a.lse)) return fail(CPATTN_EINVAL, "out/lse is null");
+    if (a.num_rows > 0 && (!a.q_row_start || !a.ctx_len || !a.block_table || !a.q || !a.k_pool || !a.v_pool))
+        return fail(CPATTN_EINVAL, "null device pointer");
+    if (a.num_tokens > 0 && !a.q_row_start) return fail(CPATTN_EINVAL, "q_row_start is null");
+    const int32_t pp = a.page_size / a.num_partners;
+    *geo = PoolGeom{a.kv_stride_stripe, a.kv_stride_page, a.kv_stride_slot, a.kv_stride_head, pp, ilog2_exact(pp),
+                    a.num_pages, 0};
+    return CPATTN_OK;
+}
+
+static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
+    if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes(a);
+    return 0;
+}
+
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" const char* cpattn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* cpattn_version(void) { return "0.1.0"; }
+
+extern "C" int64_t cpattn_struct_size(int32_t which) {
+    switch (which) {
+        case 0: return int64_t(sizeof(cp_paged_args));
+        case 1: return int64_t(sizeof(cp_own_args));
+        case 2: return int64_t(sizeof(cp_merge_args));
+        default: return -1;
+    }
+}
+
+extern "C" int32_t cp_paged_attn_workspace_size(const cp_paged_args* a, int64_t* bytes_out) {
+    PoolGeom geo;
+    if (int32_t st = check_paged(a, &geo)) return st;
+    if (!bytes_out) return fail(CPATTN_EINVAL, "bytes_out is null");
+    *bytes_out = paged_workspace(*a, geo);
+    return CPATTN_OK;
+}
+
+extern "C" int32_t cp_paged_attn_partial(const cp_paged_args* a, hipStream_t stream) {
+    PoolGeom geo;
+    if (int32_t st = check_paged(a, &geo)) return st;
+    const int64_t need = paged_workspace(*a, geo);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+        return fail(CPATTN_EINVAL, "workspace of %lld bytes needed (got %lld)", (long long)need,
+                    (long long)a->workspace_bytes);
+    if (a->num_tokens == 0) return CPATTN_OK;
+    if (decode_bf16_eligible(*a, geo)) return launch_paged_decode_bf16(*a, geo, stream);
+    return launch_paged_generic(*a, geo, stream);
+}
+
+extern "C" int32_t cp_own_token_attn(const cp_own_args* pa, hipStream_t stream) {
+    if (!pa) return fail(CPATTN_EINVAL, "cp_own_token_attn: args is null");
+    const cp_own_args& a = *pa;
+    if (a.dtype != CPATTN_F32 && a.dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype = %d unknown", a.dtype);
+    if (a.num_rows < 0 || a.bucket_tokens < 0 || a.max_row_tokens < 0) return fail(CPATTN_EINVAL, "negative size");
+    if (a.num_q_heads < 1 || a.num_kv_heads < 1 || a.num_q_heads % a.num_kv_heads)
+        return fail(CPATTN_EINVAL, "num_q_heads = %d must be a positive multiple of num_kv_heads = %d", a.num_q_heads,
+                    a.num_kv_heads);
+    if (a.head_dim != 64 && a.head_dim != 128)
+        return fail(CPATTN_EUNSUPPORTED, "own-token attention is built for head_dim 64 and 128 (got %d)", a.head_dim);
+    if (a.q_stride_token < 0 || a.q_stride_head < 0 || a.kv_stride_token < 0 || a.kv_stride_head < 0 ||
+        a.out_stride_token < 0 || a.out_stride_head < 0 || a.lse_stride_token < 0)
+        return fail(CPATTN_EINVAL, "negative stride");
+    if (a.bucket_tokens == 0) return CPATTN_OK;
+    if (!a.cu_seqlens || !a.out || !a.lse) return fail(CPATTN_EINVAL, "null device pointer");
+    if (a.num_rows > 0 && (!a.q || !a.k || !a.v)) return fail(CPATTN_EINVAL, "null device pointer");
+    return launch_own_token_generic(a, stream);
+}

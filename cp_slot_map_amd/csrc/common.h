@@ -1,0 +1,122 @@
+// Internal helpers shared by the cpattn kernels and the host entry points (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// ------------------------------------------------------------------------------------------------ host side
+// Record a message for cpattn_last_error() and return `code`.
+int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Turn the launch status of the kernels just enqueued into a cpattn status.
+int32_t check_launch(const char* what);
+
+inline int ilog2_exact(int64_t x) {  // log2(x) if x is a power of two, else -1
+    if (x <= 0 || (x & (x - 1))) return -1;
+    int s = 0;
+    while ((int64_t(1) << s) < x) ++s;
+    return s;
+}
+
+// ------------------------------------------------------------------------------------------------ device side
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Element loads as fp32 from either storage type.
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+
+// Round to nearest even, as the hardware pack instruction does (NaN stays NaN).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    bf16x2_t h = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) { return uint16_t(pack2_bf16(x, 0.0f) & 0xffffu); }
+
+// Geometry of one stripe pool set (all P stripes): strides in elements and the page-to-slot split.
+struct PoolGeom {
+    int64_t s_stripe, s_page, s_slot, s_head;
+    int32_t pp;          // slots per physical page = page_size / P
+    int32_t pp_shift;    // log2(pp) if pp is a power of two, else -1
+    int32_t num_pages;   // valid page ids are [0, num_pages); others read page 0
+    int32_t pad_;
+};
+
+// Element offset of local token i of stripe r (kv head g) inside the pool set.
+//
+// Local token i of partner r is the row's context position i*P + r. By the slot rule its logical slot is
+// page * page_size + (i*P + r) mod page_size, so it sits on logical page block_table[(i*P + r) / page_size] =
+// block_table[i / pp] at physical slot (i*P + r) mod page_size / P = i mod pp of r's pool: each stripe is an ordinary
+// paged cache of page size pp sharing the logical block table. Every kernel that reads the pool goes through this.
+__device__ __forceinline__ int64_t stripe_token_offset(const int32_t* __restrict__ bt_row, int32_t i, int32_t r,
+                                                       int32_t g, const PoolGeom& geo) {
+    int32_t pidx, slot;
+    if (geo.pp_shift >= 0) {
+        pidx = i >> geo.pp_shift;
+        slot = i & (geo.pp - 1);
+    } else {
+        pidx = i / geo.pp;
+        slot = i - pidx * geo.pp;
+    }
+    int32_t page = bt_row[pidx];
+    page = (page >= 0 && page < geo.num_pages) ? page : 0;
+    return int64_t(r) * geo.s_stripe + int64_t(page) * geo.s_page + int64_t(slot) * geo.s_slot +
+           int64_t(g) * geo.s_head;
+}
+
+// Same split for a page id already read from the block table (used where page ids are staged in LDS).
+__device__ __forceinline__ int64_t page_slot_offset(int32_t page, int32_t slot, int32_t r, int32_t g,
+                                                    const PoolGeom& geo) {
+    page = (page >= 0 && page < geo.num_pages) ? page : 0;
+    return int64_t(r) * geo.s_stripe + int64_t(page) * geo.s_page + int64_t(slot) * geo.s_slot +
+           int64_t(g) * geo.s_head;
+}
+
+// Tokens partner r holds of a row with L context tokens: positions t < L with t mod P == r.
+__device__ __forceinline__ int32_t stripe_length(int32_t L, int32_t r, int32_t P) {
+    return L > r ? (L - r + P - 1) / P : 0;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+// Write (0, -inf) for padding query tokens [t_begin, t_end) of S partials (Hq heads, Dv dims each).
+__device__ __forceinline__ void fill_padding(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse,
+                                             int64_t l_ss, int64_t l_st, int32_t S, int32_t Hq, int32_t Dv,
+                                             int32_t t_begin, int32_t t_end, int lane, int nlanes) {
+    for (int32_t t = t_begin; t < t_end; ++t) {
+        for (int32_t s = 0; s < S; ++s) {
+            for (int32_t h = 0; h < Hq; ++h) {
+                float* o = out + s * o_ss + int64_t(t) * o_st + int64_t(h) * o_sh;
+                for (int32_t d = lane; d < Dv; d += nlanes) o[d] = 0.0f;
+            }
+            for (int32_t h = lane; h < Hq; h += nlanes) lse[s * l_ss + int64_t(t) * l_st + h] = neg_inf();
+        }
+    }
+}
+
+}  // namespace cpattn

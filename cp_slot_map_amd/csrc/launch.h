@@ -1,0 +1,29 @@
+// Internal launch interface between the validating entry points and the kernel files.
+#pragma once
+
+#include "common.h"
+
+namespace cpattn {
+
+// Generic per-stripe partial: any built (dtype, head_dim, head_dim_v), any pp. One wave per (row, stripe, kv head,
+// block of query rows) streams the whole stripe; used for fp32 pools, MLA until its own kernel takes over, and any
+// shape the specialised kernels do not cover.
+int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+
+// Specialised bf16 GQA partial (head_dim = head_dim_v = 128) with MFMA score and value products and split chunks.
+bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
+int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
+int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+
+// (0, -inf) for the padding tokens [q_row_start[num_rows], num_tokens) of all S partials.
+int32_t launch_pad_partials(const cp_paged_args& a, hipStream_t stream);
+
+// (0, -inf) for tokens [starts[B], T) of S outputs with Hq heads of Dv values (starts is a device array).
+int32_t launch_pad(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse, int64_t l_ss, int64_t l_st,
+                   const int32_t* starts, int32_t B, int32_t T, int32_t S, int32_t Hq, int32_t Dv,
+                   hipStream_t stream);
+
+// Own-token causal attention (generic: f32/bf16, head_dim 64 or 128).
+int32_t launch_own_token_generic(const cp_own_args& a, hipStream_t stream);
+
+}  // namespace cpattn

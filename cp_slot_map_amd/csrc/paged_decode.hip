@@ -1,0 +1,490 @@
+// bf16 GQA per-stripe paged partial for head_dim = head_dim_v = 128, built for gfx950 MFMA.
+//
+// What it computes is the partial of one partner: attention of a row's queries over the context positions that
+// partner holds, returned as (out, natural-log lse) (mstar PR #1124, "Context / Sequence Parallel 1/5", PR description;
+// context attention over the paged cache in the vLLM compare view "[Core] Add explicit layer parallel plans",
+// FlashAttentionImpl._forward_with_dcp, which also splits the key range of one call into several pieces).
+//
+// Work decomposition. A work item is (row b, stripe s, kv head g, tile of 16 query rows, chunk of the stripe's local
+// tokens); one 64-lane wave runs it. Query rows of a kv head are (token, head-in-group) pairs, so a decode step with
+// G = 4 fills 4 rows of the 16 and a multi-token row fills more. Chunks of one (b, s, g, tile) write their
+// unnormalised partial to the workspace; the last one to arrive (device-scope counter) merges them exactly and writes
+// the stripe partial, then clears the counter. Block ids are remapped so the chunks of one item run on one XCD (the
+// hardware hands block i to XCD i mod 8), keeping workspace records in that XCD's L2.
+//
+// Per step of 16 local tokens:
+//   * scores S^T[token][row] = K . Q^T with four v_mfma_f32_16x16x32_bf16 (k = 32 head dims each). Lane l feeds token
+//     l%16's dims [32i + 8(l/16), +8) as the A operand and query row l%16's same dims as the B operand, so each of the
+//     four 16-byte K loads reads 16 whole 64-byte segments. The result leaves lane l with rows l%16 for tokens
+//     4(l/16)+0..3, exactly the A-operand layout of the value product.
+//   * online softmax in log2 units with a lazily moved running max (it moves only when a block maximum exceeds it by
+//     more than 8, so most steps skip the rescale; probabilities stay <= 256 and fp32 sums stay exact enough).
+//   * out += P . V with v_mfma_f32_16x16x16_bf16 (P split into a bf16 high part and a bf16 residual). Lane l loads tokens 4(l/16)+e, dims [8(l%16), +8): 16 lanes
+//     read a whole 256-byte row, fully coalesced. Output tile n column j is taken to be head dim 8j + n, so the B
+//     operand of tile n is element n of the lane's four token vectors: four 16-bit halves regrouped with two byte
+//     permutes, no LDS round trip.
+#include "launch.h"
+
+#include <cstdlib>
+
+namespace cpattn {
+
+constexpr int kDecodeMaxChunkPages = 320;
+// Completion counters occupy a fixed region at the start of the workspace, the same positions for every call shape,
+// so a call never finds another call's records where its counters should be. Each call leaves its counters at zero.
+constexpr int64_t kCounterBytes = int64_t(4) << 20;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
+
+struct DecodeParams {
+    const uint16_t* q;
+    int64_t q_st, q_sh;
+    const uint16_t* kp;
+    const uint16_t* vp;
+    PoolGeom geo;
+    const int32_t* q_row_start;
+    const int32_t* ctx_len;
+    const int32_t* bt;
+    int64_t bt_stride;
+    float* out;
+    int64_t o_ss, o_st, o_sh;
+    float* lse;
+    int64_t l_ss, l_st;
+    float* ws_rec;
+    int32_t* ws_cnt;
+    int32_t B, T, P, stripe_begin, S, Hq, Hkv, G;
+    int32_t max_pages, page_size, max_row_tokens;
+    int32_t n_qtiles, n_chunks, chunk_steps;
+    int32_t total_items, pad_blocks, pad_tokens_per_block;
+    int32_t rec_rows;
+    float scale_log2;
+};
+
+__device__ __forceinline__ u32x4_t load16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Pool element offsets of this lane's step loads: K token jb + l%16 (dim block 8*(l/16)), V tokens jb + 4*(l/16) + e
+// (dim block 8*(l%16)). Page ids come from the chunk's LDS copy of the block table; tokens past the chunk end are
+// clamped to its last page (their values are discarded).
+struct StepAddr {
+    int64_t k;
+    int64_t v[4];
+};
+
+__device__ __forceinline__ StepAddr step_addr(const int32_t* s_pages, int32_t pg0, int32_t npg, int32_t jb,
+                                              int32_t n16, int32_t c4, int32_t r, int32_t g, const PoolGeom& geo) {
+    StepAddr a;
+    {
+        const int32_t j = jb + n16;
+        const int32_t pidx = min((j >> geo.pp_shift) - pg0, npg - 1);
+        a.k = page_slot_offset(s_pages[pidx], j & (geo.pp - 1), r, g, geo) + 8 * c4;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int32_t j = jb + 4 * c4 + e;
+        const int32_t pidx = min((j >> geo.pp_shift) - pg0, npg - 1);
+        a.v[e] = page_slot_offset(s_pages[pidx], j & (geo.pp - 1), r, g, geo) + 8 * n16;
+    }
+    return a;
+}
+
+struct StepData {
+    u32x4_t k[4];
+    u32x4_t v[4];
+};
+
+__device__ __forceinline__ void step_load(StepData& d, const uint16_t* __restrict__ kp,
+                                          const uint16_t* __restrict__ vp, const StepAddr& a) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d.k[i] = load16(kp + a.k + 32 * i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + a.v[e]);
+}
+
+struct SoftmaxState {
+    f32x4_t o[8];      // o[n][ii]: query row 4*(l/16)+ii, head dim 8*(l%16)+n (unnormalised)
+    float m;           // running max (log2 units) of query row l%16
+    float l;           // this lane's share of the running sum of query row l%16
+};
+
+__device__ __forceinline__ void step_compute(SoftmaxState& st, const StepData& d, const bf16x8_t (&qop)[4],
+                                             int32_t jb, int32_t j1, int32_t c4, float scale_log2, int lane) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(d.k[i]), qop[i], sacc, 0, 0, 0);
+
+    const bool tail = jb + 16 > j1;  // wave-uniform
+    float sv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        sv[ii] = sacc[ii] * scale_log2;
+        if (tail && jb + 4 * c4 + ii >= j1) sv[ii] = neg_inf();
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > st.m + 8.0f)) {
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = exp2f(st.m - m_new);   // 0 on the first step (m = -inf)
+        st.l *= alpha;
+        st.m = m_new;
+        float a_o[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) a_o[ii] = __shfl(alpha, 4 * c4 + ii);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) st.o[n][ii] *= a_o[ii];
+    }
+    float pv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) pv[ii] = __builtin_amdgcn_exp2f(sv[ii] - st.m);
+    st.l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    // P enters the value product as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)): about 16 significant bits,
+    // so a peaked softmax over a few tokens keeps fp32-level accuracy. The second MFMA per tile is cheap next to the
+    // memory time of a step.
+    const u32x2_t pw = {pack2_bf16(pv[0], pv[1]), pack2_bf16(pv[2], pv[3])};
+    const s16x4_t pop = __builtin_bit_cast(s16x4_t, pw);
+    float pr[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t w = pw[ii >> 1];
+        pr[ii] = pv[ii] - __uint_as_float((ii & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    const u32x2_t pwl = {pack2_bf16(pr[0], pr[1]), pack2_bf16(pr[2], pr[3])};
+    const s16x4_t pop_lo = __builtin_bit_cast(s16x4_t, pwl);
+
+    u32x4_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = d.v[e];
+        if (tail && jb + 4 * c4 + e >= j1) v[e] = (u32x4_t){0u, 0u, 0u, 0u};   // select, never 0 * NaN
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const int dw = n >> 1;
+        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
+        const s16x4_t vop = __builtin_bit_cast(s16x4_t, (u32x2_t){lo, hi});
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, vop, st.o[n], 0, 0, 0);
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop_lo, vop, st.o[n], 0, 0, 0);
+    }
+    (void)lane;
+}
+
+__device__ __forceinline__ void write_row(const DecodeParams& p, int32_t s, int32_t tok0, int32_t row0, int32_t g,
+                                          int32_t row, int32_t n16, const float (&vals)[8]) {
+    const int32_t rho = row0 + row;
+    const int32_t t = tok0 + rho / p.G;
+    const int32_t h = g * p.G + rho % p.G;
+    float* o = p.out + s * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * n16;
+    *reinterpret_cast<f32x4_t*>(o) = (f32x4_t){vals[0], vals[1], vals[2], vals[3]};
+    *reinterpret_cast<f32x4_t*>(o + 4) = (f32x4_t){vals[4], vals[5], vals[6], vals[7]};
+}
+
+__device__ __forceinline__ void write_lse(const DecodeParams& p, int32_t s, int32_t tok0, int32_t row0, int32_t g,
+                                          int32_t row, float m_log2, float l) {
+    const int32_t rho = row0 + row;
+    const int32_t t = tok0 + rho / p.G;
+    const int32_t h = g * p.G + rho % p.G;
+    p.lse[s * p.l_ss + int64_t(t) * p.l_st + h] = l > 0.f ? (m_log2 + log2f(l)) * kLn2 : neg_inf();
+}
+
+__global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams p) {
+    __shared__ int32_t s_pages[kDecodeMaxChunkPages];
+    const int lane = threadIdx.x;
+    const int32_t nb = gridDim.x;                 // a multiple of 8
+    const int32_t bid = blockIdx.x;
+    const int32_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+
+    if (logical >= p.total_items) {               // padding-token fill role
+        const int32_t k = logical - p.total_items;
+        if (k >= p.pad_blocks) return;
+        const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
+        const int32_t t0 = max(k * p.pad_tokens_per_block, first);
+        const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
+        if (t0 < t1) fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        return;
+    }
+
+    int32_t item = logical;
+    const int32_t c = item % p.n_chunks;
+    item /= p.n_chunks;
+    const int32_t qt = item % p.n_qtiles;
+    item /= p.n_qtiles;
+    const int32_t g = item % p.Hkv;
+    item /= p.Hkv;
+    const int32_t s = item % p.S;
+    const int32_t b = item / p.S;
+    const int32_t triple = logical / p.n_chunks;
+
+    const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
+    const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
+    const int32_t nrows = ntok * p.G;
+    const int32_t row0 = qt * 16;
+    if (row0 >= nrows) return;
+    const int32_t tile_rows = min(16, nrows - row0);
+
+    const int32_t r = p.stripe_begin + s;
+    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t Lr = stripe_length(L, r, p.P);
+    const int32_t CH = p.chunk_steps * 16;
+    const int32_t nch = (Lr + CH - 1) / CH;
+    if (c >= max(nch, 1)) return;
+    const int32_t j0 = c * CH;
+    const int32_t j1 = min(j0 + CH, Lr);
+
+    const int32_t n16 = lane & 15;
+    const int32_t c4 = lane >> 4;
+
+    // Query operand: row n16 of the tile, dims [32i + 8*c4, +8).
+    bf16x8_t qop[4];
+    {
+        const int32_t rho = row0 + n16;
+        if (rho < nrows) {
+            const uint16_t* qp = p.q + int64_t(tok0 + rho / p.G) * p.q_st + int64_t(g * p.G + rho % p.G) * p.q_sh + 8 * c4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8(load16(qp + 32 * i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8((u32x4_t){0u, 0u, 0u, 0u});
+        }
+    }
+
+    // Stage the chunk's page ids.
+    const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
+    const int32_t pg0 = j0 >> p.geo.pp_shift;
+    const int32_t npg = j1 > j0 ? ((j1 - 1) >> p.geo.pp_shift) - pg0 + 1 : 1;
+    for (int32_t k = lane; k < npg; k += 64) s_pages[k] = j1 > j0 ? bt_row[pg0 + k] : 0;
+    __syncthreads();
+
+    SoftmaxState st;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    st.m = neg_inf();
+    st.l = 0.f;
+
+    const int32_t nsteps = (j1 - j0 + 15) >> 4;
+    if (nsteps > 0) {
+        StepData da, db;
+        step_load(da, p.kp, p.vp, step_addr(s_pages, pg0, npg, j0, n16, c4, r, g, p.geo));
+        int32_t it = 0;
+        for (; it + 2 <= nsteps; it += 2) {
+            const int32_t jb = j0 + it * 16;
+            step_load(db, p.kp, p.vp, step_addr(s_pages, pg0, npg, jb + 16, n16, c4, r, g, p.geo));
+            step_compute(st, da, qop, jb, j1, c4, p.scale_log2, lane);
+            if (it + 2 < nsteps) step_load(da, p.kp, p.vp, step_addr(s_pages, pg0, npg, jb + 32, n16, c4, r, g, p.geo));
+            step_compute(st, db, qop, jb + 16, j1, c4, p.scale_log2, lane);
+        }
+        if (it < nsteps) step_compute(st, da, qop, j0 + it * 16, j1, c4, p.scale_log2, lane);
+    }
+
+    // Row sums: combine the four lane groups that share a query row.
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    float l_o[4], m_o[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        l_o[ii] = __shfl(st.l, 4 * c4 + ii);
+        m_o[ii] = __shfl(st.m, 4 * c4 + ii);
+    }
+
+    if (nch <= 1) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int32_t row = 4 * c4 + ii;
+            if (row < tile_rows) {
+                const float inv = l_o[ii] > 0.f ? 1.0f / l_o[ii] : 0.f;
+                float vals[8];
+#pragma unroll
+                for (int n = 0; n < 8; ++n) vals[n] = st.o[n][ii] * inv;
+                write_row(p, s, tok0, row0, g, row, n16, vals);
+            }
+        }
+        if (c4 == 0 && n16 < tile_rows) write_lse(p, s, tok0, row0, g, n16, st.m, st.l);
+        return;
+    }
+
+    // Several chunks: store this chunk's unnormalised record, then the last arriver merges.
+    const int32_t RR = p.rec_rows;
+    const int64_t rec_floats = int64_t(RR) * 130;
+    float* rec = p.ws_rec + int64_t(logical) * rec_floats;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int32_t row = 4 * c4 + ii;
+        if (row < tile_rows) {
+            float* o = rec + row * 128 + 8 * n16;
+            *reinterpret_cast<f32x4_t*>(o) = (f32x4_t){st.o[0][ii], st.o[1][ii], st.o[2][ii], st.o[3][ii]};
+            *reinterpret_cast<f32x4_t*>(o + 4) = (f32x4_t){st.o[4][ii], st.o[5][ii], st.o[6][ii], st.o[7][ii]};
+        }
+    }
+    if (c4 == 0 && n16 < tile_rows) {
+        rec[RR * 128 + n16] = st.m;
+        rec[RR * 128 + RR + n16] = st.l;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(p.ws_cnt + triple, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != nch - 1) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    const float* rec0 = p.ws_rec + int64_t(triple) * p.n_chunks * rec_floats;
+    // Rows of the O layout (4*c4 + ii) and the lse row (n16) are merged independently.
+    float M_o[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+    float M_r = neg_inf();
+    for (int32_t cc = 0; cc < nch; ++cc) {
+        const float* rc = rec0 + cc * rec_floats + RR * 128;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int32_t row = 4 * c4 + ii;
+            if (row < tile_rows) M_o[ii] = fmaxf(M_o[ii], rc[row]);
+        }
+        if (n16 < tile_rows) M_r = fmaxf(M_r, rc[n16]);
+    }
+    float acc[4][8];
+    float L_o[4] = {0.f, 0.f, 0.f, 0.f};
+    float L_r = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[ii][n] = 0.f;
+    for (int32_t cc = 0; cc < nch; ++cc) {
+        const float* rc = rec0 + cc * rec_floats;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int32_t row = 4 * c4 + ii;
+            if (row < tile_rows) {
+                const float w = exp2f(rc[RR * 128 + row] - M_o[ii]);
+                L_o[ii] += w * rc[RR * 128 + RR + row];
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16);
+                const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16 + 4);
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    acc[ii][n] += w * a[n];
+                    acc[ii][n + 4] += w * bq[n];
+                }
+            }
+        }
+        if (n16 < tile_rows) L_r += exp2f(rc[RR * 128 + n16] - M_r) * rc[RR * 128 + RR + n16];
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int32_t row = 4 * c4 + ii;
+        if (row < tile_rows) {
+            const float inv = L_o[ii] > 0.f ? 1.0f / L_o[ii] : 0.f;
+            float vals[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) vals[n] = acc[ii][n] * inv;
+            write_row(p, s, tok0, row0, g, row, n16, vals);
+        }
+    }
+    if (c4 == 0 && n16 < tile_rows) write_lse(p, s, tok0, row0, g, n16, M_r, L_r);
+    if (lane == 0) p.ws_cnt[triple] = 0;   // ready for the next call
+}
+
+static int32_t decode_chunk_steps() {
+    static int32_t steps = [] {
+        const char* e = std::getenv("CPATTN_DECODE_CHUNK_STEPS");
+        int v = e ? std::atoi(e) : 16;
+        if (v < 1) v = 1;
+        if (v > 16) v = 16;
+        return v;
+    }();
+    return steps;
+}
+
+struct DecodeShape {
+    int64_t n_qtiles, n_chunks, total_items, rec_rows, triples;
+};
+
+static DecodeShape decode_shape(const cp_paged_args& a) {
+    DecodeShape d{};
+    const int64_t G = a.num_q_heads / a.num_kv_heads;
+    const int64_t rows = int64_t(a.max_row_tokens) * G;
+    d.n_qtiles = std::max<int64_t>(1, (rows + 15) / 16);
+    const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
+    const int64_t CH = int64_t(decode_chunk_steps()) * 16;
+    d.n_chunks = std::max<int64_t>(1, (max_lr + CH - 1) / CH);
+    d.triples = int64_t(a.num_rows) * a.stripe_count * a.num_kv_heads * d.n_qtiles;
+    if (d.triples > kMaxCounters) d.n_chunks = 1;   // too many items to count: no split, no workspace
+    d.total_items = d.triples * d.n_chunks;
+    const int64_t rr = std::min<int64_t>(16, rows);
+    d.rec_rows = std::max<int64_t>(4, (rr + 3) / 4 * 4);
+    return d;
+}
+
+bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
+    if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != 128 || a.head_dim_v != 128) return false;
+    if (geo.pp_shift < 0 || geo.pp > 256) return false;
+    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool) || !al16(a.out)) return false;
+    if ((a.q_stride_token | a.q_stride_head | a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot |
+         a.kv_stride_head) & 7)
+        return false;
+    if ((a.out_stride_stripe | a.out_stride_token | a.out_stride_head) & 3) return false;
+    const DecodeShape d = decode_shape(a);
+    if (d.total_items + (a.num_tokens + 3) / 4 + 8 > (int64_t(1) << 31) - 1) return false;
+    // A chunk covers at most chunk_steps*16 tokens, so at most that many pages (+1) are staged.
+    if (int64_t(decode_chunk_steps()) * 16 / std::max(1, geo.pp) + 1 > kDecodeMaxChunkPages) return false;
+    return true;
+}
+
+int64_t decode_bf16_workspace_bytes(const cp_paged_args& a) {
+    const DecodeShape d = decode_shape(a);
+    if (d.n_chunks <= 1) return 0;
+    return kCounterBytes + d.total_items * d.rec_rows * 130 * 4;
+}
+
+int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
+    const DecodeShape d = decode_shape(a);
+    DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.q_st = a.q_stride_token;
+    p.q_sh = a.q_stride_head;
+    p.kp = static_cast<const uint16_t*>(a.k_pool);
+    p.vp = static_cast<const uint16_t*>(a.v_pool);
+    p.geo = geo;
+    p.q_row_start = a.q_row_start;
+    p.ctx_len = a.ctx_len;
+    p.bt = a.block_table;
+    p.bt_stride = a.bt_stride;
+    p.out = a.out;
+    p.o_ss = a.out_stride_stripe;
+    p.o_st = a.out_stride_token;
+    p.o_sh = a.out_stride_head;
+    p.lse = a.lse;
+    p.l_ss = a.lse_stride_stripe;
+    p.l_st = a.lse_stride_token;
+    if (d.n_chunks > 1) {
+        p.ws_cnt = static_cast<int32_t*>(a.workspace);
+        p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + kCounterBytes);
+    }
+    p.B = a.num_rows;
+    p.T = a.num_tokens;
+    p.P = a.num_partners;
+    p.stripe_begin = a.stripe_begin;
+    p.S = a.stripe_count;
+    p.Hq = a.num_q_heads;
+    p.Hkv = a.num_kv_heads;
+    p.G = a.num_q_heads / a.num_kv_heads;
+    p.max_pages = a.max_pages;
+    p.page_size = a.page_size;
+    p.max_row_tokens = a.max_row_tokens;
+    p.n_qtiles = int32_t(d.n_qtiles);
+    p.n_chunks = int32_t(d.n_chunks);
+    p.chunk_steps = decode_chunk_steps();
+    p.total_items = int32_t(d.total_items);
+    p.pad_tokens_per_block = 4;
+    p.pad_blocks = (a.num_tokens + 3) / 4;
+    p.rec_rows = int32_t(d.rec_rows);
+    p.scale_log2 = a.scale * kLog2e;
+    const int64_t blocks = ((d.total_items + p.pad_blocks) + 7) / 8 * 8;
+    if (blocks == 0) return CPATTN_OK;
+    hipLaunchKernelGGL(gqa_decode_bf16_kernel, dim3(uint32_t(blocks)), dim3(64), 0, stream, p);
+    return check_launch("cp_paged_attn_partial (bf16 decode)");
+}
+
+}  // namespace cpattn

@@ -1,0 +1,289 @@
+/*
+ * cpattn: attention over a context-parallel striped paged KV pool, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (mstar PR #1124, "Context / Sequence Parallel 1/5: split the KV cache by position across GPUs (DCP)",
+ * PR description and commit message): a paged pool with context parallelism spreads each page's token slots over P
+ * partners. The token in logical slot s is kept by partner s mod P at index floor(s / P) of that partner's pool, and
+ * page ids stay logical. Each partner attends the slots it holds and returns a partial output together with that
+ * partial's log-sum-exp; the partials are combined without approximation. When a row brings several tokens in one
+ * step, they also attend each other, using the K/V the layer hands over, and that partial joins the combination. The vLLM compare view
+ * "[Core] Add explicit layer parallel plans" (FlashAttentionImpl._forward_with_dcp) shows the same shape: context
+ * attention over the paged cache with (out, lse), a combine across ranks, own-token attention with the query offsets
+ * used as key offsets, and a final LSE merge.
+ *
+ * On one GPU every stripe's pool is resident, so the exchange between partners is simply the merge reading the
+ * partial buffers.
+ *
+ * Conventions for every entry point:
+ *   - Every call returns a status: CPATTN_OK, CPATTN_EINVAL (an argument is wrong), CPATTN_EUNSUPPORTED (valid but no
+ *     kernel is built for it, e.g. a head dim) or CPATTN_ELAUNCH (the HIP launch failed). On any non-OK status
+ *     nothing was enqueued; cpattn_last_error() gives a message for the calling thread. Nothing asserts or throws.
+ *   - All validation that can be done on the host happens before anything is enqueued. Values that live in device
+ *     memory (lengths, block tables, offsets) cannot be checked there; kernels clamp them so that no access leaves
+ *     the buffers described by the arguments (see each entry point).
+ *   - Tensor arguments are device pointers owned by the caller. The library allocates no device memory and keeps no
+ *     pointer after the call returns, apart from the work it queued on `stream`. Calls are asynchronous on `stream`
+ *     (NULL = the null stream).
+ *   - Strides are in elements. The innermost (head-dim) axis of every tensor is contiguous.
+ *   - LSEs are natural-log log-sum-exps of the scaled scores, fp32. An empty key set gives out = 0 and lse = -inf.
+ */
+#ifndef CPATTN_H_
+#define CPATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_OK 0
+#define CPATTN_EINVAL 1
+#define CPATTN_EUNSUPPORTED 2
+#define CPATTN_ELAUNCH 3
+
+#define CPATTN_F32 0
+#define CPATTN_BF16 1
+
+#define CPATTN_GQA 0
+#define CPATTN_MLA 1
+
+/* P <= 16 stripes plus the own-token partial. */
+#define CPATTN_MAX_PARTIALS 17
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* cpattn_last_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+const char* cpattn_version(void);
+
+/* sizeof() of the argument structs, for bindings to check their layout: which = 0 cp_paged_args, 1 cp_own_args,
+ * 2 cp_merge_args. Returns -1 for an unknown `which`. */
+int64_t cpattn_struct_size(int32_t which);
+
+/*
+ * cp_slot_map: logical slot -> (partner, physical slot); the write-addressing path.
+ *
+ * Source: the slot rule of mstar PR #1124 (PR description); the review thread on resident planning notes that a
+ * partner pool holds page_size / P slots a page, which is why every write path must go through this map.
+ *
+ *   logical_slot  device int64 [n]: page_id * page_size + offset of each token to write; < 0 marks a padding token.
+ *   partner_out   device int32 [n]: s mod P, or -1 for s < 0.
+ *   phys_out      device int64 [n]: floor(s / P) (= page_id * (page_size / P) + offset / P), or -1 for s < 0.
+ * EINVAL: n < 0, P < 1, page_size < 1, page_size % P != 0, or a null pointer with n > 0. n = 0 enqueues nothing.
+ */
+int32_t cp_slot_map(const int64_t* logical_slot, int64_t n, int32_t page_size, int32_t num_partners,
+                    int32_t* partner_out, int64_t* phys_out, hipStream_t stream);
+
+/*
+ * cp_slot_map_rank: the per-rank write view. Rank `rank` writes a token it owns at its physical slot and every other
+ * token at `sink_slot` (a slot of the sink page in its own pool), as the PR description states for non-owners.
+ *   write_slot_out  device int64 [n]: physical slot for owned tokens, sink_slot otherwise, -1 for s < 0.
+ * EINVAL: as cp_slot_map, plus rank outside [0, P) or sink_slot < 0.
+ */
+int32_t cp_slot_map_rank(const int64_t* logical_slot, int64_t n, int32_t page_size, int32_t num_partners,
+                         int32_t rank, int64_t sink_slot, int64_t* write_slot_out, hipStream_t stream);
+
+/*
+ * cp_kv_write: fused slot map + write of K (and V) rows into the stripe pools, for stripes
+ * [stripe_begin, stripe_begin + stripe_count) held by the caller.
+ *
+ * Source: every write-addressing path must go through the placement, and a token is written by its owner and to the
+ * sink page on every other rank (mstar PR #1124, PR description and commit message; the review thread on resident
+ * planning shows what goes wrong when a write path skips it).
+ *
+ *   logical_slot  device int64 [n]; < 0 = padding (written nowhere).
+ *   k_src         device [n, num_kv_heads, head_dim] (token stride src_stride_token, head stride src_stride_head).
+ *   v_src         device [n, num_kv_heads, head_dim_v] with the same strides, or NULL (MLA: the latent row is K).
+ *   pools         layout of cp_paged_args (element (r, page, slot, g, d) at pool + r*kv_stride_stripe + ...).
+ *   sink_slot     >= 0: stripes in range that do not own a token write it to this physical slot (per-rank view);
+ *                 < 0: only the owner writes (all stripes resident on one device).
+ * A token whose page id falls outside [0, num_pages) is not written. Tokens sharing a destination race (last wins).
+ * EINVAL: bad geometry, stripe range, null pointers, negative sizes or strides, sink_slot >= num_pages * page_size / P.
+ */
+int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const void* k_src, const void* v_src,
+                    int64_t src_stride_token, int64_t src_stride_head, int32_t dtype, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t head_dim_v, void* k_pool, void* v_pool, int64_t kv_stride_stripe,
+                    int64_t kv_stride_page, int64_t kv_stride_slot, int64_t kv_stride_head, int32_t page_size,
+                    int32_t num_partners, int32_t num_pages, int32_t stripe_begin, int32_t stripe_count,
+                    int64_t sink_slot, hipStream_t stream);
+
+/*
+ * Arguments of cp_paged_attn_partial.
+ *
+ * Query layout: q element (token t, head h, dim d) at q + t*q_stride_token + h*q_stride_head + d, tokens of row b
+ * being [q_row_start[b], q_row_start[b+1]). Tokens in [q_row_start[num_rows], num_tokens) are padding.
+ *
+ * Pool layout: element (stripe r, page p, slot j, kv head g, dim d) of the K pool is at
+ *   k_pool + r*kv_stride_stripe + p*kv_stride_page + j*kv_stride_slot + g*kv_stride_head + d,
+ * the same for v_pool. Stripe r's pool has num_pages pages of page_size / P slots; page ids are the logical ones
+ * from the block table. For MLA each slot holds one latent row of head_dim (576) values: the key is the whole row and
+ * the value its first head_dim_v (512) columns; v_pool must equal k_pool and kv_stride_head is ignored.
+ *
+ * Partial layout (S = stripe_count, stripe index relative to stripe_begin):
+ *   out (s, t, h, d) at out + s*out_stride_stripe + t*out_stride_token + h*out_stride_head + d   (fp32)
+ *   lse (s, t, h)    at lse + s*lse_stride_stripe + t*lse_stride_token + h                     (fp32)
+ */
+typedef struct cp_paged_args {
+    int32_t kind;             /* CPATTN_GQA or CPATTN_MLA */
+    int32_t dtype;            /* element type of q, k_pool, v_pool: CPATTN_F32 or CPATTN_BF16 */
+    int32_t num_rows;         /* B: rows (requests) */
+    int32_t num_tokens;       /* T: query tokens in the (possibly padded) bucket */
+    int32_t num_partners;     /* P: stripes of the pool; must divide page_size */
+    int32_t stripe_begin;     /* first stripe attended by this call */
+    int32_t stripe_count;     /* S: stripes attended; out and lse hold S partials */
+    int32_t page_size;        /* logical page size (slots of a logical page) */
+    int32_t num_pages;        /* pages in each stripe pool; block-table entries outside [0, num_pages) read page 0 */
+    int32_t num_q_heads;      /* Hq */
+    int32_t num_kv_heads;     /* Hkv; Hq % Hkv == 0; query head h reads kv head h / (Hq / Hkv) */
+    int32_t head_dim;         /* qk dim: 64 or 128 (GQA), 576 (MLA) */
+    int32_t head_dim_v;       /* value dim: equal to head_dim (GQA), 512 (MLA) */
+    float scale;              /* softmax scale applied to q.k */
+    int32_t max_ctx_len;      /* host upper bound of ctx_len[b], sizes the launch; larger device values are clamped */
+    int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
+    int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
+    int32_t reserved0;
+    const int32_t* q_row_start;  /* device int32 [num_rows + 1], non-decreasing, q_row_start[num_rows] <= num_tokens */
+    const int32_t* ctx_len;      /* device int32 [num_rows]: context tokens of row b in the pool (all stripes) */
+    const int32_t* block_table;  /* device int32 [num_rows, bt_stride]: logical page ids */
+    int64_t bt_stride;
+    const void* q;
+    int64_t q_stride_token, q_stride_head;
+    const void* k_pool;
+    const void* v_pool;
+    int64_t kv_stride_stripe, kv_stride_page, kv_stride_slot, kv_stride_head;
+    float* out;
+    int64_t out_stride_stripe, out_stride_token, out_stride_head;
+    float* lse;
+    int64_t lse_stride_stripe, lse_stride_token;
+    void* workspace;          /* device scratch of cp_paged_attn_workspace_size() bytes (NULL if that is 0). Its
+                                 first 4 MiB hold completion counters that must be zero before the first call; every
+                                 call leaves them zero when it completes. The rest is overwritten freely. Calls that
+                                 share a workspace must not run concurrently. */
+    int64_t workspace_bytes;
+} cp_paged_args;
+
+/*
+ * cp_paged_attn_partial: per-stripe paged attention returning out + lse, for every stripe r in
+ * [stripe_begin, stripe_begin + stripe_count).
+ *
+ * Source: each partner attends the slots it holds and returns its partial with the partial's log-sum-exp (mstar
+ * PR #1124, PR description; the PR also notes that a decode kernel without an LSE output cannot be used because the
+ * merge needs it); context attention over the paged cache through the block table returning (out, lse) in the vLLM
+ * compare view, FlashAttentionImpl._forward_with_dcp.
+ *
+ * For every real query token t of row b, head h and stripe r: the keys are the context positions p < ctx_len[b] with
+ * p mod P == r (the slots partner r holds); local token i of stripe r is position i*P + r, found at page
+ * block_table[b][i / (page_size/P)], slot i % (page_size/P) of r's pool. Every query token of a row sees the whole
+ * context (no mask). Rows with ctx_len[b] <= r give (0, -inf). Padding tokens get out = 0 and lse = -inf and their
+ * queries are not read.
+ *
+ * EINVAL: a null args/pointer, Hq % Hkv != 0, page_size % P != 0, a stripe range outside [0, P), negative sizes or
+ * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
+ * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
+ * (128, 128); MLA bf16 with (576, 512).
+ */
+int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
+
+/* Workspace bytes cp_paged_attn_partial needs for `args` (depends on shapes and the host bounds only). */
+int32_t cp_paged_attn_workspace_size(const cp_paged_args* args, int64_t* bytes_out);
+
+/*
+ * Arguments of cp_own_token_attn.
+ *   q (t, h, d) at q + t*q_stride_token + h*q_stride_head + d; k and v (t, g, d) at k/v + t*kv_stride_token +
+ *   g*kv_stride_head + d; out (t, h, d) at out + t*out_stride_token + h*out_stride_head + d; lse (t, h) at
+ *   lse + t*lse_stride_token + h.
+ */
+typedef struct cp_own_args {
+    int32_t dtype;            /* CPATTN_F32 or CPATTN_BF16, for q, k, v */
+    int32_t num_rows;         /* real rows; row b owns bucket tokens [cu_seqlens[b], cu_seqlens[b+1]) */
+    int32_t bucket_tokens;    /* tokens in the bucket; [cu_seqlens[num_rows], bucket_tokens) is padding */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;         /* 64 or 128 */
+    float scale;
+    int32_t max_row_tokens;   /* host upper bound of a row's tokens (sizes the launch; longer rows are clamped) */
+    const int32_t* cu_seqlens;   /* device int32 [num_rows + 1], non-decreasing; values are clamped to the bucket */
+    const void* q;
+    int64_t q_stride_token, q_stride_head;
+    const void* k;
+    const void* v;
+    int64_t kv_stride_token, kv_stride_head;
+    float* out;
+    int64_t out_stride_token, out_stride_head;
+    float* lse;
+    int64_t lse_stride_token;
+} cp_own_args;
+
+/*
+ * cp_own_token_attn: causal attention of each row's in-step queries over the row's in-step K/V.
+ *
+ * Source: when a row brings more than one token in a step, those tokens also attend one another, using the K/V that
+ * the layer hands over rather than the pool, and in a padded (captured) bucket the keys of padding rows must stay
+ * invisible to this kernel (mstar PR #1124, PR description; its review thread on the padding test reports NaN in
+ * padding keys spreading to every real row when padding rows sat in the bucket); the own-token call in the vLLM
+ * compare view passes the query offsets as the key offsets.
+ *
+ * Query i of a row (0-based within the row) sees the row's keys 0..i. Keys and queries of padding tokens are never
+ * read; padding tokens get out = 0 and lse = -inf.
+ * EINVAL: null pointers, negative sizes, Hq % Hkv != 0. EUNSUPPORTED: head_dim other than 64 or 128.
+ */
+int32_t cp_own_token_attn(const cp_own_args* args, hipStream_t stream);
+
+/*
+ * Arguments of cp_lse_merge. Partial i: out (t, h, d) at part_out[i] + t*part_out_stride_token[i] +
+ * h*part_out_stride_head[i] + d and lse (t, h) at part_lse[i] + t*part_lse_stride_token[i] + h*part_lse_stride_head[i].
+ * Output (t, h, d) at out + t*out_stride_token + h*out_stride_head + d; lse_out (t, h) at lse_out +
+ * t*lse_out_stride_token + h.
+ */
+typedef struct cp_merge_args {
+    int32_t num_partials;     /* N in [1, CPATTN_MAX_PARTIALS] */
+    int32_t num_tokens;       /* T */
+    int32_t num_heads;        /* H */
+    int32_t head_dim_v;       /* Dv, a multiple of 4 */
+    int32_t out_dtype;        /* CPATTN_F32 or CPATTN_BF16 (round to nearest even) */
+    int32_t reserved0;
+    const int32_t* token_count;  /* nullable device int32 [1]: tokens >= *token_count are padding: written as
+                                    (0, -inf) without reading the partials */
+    const float* part_out[CPATTN_MAX_PARTIALS];
+    const float* part_lse[CPATTN_MAX_PARTIALS];
+    int64_t part_out_stride_token[CPATTN_MAX_PARTIALS];
+    int64_t part_out_stride_head[CPATTN_MAX_PARTIALS];
+    int64_t part_lse_stride_token[CPATTN_MAX_PARTIALS];
+    int64_t part_lse_stride_head[CPATTN_MAX_PARTIALS];
+    void* out;
+    int64_t out_stride_token, out_stride_head;
+    float* lse_out;           /* nullable */
+    int64_t lse_out_stride_token;
+} cp_merge_args;
+
+/*
+ * cp_lse_merge: exact combination of N partials by their LSEs.
+ *
+ * Source: the partials are merged exactly (mstar PR #1124, PR description); dcp_combine and merge_attn_states in the
+ * vLLM compare view, FlashAttentionImpl._forward_with_dcp.
+ *
+ * M = max_i lse_i; M = -inf gives out = 0, lse = -inf; otherwise lse = M + log sum_i exp(lse_i - M) and
+ * out = sum_i exp(lse_i - lse) * o_i. A partial with lse_i = -inf is not read (its out row may hold anything).
+ * EINVAL: N outside [1, CPATTN_MAX_PARTIALS], null pointers, Dv % 4 != 0, negative sizes, out aliasing a partial.
+ */
+int32_t cp_lse_merge(const cp_merge_args* args, hipStream_t stream);
+
+/*
+ * cp_debug_gather_stripe (test support): copy stripe r's keys of one row, in local order, into a dense buffer, through
+ * the same device addressing function the attention kernels use, so page addressing can be checked bit for bit.
+ *   dst (i, g, d) at dst + (i*num_kv_heads + g)*head_dim + d for i < ceil((ctx_len - r) / P), same dtype as the pool.
+ *   block_table_row: device int32 [>= ceil(ctx_len / page_size)].
+ * EINVAL: bad geometry, r outside [0, P), null pointers, negative sizes.
+ */
+int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe, int64_t kv_stride_page,
+                               int64_t kv_stride_slot, int64_t kv_stride_head, int32_t num_pages,
+                               const int32_t* block_table_row, int32_t ctx_len, int32_t page_size,
+                               int32_t num_partners, int32_t r, int32_t num_kv_heads, int32_t head_dim, void* dst,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H_ */

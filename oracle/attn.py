@@ -7,7 +7,7 @@ Sources:
   description: each rank attends the slots it holds and returns its partial output together with the partial's
   log-sum-exp; the partials are then merged exactly; a step with more than one token in a row also attends the row's
   own in-step tokens, taken from the K/V the layer hands over, and that result is merged in as well. The review
-  thread on the padding test adds that padding merges to zero and reaches no real row.
+  thread on the padding test adds that padding tokens must come out as zero and must never influence a real row.
 * vLLM compare view "[Core] Add explicit layer parallel plans", ``FlashAttentionImpl._forward_with_dcp``: context
   attention over the paged cache returns (out, lse); the own-token call uses the query offsets as key offsets; the
   two are merged by their LSEs; with no context anywhere only the own-token call runs.

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/cpattn.h declares, agrees with the binding on
+struct layouts, and refuses bad arguments on the host before anything is enqueued (no compute call is made)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from cp_slot_map_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(c\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("cp_slot_map", "cp_paged_attn_partial", "cp_own_token_attn", "cp_lse_merge"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in cpattn.h but not exported"
+        assert name in _lib.EXPORTS, f"{name} has no binding signature"
+
+
+def test_struct_layouts_match(lib):
+    assert lib.cpattn_struct_size(0) == C.sizeof(_lib.PagedArgs)
+    assert lib.cpattn_struct_size(1) == C.sizeof(_lib.OwnArgs)
+    assert lib.cpattn_struct_size(2) == C.sizeof(_lib.MergeArgs)
+    assert lib.cpattn_struct_size(7) == -1
+
+
+def test_version(lib):
+    assert re.match(rb"^\d+\.\d+\.\d+$", lib.cpattn_version())
+
+
+def _err(lib):
+    return lib.cpattn_last_error().decode()
+
+
+def test_slot_map_refusals(lib):
+    assert lib.cp_slot_map(None, 4, 16, 3, None, None, None) == _lib.CPATTN_EINVAL
+    assert "divide" in _err(lib)
+    assert lib.cp_slot_map(None, 4, 16, 0, None, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, -1, 16, 4, None, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, 4, 16, 4, None, None, None) == _lib.CPATTN_EINVAL   # null pointers
+    assert lib.cp_slot_map(None, 0, 16, 4, None, None, None) == _lib.CPATTN_OK      # nothing to do
+    assert lib.cp_slot_map_rank(None, 4, 16, 4, 4, 0, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map_rank(None, 4, 16, 4, 1, -2, None, None) == _lib.CPATTN_EINVAL
+
+
+def _paged(**kw):
+    a = _lib.PagedArgs()
+    base = dict(kind=0, dtype=1, num_rows=2, num_tokens=2, num_partners=4, stripe_begin=0, stripe_count=4,
+                page_size=16, num_pages=10, num_q_heads=32, num_kv_heads=8, head_dim=128, head_dim_v=128, scale=0.1,
+                max_ctx_len=100, max_row_tokens=1, max_pages=8, bt_stride=8, q_row_start=8, ctx_len=8,
+                block_table=8, q=16, k_pool=16, v_pool=16, out=16, lse=16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(num_partners=3), _lib.CPATTN_EINVAL),
+    (dict(num_q_heads=30), _lib.CPATTN_EINVAL),
+    (dict(stripe_begin=2, stripe_count=3), _lib.CPATTN_EINVAL),
+    (dict(num_pages=0), _lib.CPATTN_EINVAL),
+    (dict(bt_stride=4), _lib.CPATTN_EINVAL),
+    (dict(kind=5), _lib.CPATTN_EINVAL),
+    (dict(dtype=9), _lib.CPATTN_EINVAL),
+    (dict(head_dim=96, head_dim_v=96), _lib.CPATTN_EUNSUPPORTED),
+    (dict(head_dim=128, head_dim_v=64), _lib.CPATTN_EUNSUPPORTED),
+    (dict(kind=1, num_kv_heads=8), _lib.CPATTN_EINVAL),
+    (dict(kind=1, num_kv_heads=1, head_dim=576, head_dim_v=512, v_pool=32), _lib.CPATTN_EINVAL),
+    (dict(kind=1, num_kv_heads=1, head_dim=512, head_dim_v=512), _lib.CPATTN_EUNSUPPORTED),
+    (dict(q=0), _lib.CPATTN_EINVAL),
+    (dict(num_rows=-1), _lib.CPATTN_EINVAL),
+    (dict(kv_stride_page=-8), _lib.CPATTN_EINVAL),
+])
+def test_paged_refusals(lib, bad, code):
+    a = _paged(**bad)
+    assert lib.cp_paged_attn_partial(C.byref(a), None) == code
+    assert _err(lib)
+    n = C.c_int64(-1)
+    assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == code
+
+
+def test_paged_null_args(lib):
+    assert lib.cp_paged_attn_partial(None, None) == _lib.CPATTN_EINVAL
+
+
+def test_paged_workspace_size_is_host_only(lib):
+    # bf16 D=128 decode with split chunks needs a workspace; fp32 (generic path) needs none
+    a = _paged(max_ctx_len=8192, kv_stride_slot=128, kv_stride_head=512, kv_stride_page=4096, kv_stride_stripe=40960,
+               q_stride_token=4096, q_stride_head=128, out_stride_stripe=8192, out_stride_token=4096,
+               out_stride_head=128, lse_stride_stripe=64, lse_stride_token=32)
+    n = C.c_int64(-1)
+    assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == _lib.CPATTN_OK
+    assert n.value > 0
+    # too small a workspace is refused before any launch
+    assert lib.cp_paged_attn_partial(C.byref(a), None) == _lib.CPATTN_EINVAL
+    assert "workspace" in _err(lib)
+    b = _paged(dtype=0)
+    assert lib.cp_paged_attn_workspace_size(C.byref(b), C.byref(n)) == _lib.CPATTN_OK and n.value == 0
+
+
+def test_own_token_refusals(lib):
+    a = _lib.OwnArgs()
+    a.dtype, a.num_rows, a.bucket_tokens, a.num_q_heads, a.num_kv_heads, a.head_dim = 1, 2, 16, 32, 8, 96
+    assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EUNSUPPORTED
+    a.head_dim, a.num_q_heads = 128, 30
+    assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EINVAL
+    a.num_q_heads = 32
+    assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EINVAL       # null pointers
+    a.bucket_tokens = 0
+    assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_OK
+    assert lib.cp_own_token_attn(None, None) == _lib.CPATTN_EINVAL
+
+
+def test_merge_refusals(lib):
+    a = _lib.MergeArgs()
+    a.num_partials, a.num_tokens, a.num_heads, a.head_dim_v = 0, 4, 2, 8
+    assert lib.cp_lse_merge(C.byref(a), None) == _lib.CPATTN_EINVAL
+    a.num_partials = 18
+    assert lib.cp_lse_merge(C.byref(a), None) == _lib.CPATTN_EINVAL
+    a.num_partials, a.head_dim_v = 2, 6
+    assert lib.cp_lse_merge(C.byref(a), None) == _lib.CPATTN_EINVAL
+    a.head_dim_v, a.out = 8, 64
+    a.part_out[0], a.part_lse[0] = 64, 128
+    a.part_out[1], a.part_lse[1] = 256, 512
+    assert lib.cp_lse_merge(C.byref(a), None) == _lib.CPATTN_EINVAL           # out aliases partial 0
+    assert "alias" in _err(lib)
+    a.out_dtype = 7
+    assert lib.cp_lse_merge(C.byref(a), None) == _lib.CPATTN_EINVAL
+    assert lib.cp_lse_merge(None, None) == _lib.CPATTN_EINVAL
+
+
+def test_kv_write_refusals(lib):
+    args = [None, 4, None, None, 0, 0, 1, 8, 128, 128, None, None, 0, 0, 0, 0, 16, 4, 10, 0, 4, -1, None]
+    bad = list(args)
+    bad[17] = 3                                                               # P does not divide page_size
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
+    bad = list(args)
+    bad[20] = 5                                                               # stripe range past P
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
+    bad = list(args)
+    bad[21] = 10 * 4                                                          # sink outside the pool
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
+    assert lib.cp_kv_write(*args) == _lib.CPATTN_EINVAL                      # null pointers
+    bad = list(args)
+    bad[1] = 0
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_OK
+
+
+def test_debug_gather_refusals(lib):
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 4, 1, 8, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 8, None, None) == _lib.CPATTN_OK

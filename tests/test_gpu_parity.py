@@ -1,0 +1,197 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from cp_slot_map_amd import api, pool
+from tests.gpu_helpers import check_lse, check_out, check_padding, compare_rows, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+# ------------------------------------------------------------------------------------------- integer paths
+@pytest.mark.parametrize("page_size,P", [(16, 1), (16, 2), (16, 4), (16, 8), (16, 16), (64, 4), (48, 4), (6, 3)])
+def test_slot_map_bit_exact(page_size, P):
+    say(f"slot_map page_size={page_size} P={P}")
+    rng = np.random.default_rng(page_size * 31 + P)
+    s = np.concatenate([rng.integers(-5, 1 << 40, size=5000), np.arange(-3, 300), [0, (1 << 62) + 7]])
+    partner, phys = api.slot_map(torch.from_numpy(s).to(DEV), page_size, P)
+    rp, rq = oracle.slot_map(s, page_size, P)
+    assert np.array_equal(partner.cpu().numpy().astype(np.int64), rp)
+    assert np.array_equal(phys.cpu().numpy(), rq)
+    for rank in range(P):
+        w = api.slot_map_rank(torch.from_numpy(s).to(DEV), page_size, P, rank, 3)
+        assert np.array_equal(w.cpu().numpy(), oracle.slot_map_rank(s, page_size, P, rank, 3))
+
+
+def test_slot_map_empty_and_errors():
+    p, q = api.slot_map(torch.empty(0, dtype=torch.int64, device=DEV), 16, 4)
+    assert p.numel() == 0 and q.numel() == 0
+    with pytest.raises(RuntimeError):
+        api.slot_map(torch.zeros(4, dtype=torch.int64, device=DEV), 16, 3)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("llama8b", dict(batch=3, ctx_lengths=[1, 37, 301])),
+    ("longctx", dict(batch=3, ctx_lengths=[3, 50, 129])),
+    ("mla", dict(batch=2, ctx_lengths=[5, 200])),
+])
+@pytest.mark.parametrize("layout", ["hnd", "nhd"])
+def test_write_path_and_page_addressing_bit_exact(name, kw, layout):
+    """kv_write places every token by the slot rule; the kernels' addressing reads stripe r back as positions r::P."""
+    wl = workloads.make(name, **kw)
+    if wl.kind == "mla" and layout == "nhd":
+        pytest.skip("MLA pools have one layout")
+    say(f"write path {name} {layout}")
+    batch = pool.build_batch(wl, DEV, layout=layout)
+    P, ps = wl.partners, wl.page_size
+    for b in range(wl.batch):
+        rv = workloads.row_values(wl, b, DEV)
+        c = int(wl.ctx_len[b])
+        for r in range(P):
+            got = api.debug_gather_stripe(batch.k_pool, batch.block_table[b], c, ps, P, r, kind=wl.kind)
+            want = rv.k_ctx[r::P]
+            assert got.shape == want.shape
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32))
+    # the whole pool, NaN where the oracle's placement leaves a slot untouched
+    rows = [workloads.row_values(wl, b, DEV).k_ctx.cpu().double().numpy().reshape(int(wl.ctx_len[b]), -1)
+            for b in range(wl.batch)]
+    ref = oracle.place_logical_rows(rows, wl.block_table, wl.ctx_len, ps, P, wl.num_pages)
+    pp = ps // P
+    kp = batch.k_pool.double().cpu().numpy()
+    for r in range(P):
+        got = kp[r].reshape(wl.num_pages * pp, -1)
+        assert np.array_equal(np.isnan(got), np.isnan(ref[r]))
+        fin = ~np.isnan(ref[r])
+        assert np.array_equal(got[fin], ref[r][fin])
+
+
+# ----------------------------------------------------------------------------------------------- merge
+def test_merge_edge_cases():
+    say("merge edge cases")
+    g = torch.Generator(device=DEV).manual_seed(5)
+    T, H, Dv, N = 37, 6, 128, 5
+    outs = [torch.randn(T, H, Dv, generator=g, device=DEV) for _ in range(N)]
+    lses = [torch.randn(T, H, generator=g, device=DEV) * 3 for _ in range(N)]
+    lses[1][:5] = -float("inf")
+    outs[1][:5] = float("nan")                 # an empty partial's row is never read
+    for i in range(N):
+        lses[i][7] = -float("inf")             # token 7: every partial empty
+    mo, ml = api.lse_merge(outs, lses)
+    ro, rl = oracle.merge([o.cpu() for o in outs[:1]] + [torch.where(torch.isnan(outs[1]), 0, outs[1]).cpu()]
+                          + [o.cpu() for o in outs[2:]], [l.cpu() for l in lses])
+    check_out(mo, ro, "merge out")
+    check_lse(ml, rl, "merge lse")
+    assert torch.all(mo[7] == 0) and torch.all(torch.isneginf(ml[7]))
+    # bf16 output is the round-to-nearest-even of the fp32 merge
+    mb, _ = api.lse_merge(outs, lses, out_dtype=torch.bfloat16)
+    assert torch.equal(mb, mo.to(torch.bfloat16))
+    # padding tokens given by a device count are written as (0, -inf) without reading
+    cnt = torch.tensor([20], dtype=torch.int32, device=DEV)
+    po, pl = api.lse_merge(outs, lses, token_count=cnt)
+    assert torch.equal(po[:20], mo[:20]) and torch.all(po[20:] == 0) and torch.all(torch.isneginf(pl[20:]))
+    # one partial is the identity; an empty partial changes nothing
+    io, il = api.lse_merge(outs[:1], lses[:1])
+    live = torch.isfinite(lses[0])
+    assert torch.equal(io[live], outs[0][live]) and torch.equal(il[live], lses[0][live])
+    assert torch.all(io[~live] == 0) and torch.all(torch.isneginf(il[~live]))
+
+
+# ------------------------------------------------------------------------------------ attention parity
+SMALL = [
+    ("tiny", {}),
+    ("llama8b", dict(batch=7, ctx_lengths=[1, 3, 4, 17, 255, 1031, 4100])),
+    ("longctx", dict(batch=4, ctx_lengths=[5, 100, 4097, 9001])),
+    ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000])),
+    ("mixed", dict(batch=6, new_lengths=[1, 1, 5, 33, 1, 70], ctx_lengths=[0, 19, 0, 300, 1000, 2100], pad_rows=2)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_step_parity_small(name, kw):
+    wl = workloads.make(name, **kw)
+    say(f"step parity {name} B={wl.batch} ctx={list(wl.ctx_len)} new={list(wl.new_len)}")
+    batch = pool.build_batch(wl, DEV)                      # NaN in every slot that holds no token
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_nan_poison_is_bit_identical_to_zero_fill(name, kw):
+    """Slots, pages, queries and in-step K/V that hold no real token are never read: NaN there changes no bit."""
+    wl = workloads.make(name, **kw)
+    say(f"poison {name}")
+    a = pool.run_step(pool.build_batch(wl, DEV, fill=float("nan")))
+    b = pool.run_step(pool.build_batch(wl, DEV, fill=0.0))
+    t = wl.num_tokens
+    assert torch.equal(a[0][:t], b[0][:t]) and torch.equal(a[1][:t], b[1][:t])
+    assert torch.equal(a[2][:, :t], b[2][:, :t]) and torch.equal(a[3][:, :t], b[3][:, :t])
+    check_padding(wl, a)
+
+
+def test_stripe_subset_matches_all_stripes():
+    """One rank's share (stripe_begin, stripe_count = 1) equals the same stripe of the all-stripes call."""
+    wl = workloads.make("llama8b", batch=5, ctx_lengths=[9, 400, 1100, 3000, 64])
+    batch = pool.build_batch(wl, DEV)
+    _, _, po, pl, _ = pool.run_step(batch)
+    for r in range(wl.partners):
+        o, l = api.paged_attn_partial(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
+                                      batch.block_table, page_size=wl.page_size, partners=wl.partners,
+                                      scale=wl.scale, stripe_begin=r, stripe_count=1,
+                                      max_ctx_len=batch.max_ctx_len, max_row_tokens=1)
+        assert torch.equal(o[0], po[r]) and torch.equal(l[0], pl[r])
+
+
+def test_repeat_calls_are_deterministic():
+    """Split chunks merged by the last arriver give the same bits on every call (the counters reset themselves)."""
+    wl = workloads.make("llama8b", batch=4, ctx_lengths=[8192, 5000, 2000, 7777])
+    batch = pool.build_batch(wl, DEV)
+    first = pool.run_step(batch)
+    for _ in range(3):
+        again = pool.run_step(batch)
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+
+
+def test_empty_batch_and_empty_context():
+    wl = workloads.make("llama8b", batch=3, ctx_lengths=[0, 0, 2])
+    batch = pool.build_batch(wl, DEV)
+    mo, ml, po, pl, _ = pool.run_step(batch)
+    assert torch.all(mo[:2] == 0) and torch.all(torch.isneginf(ml[:2]))
+    assert torch.all(torch.isneginf(pl[2:, 2]))          # stripes 2, 3 of a 2-token row are empty
+    compare_rows(wl, batch, (mo, ml, po, pl, None), [2], DEV)
+
+
+# ------------------------------------------------------------------------- full sizes, sampled rows
+FULL = [("tiny", None), ("llama8b", 6), ("longctx", 4), ("mla", 3), ("mixed", 5)]
+
+
+@pytest.mark.parametrize("name,nsample", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_rows(name, nsample):
+    wl = workloads.make(name)
+    say(f"full size {name}: B={wl.batch} ctx tokens={int(wl.ctx_len.sum())}")
+    batch = pool.build_batch(wl, DEV, fill=0.0)
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    if nsample is None:
+        rows = range(wl.batch)
+    else:
+        order = np.argsort(wl.ctx_len + wl.new_len)
+        rng = np.random.default_rng(7)
+        rows = sorted(set([int(order[0]), int(order[-1])] +
+                          [int(x) for x in rng.choice(wl.batch, size=nsample - 2, replace=False)]))
+    w = compare_rows(wl, batch, res, rows, DEV, check_partials=True)
+    check_padding(wl, res)
+    say(f"  rows {list(rows)} worst {w}")
+    # properties at every token: finite outputs, lse finite for rows with context or own tokens
+    t = wl.num_tokens
+    assert torch.isfinite(res[0][:t]).all() and torch.isfinite(res[1][:t]).all()
+    del batch, res
+    torch.cuda.empty_cache()
