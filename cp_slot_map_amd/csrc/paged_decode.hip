@@ -7,10 +7,11 @@
 //
 // Work decomposition. A work item is (row b, stripe s, kv head g, tile of 16 query rows, chunk of the stripe's local
 // tokens); one 64-lane wave runs it. Query rows of a kv head are (token, head-in-group) pairs, so a decode step with
-// G = 4 fills 4 rows of the 16 and a multi-token row fills more. Chunks of one (b, s, g, tile) write their
-// unnormalised partial to the workspace; the last one to arrive (device-scope counter) merges them exactly and writes
-// the stripe partial, then clears the counter. Block ids are remapped so the chunks of one item run on one XCD (the
-// hardware hands block i to XCD i mod 8), keeping workspace records in that XCD's L2.
+// G = 4 fills 4 rows of the 16 and a multi-token row fills more. Fixed-size chunks keep every wave busy for about the
+// same time whatever the spread of context lengths. An item whose stripe fits in one chunk writes the stripe partial
+// directly; otherwise each chunk writes its unnormalised partial (o, running max, running sum) to the workspace and a
+// second small kernel merges the chunks of each item exactly. The kernel boundary orders the two, so no device-scope
+// fence is needed (such fences write back and invalidate a whole XCD L2, which costs far more than the extra launch).
 //
 // Per step of 16 local tokens:
 //   * scores S^T[token][row] = K . Q^T with four v_mfma_f32_16x16x32_bf16 (k = 32 head dims each). Lane l feeds token
@@ -29,11 +30,8 @@
 
 namespace cpattn {
 
-constexpr int kDecodeMaxChunkPages = 320;
-// Completion counters occupy a fixed region at the start of the workspace, the same positions for every call shape,
-// so a call never finds another call's records where its counters should be. Each call leaves its counters at zero.
-constexpr int64_t kCounterBytes = int64_t(4) << 20;
-constexpr int64_t kMaxCounters = kCounterBytes / 4;
+constexpr int kDecodeMaxChunkPages = 520;
+
 
 struct DecodeParams {
     const uint16_t* q;
@@ -50,7 +48,6 @@ struct DecodeParams {
     float* lse;
     int64_t l_ss, l_st;
     float* ws_rec;
-    int32_t* ws_cnt;
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G;
     int32_t max_pages, page_size, max_row_tokens;
     int32_t n_qtiles, n_chunks, chunk_steps;
@@ -59,46 +56,47 @@ struct DecodeParams {
     float scale_log2;
 };
 
+// s_waitcnt with vmcnt = 0 and the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]).
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Pool element offsets of this lane's step loads: K token jb + l%16 (dim block 8*(l/16)), V tokens jb + 4*(l/16) + e
-// (dim block 8*(l%16)). Page ids come from the chunk's LDS copy of the block table; tokens past the chunk end are
-// clamped to its last page (their values are discarded).
-struct StepAddr {
-    int64_t k;
-    int64_t v[4];
-};
-
-__device__ __forceinline__ StepAddr step_addr(const int32_t* s_pages, int32_t pg0, int32_t npg, int32_t jb,
-                                              int32_t n16, int32_t c4, int32_t r, int32_t g, const PoolGeom& geo) {
-    StepAddr a;
-    {
-        const int32_t j = jb + n16;
-        const int32_t pidx = min((j >> geo.pp_shift) - pg0, npg - 1);
-        a.k = page_slot_offset(s_pages[pidx], j & (geo.pp - 1), r, g, geo) + 8 * c4;
-    }
+// Load mapping. Instruction e of a step reads, for K and V alike, the step tokens 4e + l/16 at head dims
+// [8*(l%16), +8): sixteen lanes cover one 256-byte row and the 64 lanes four consecutive tokens, i.e. one contiguous
+// stretch of a page (a whole page of one head when page_size / P = 4). Fragmenting an instruction over several pages
+// costs a large share of HBM bandwidth, so each instruction stays inside one page wherever the page allows. K and V
+// pools share their layout, so one set of offsets serves both. Page ids come from the chunk's LDS copy of the block
+// table; tokens past the chunk end are clamped to its last page and their values are discarded.
+//
+// Token order inside a step. The value product contracts over k = 4*(l/16) + e, which this mapping ties to step token
+// 4e + l/16. Score row m of the MFMA is therefore given token sigma(m) = 4(m mod 4) + m/4, which puts the probability
+// of token 4e + l/16 exactly where the value operand expects it.
+__device__ __forceinline__ void step_offsets(int64_t (&off)[4], const int32_t* s_pages, int32_t pg0, int32_t npg,
+                                             int32_t jb, int32_t c4, int64_t base_rg, const PoolGeom& geo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int32_t j = jb + 4 * c4 + e;
+        const int32_t j = jb + 4 * e + c4;
         const int32_t pidx = min((j >> geo.pp_shift) - pg0, npg - 1);
-        a.v[e] = page_slot_offset(s_pages[pidx], j & (geo.pp - 1), r, g, geo) + 8 * n16;
+        int32_t page = s_pages[pidx];
+        page = (page >= 0 && page < geo.num_pages) ? page : 0;
+        off[e] = base_rg + int64_t(page) * geo.s_page + int64_t(j & (geo.pp - 1)) * geo.s_slot;
     }
-    return a;
 }
 
 struct StepData {
-    u32x4_t k[4];
+    u32x4_t k[4];      // step token 4e + l/16, dims [8*(l%16), +8)
     u32x4_t v[4];
 };
 
 __device__ __forceinline__ void step_load(StepData& d, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, const StepAddr& a) {
+                                          const uint16_t* __restrict__ vp, const int64_t (&off)[4], int32_t n16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.k[i] = load16(kp + a.k + 32 * i);
+    for (int e = 0; e < 4; ++e) d.k[e] = load16(kp + off[e] + 8 * n16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + a.v[e]);
+    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + off[e] + 8 * n16);
 }
 
 struct SoftmaxState {
@@ -107,18 +105,33 @@ struct SoftmaxState {
     float l;           // this lane's share of the running sum of query row l%16
 };
 
+// LDS slot (16-byte units) of step token t, head-dim block j, in the K re-layout buffer. The XOR with t spreads both
+// the row-wise writes and the column-wise MFMA-operand reads over all bank groups.
+__device__ __forceinline__ int kx_index(int t, int j) { return (t & 3) * 64 + (t >> 2) * 16 + (j ^ t); }
+
+__device__ __forceinline__ int sigma(int m) { return 4 * (m & 3) + (m >> 2); }
+
 __device__ __forceinline__ void step_compute(SoftmaxState& st, const StepData& d, const bf16x8_t (&qop)[4],
-                                             int32_t jb, int32_t j1, int32_t c4, float scale_log2, int lane) {
+                                             u32x4_t* __restrict__ kx, int32_t jb, int32_t j1, int32_t n16,
+                                             int32_t c4, float scale_log2) {
+    // K from load layout (token per lane group, dims across lanes) to A-operand layout (token sigma(l%16) per lane,
+    // dim block per lane group) through LDS. LDS operations of one wave complete in order: no barrier is needed.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kx[kx_index(4 * e + c4, n16)] = d.k[e];
+    u32x4_t kop[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kop[i] = kx[kx_index(sigma(n16), 4 * i + c4)];
+
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(d.k[i]), qop[i], sacc, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[i]), qop[i], sacc, 0, 0, 0);
 
     const bool tail = jb + 16 > j1;  // wave-uniform
     float sv[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-        sv[ii] = sacc[ii] * scale_log2;
-        if (tail && jb + 4 * c4 + ii >= j1) sv[ii] = neg_inf();
+        sv[ii] = sacc[ii] * scale_log2;          // score of step token 4*ii + l/16
+        if (tail && jb + 4 * ii + c4 >= j1) sv[ii] = neg_inf();
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -158,7 +171,7 @@ __device__ __forceinline__ void step_compute(SoftmaxState& st, const StepData& d
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         v[e] = d.v[e];
-        if (tail && jb + 4 * c4 + e >= j1) v[e] = (u32x4_t){0u, 0u, 0u, 0u};   // select, never 0 * NaN
+        if (tail && jb + 4 * e + c4 >= j1) v[e] = (u32x4_t){0u, 0u, 0u, 0u};   // select, never 0 * NaN
     }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -170,7 +183,6 @@ __device__ __forceinline__ void step_compute(SoftmaxState& st, const StepData& d
         st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, vop, st.o[n], 0, 0, 0);
         st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop_lo, vop, st.o[n], 0, 0, 0);
     }
-    (void)lane;
 }
 
 __device__ __forceinline__ void write_row(const DecodeParams& p, int32_t s, int32_t tok0, int32_t row0, int32_t g,
@@ -191,8 +203,10 @@ __device__ __forceinline__ void write_lse(const DecodeParams& p, int32_t s, int3
     p.lse[s * p.l_ss + int64_t(t) * p.l_st + h] = l > 0.f ? (m_log2 + log2f(l)) * kLn2 : neg_inf();
 }
 
+template <int DEPTH>
 __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams p) {
     __shared__ int32_t s_pages[kDecodeMaxChunkPages];
+    __shared__ u32x4_t s_kx[256];
     const int lane = threadIdx.x;
     const int32_t nb = gridDim.x;                 // a multiple of 8
     const int32_t bid = blockIdx.x;
@@ -208,16 +222,16 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         return;
     }
 
+    // Item order (kv head fastest, then chunk, tile, stripe, row): the heads of one page run side by side.
     int32_t item = logical;
+    const int32_t g = item % p.Hkv;
+    item /= p.Hkv;
     const int32_t c = item % p.n_chunks;
     item /= p.n_chunks;
     const int32_t qt = item % p.n_qtiles;
     item /= p.n_qtiles;
-    const int32_t g = item % p.Hkv;
-    item /= p.Hkv;
     const int32_t s = item % p.S;
     const int32_t b = item / p.S;
-    const int32_t triple = logical / p.n_chunks;
 
     const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
     const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
@@ -258,6 +272,10 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
     const int32_t pg0 = j0 >> p.geo.pp_shift;
     const int32_t npg = j1 > j0 ? ((j1 - 1) >> p.geo.pp_shift) - pg0 + 1 : 1;
     for (int32_t k = lane; k < npg; k += 64) s_pages[k] = j1 > j0 ? bt_row[pg0 + k] : 0;
+    // Retire the query and block-table loads here, before the first prefetch is issued: the wait-count pass cannot
+    // tell, inside the loop, that these older loads finished, and would otherwise drain every outstanding load
+    // (the prefetched steps included) before the first use of the query operand in each iteration.
+    wait_all_vmem();
     __syncthreads();
 
     SoftmaxState st;
@@ -266,19 +284,30 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
     st.m = neg_inf();
     st.l = 0.f;
 
+    // Ring of DEPTH register buffers: the loads of step k + DEPTH - 1 are in flight while step k is computed. Every
+    // prefetch is issued unconditionally (a step past the end re-reads the chunk's last step, a cache hit), so the
+    // number of loads in flight is the same on every path and each wait only retires the step about to be used.
+    const int64_t base_rg = int64_t(r) * p.geo.s_stripe + int64_t(g) * p.geo.s_head;
     const int32_t nsteps = (j1 - j0 + 15) >> 4;
-    if (nsteps > 0) {
-        StepData da, db;
-        step_load(da, p.kp, p.vp, step_addr(s_pages, pg0, npg, j0, n16, c4, r, g, p.geo));
-        int32_t it = 0;
-        for (; it + 2 <= nsteps; it += 2) {
-            const int32_t jb = j0 + it * 16;
-            step_load(db, p.kp, p.vp, step_addr(s_pages, pg0, npg, jb + 16, n16, c4, r, g, p.geo));
-            step_compute(st, da, qop, jb, j1, c4, p.scale_log2, lane);
-            if (it + 2 < nsteps) step_load(da, p.kp, p.vp, step_addr(s_pages, pg0, npg, jb + 32, n16, c4, r, g, p.geo));
-            step_compute(st, db, qop, jb + 16, j1, c4, p.scale_log2, lane);
+    const int32_t last = max(nsteps - 1, 0);
+    StepData buf[DEPTH];
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) {
+        int64_t off[4];
+        step_offsets(off, s_pages, pg0, npg, j0 + 16 * min(u, last), c4, base_rg, p.geo);
+        step_load(buf[u], p.kp, p.vp, off, n16);
+    }
+    for (int32_t it = 0; it < nsteps; it += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+            const int32_t k = it + u;
+            {
+                int64_t off[4];
+                step_offsets(off, s_pages, pg0, npg, j0 + 16 * min(k + DEPTH - 1, last), c4, base_rg, p.geo);
+                step_load(buf[(u + DEPTH - 1) % DEPTH], p.kp, p.vp, off, n16);
+            }
+            if (k < nsteps) step_compute(st, buf[u], qop, s_kx, j0 + 16 * k, j1, n16, c4, p.scale_log2);
         }
-        if (it < nsteps) step_compute(st, da, qop, j0 + it * 16, j1, c4, p.scale_log2, lane);
     }
 
     // Row sums: combine the four lane groups that share a query row.
@@ -307,10 +336,9 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         return;
     }
 
-    // Several chunks: store this chunk's unnormalised record, then the last arriver merges.
+    // Several chunks: store this chunk's unnormalised record; gqa_decode_chunk_merge_kernel combines them.
     const int32_t RR = p.rec_rows;
-    const int64_t rec_floats = int64_t(RR) * 130;
-    float* rec = p.ws_rec + int64_t(logical) * rec_floats;
+    float* rec = p.ws_rec + int64_t(logical) * RR * 130;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         const int32_t row = 4 * c4 + ii;
@@ -324,41 +352,56 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         rec[RR * 128 + n16] = st.m;
         rec[RR * 128 + RR + n16] = st.l;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    int32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(p.ws_cnt + triple, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0);
-    if (old != nch - 1) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
-    const float* rec0 = p.ws_rec + int64_t(triple) * p.n_chunks * rec_floats;
-    // Rows of the O layout (4*c4 + ii) and the lse row (n16) are merged independently.
-    float M_o[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-    float M_r = neg_inf();
-    for (int32_t cc = 0; cc < nch; ++cc) {
-        const float* rc = rec0 + cc * rec_floats + RR * 128;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int32_t row = 4 * c4 + ii;
-            if (row < tile_rows) M_o[ii] = fmaxf(M_o[ii], rc[row]);
-        }
-        if (n16 < tile_rows) M_r = fmaxf(M_r, rc[n16]);
-    }
+// Exact merge of the chunk records of every item that needed more than one chunk: with M = max_c m_c,
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c and lse = (M + log2 sum_c 2^(m_c - M) l_c) ln 2.
+// One wave per (row, stripe, kv head, query tile); lanes hold the same (row, dim) layout as the chunk kernel.
+__global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x;
+    const int32_t triple = blockIdx.x;            // (row, stripe, tile) * Hkv + kv head
+    const int32_t g = triple % p.Hkv;
+    int32_t item = triple / p.Hkv;
+    const int32_t tile = item;                     // (row * S + stripe) * n_qtiles + tile
+    const int32_t qt = item % p.n_qtiles;
+    item /= p.n_qtiles;
+    const int32_t s = item % p.S;
+    const int32_t b = item / p.S;
+    if (b >= p.B) return;
+    const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
+    const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
+    const int32_t row0 = qt * 16;
+    if (row0 >= nrows) return;
+    const int32_t tile_rows = min(16, nrows - row0);
+    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P);
+    const int32_t CH = p.chunk_steps * 16;
+    const int32_t nch = (Lr + CH - 1) / CH;
+    if (nch <= 1) return;                       // written directly by the chunk kernel
+    const int32_t n16 = lane & 15, c4 = lane >> 4;
+    const int32_t RR = p.rec_rows;
+    const int64_t rec_floats = int64_t(RR) * 130;
+    // Chunk c of this item is record ((tile * n_chunks + c) * Hkv + g).
+    const float* rec0 = p.ws_rec + (int64_t(tile) * p.n_chunks * p.Hkv + g) * rec_floats;
+    const int64_t rec_step = int64_t(p.Hkv) * rec_floats;
+    constexpr int kMaxUnrolled = 16;   // items with up to this many chunks keep every chunk's max and sum in registers
+
+    float M_o[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()}, L_o[4] = {0.f, 0.f, 0.f, 0.f};
+    float M_r = neg_inf(), L_r = 0.f;
     float acc[4][8];
-    float L_o[4] = {0.f, 0.f, 0.f, 0.f};
-    float L_r = 0.f;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[ii][n] = 0.f;
-    for (int32_t cc = 0; cc < nch; ++cc) {
-        const float* rc = rec0 + cc * rec_floats;
+
+    auto add_chunk = [&](const float* rc, const float (&mo)[4], const float (&lo)[4], float mr, float lr) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int32_t row = 4 * c4 + ii;
             if (row < tile_rows) {
-                const float w = exp2f(rc[RR * 128 + row] - M_o[ii]);
-                L_o[ii] += w * rc[RR * 128 + RR + row];
+                const float w = exp2f(mo[ii] - M_o[ii]);
+                L_o[ii] += w * lo[ii];
                 const f32x4_t a = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16);
                 const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16 + 4);
 #pragma unroll
@@ -368,7 +411,60 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
                 }
             }
         }
-        if (n16 < tile_rows) L_r += exp2f(rc[RR * 128 + n16] - M_r) * rc[RR * 128 + RR + n16];
+        if (n16 < tile_rows) L_r += exp2f(mr - M_r) * lr;
+    };
+
+    if (nch <= kMaxUnrolled) {
+        // Every chunk's maxima and sums are loaded together (static indices keep them in registers).
+        float m_o[kMaxUnrolled][4], l_o[kMaxUnrolled][4], m_r[kMaxUnrolled], l_r[kMaxUnrolled];
+#pragma unroll
+        for (int cc = 0; cc < kMaxUnrolled; ++cc) {
+            const float* rc = rec0 + cc * rec_step + RR * 128;
+            const bool live = cc < nch;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int32_t row = 4 * c4 + ii;
+                const bool ok = live && row < tile_rows;
+                m_o[cc][ii] = ok ? rc[row] : neg_inf();
+                l_o[cc][ii] = ok ? rc[RR + row] : 0.f;
+            }
+            m_r[cc] = (live && n16 < tile_rows) ? rc[n16] : neg_inf();
+            l_r[cc] = (live && n16 < tile_rows) ? rc[RR + n16] : 0.f;
+        }
+#pragma unroll
+        for (int cc = 0; cc < kMaxUnrolled; ++cc) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) M_o[ii] = fmaxf(M_o[ii], m_o[cc][ii]);
+            M_r = fmaxf(M_r, m_r[cc]);
+        }
+        // Values four chunks at a time.
+#pragma unroll
+        for (int cg = 0; cg < kMaxUnrolled; cg += 4) {
+            if (cg >= nch) break;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (cg + u < nch) add_chunk(rec0 + (cg + u) * rec_step, m_o[cg + u], l_o[cg + u], m_r[cg + u], l_r[cg + u]);
+        }
+    } else {
+        for (int32_t cc = 0; cc < nch; ++cc) {
+            const float* rc = rec0 + cc * rec_step + RR * 128;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                if (4 * c4 + ii < tile_rows) M_o[ii] = fmaxf(M_o[ii], rc[4 * c4 + ii]);
+            if (n16 < tile_rows) M_r = fmaxf(M_r, rc[n16]);
+        }
+        for (int32_t cc = 0; cc < nch; ++cc) {
+            const float* rc = rec0 + cc * rec_step;
+            float mo[4], lo[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int32_t row = min(4 * c4 + ii, RR - 1);
+                mo[ii] = rc[RR * 128 + row];
+                lo[ii] = rc[RR * 128 + RR + row];
+            }
+            const int32_t rr = min(n16, RR - 1);
+            add_chunk(rc, mo, lo, rc[RR * 128 + rr], rc[RR * 128 + RR + rr]);
+        }
     }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -382,7 +478,6 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         }
     }
     if (c4 == 0 && n16 < tile_rows) write_lse(p, s, tok0, row0, g, n16, M_r, L_r);
-    if (lane == 0) p.ws_cnt[triple] = 0;   // ready for the next call
 }
 
 static int32_t decode_chunk_steps() {
@@ -390,10 +485,20 @@ static int32_t decode_chunk_steps() {
         const char* e = std::getenv("CPATTN_DECODE_CHUNK_STEPS");
         int v = e ? std::atoi(e) : 16;
         if (v < 1) v = 1;
-        if (v > 16) v = 16;
+        if (v > 32) v = 32;
         return v;
     }();
     return steps;
+}
+
+// Prefetch depth of the step ring (2 or 3 buffers of 8 KB per wave).
+static int32_t decode_depth() {
+    static int32_t depth = [] {
+        const char* e = std::getenv("CPATTN_DECODE_DEPTH");
+        int v = e ? std::atoi(e) : 3;
+        return v == 2 ? 2 : 3;
+    }();
+    return depth;
 }
 
 struct DecodeShape {
@@ -409,7 +514,6 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
     const int64_t CH = int64_t(decode_chunk_steps()) * 16;
     d.n_chunks = std::max<int64_t>(1, (max_lr + CH - 1) / CH);
     d.triples = int64_t(a.num_rows) * a.stripe_count * a.num_kv_heads * d.n_qtiles;
-    if (d.triples > kMaxCounters) d.n_chunks = 1;   // too many items to count: no split, no workspace
     d.total_items = d.triples * d.n_chunks;
     const int64_t rr = std::min<int64_t>(16, rows);
     d.rec_rows = std::max<int64_t>(4, (rr + 3) / 4 * 4);
@@ -435,7 +539,7 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a) {
     const DecodeShape d = decode_shape(a);
     if (d.n_chunks <= 1) return 0;
-    return kCounterBytes + d.total_items * d.rec_rows * 130 * 4;
+    return d.total_items * d.rec_rows * 130 * 4;
 }
 
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
@@ -458,10 +562,7 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.lse = a.lse;
     p.l_ss = a.lse_stride_stripe;
     p.l_st = a.lse_stride_token;
-    if (d.n_chunks > 1) {
-        p.ws_cnt = static_cast<int32_t*>(a.workspace);
-        p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + kCounterBytes);
-    }
+    if (d.n_chunks > 1) p.ws_rec = static_cast<float*>(a.workspace);
     p.B = a.num_rows;
     p.T = a.num_tokens;
     p.P = a.num_partners;
@@ -483,8 +584,17 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.scale_log2 = a.scale * kLog2e;
     const int64_t blocks = ((d.total_items + p.pad_blocks) + 7) / 8 * 8;
     if (blocks == 0) return CPATTN_OK;
-    hipLaunchKernelGGL(gqa_decode_bf16_kernel, dim3(uint32_t(blocks)), dim3(64), 0, stream, p);
-    return check_launch("cp_paged_attn_partial (bf16 decode)");
+    const dim3 grid{uint32_t(blocks), 1, 1};
+    if (decode_depth() == 2)
+        hipLaunchKernelGGL((gqa_decode_bf16_kernel<2>), grid, dim3(64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gqa_decode_bf16_kernel<3>), grid, dim3(64), 0, stream, p);
+    if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode)")) return st;
+    if (d.n_chunks > 1 && d.triples > 0) {
+        hipLaunchKernelGGL(gqa_decode_chunk_merge_kernel, dim3(uint32_t(d.triples)), dim3(64), 0, stream, p);
+        return check_launch("cp_paged_attn_partial (chunk merge)");
+    }
+    return CPATTN_OK;
 }
 
 }  // namespace cpattn

@@ -156,10 +156,9 @@ typedef struct cp_paged_args {
     int64_t out_stride_stripe, out_stride_token, out_stride_head;
     float* lse;
     int64_t lse_stride_stripe, lse_stride_token;
-    void* workspace;          /* device scratch of cp_paged_attn_workspace_size() bytes (NULL if that is 0). Its
-                                 first 4 MiB hold completion counters that must be zero before the first call; every
-                                 call leaves them zero when it completes. The rest is overwritten freely. Calls that
-                                 share a workspace must not run concurrently. */
+    void* workspace;          /* device scratch of cp_paged_attn_workspace_size() bytes (NULL if that is 0); no
+                                 initial contents are required and it holds nothing useful after the call. Calls
+                                 that share a workspace must be ordered (e.g. on one stream). */
     int64_t workspace_bytes;
 } cp_paged_args;
 
