@@ -3,7 +3,8 @@
 // The partials of a partitioned key set recombine exactly (mstar PR #1124, "Context / Sequence Parallel 1/5", PR
 // description; dcp_combine and merge_attn_states in the vLLM compare view "[Core] Add explicit layer parallel plans",
 // FlashAttentionImpl._forward_with_dcp): with M = max_i lse_i, lse = M + log sum_i exp(lse_i - M) and
-// out = sum_i exp(lse_i - lse) * o_i. Empty partials (lse = -inf) weigh zero and are never read.
+// out = sum_i exp(lse_i - lse) * o_i. Empty partials (lse = -inf) weigh zero and are selected out, so their rows never
+// reach the result.
 //
 // HBM-bound: one thread per (token, head, 4 dims) reads N float4 and N lse values (the lse loads hit cache across the
 // Dv/4 threads of a (token, head)) and writes one float4 (or 4 bf16).
@@ -34,39 +35,39 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int32_t h = int32_t(th % p.H);
     const int32_t t = int32_t(th / p.H);
 
+    // All loads are issued before any is used (one memory round trip). A partial whose lse is -inf is selected out,
+    // never multiplied, so whatever its out row holds cannot reach the result.
+    const bool padding = p.token_count != nullptr && t >= *p.token_count;
     float l[CPATTN_MAX_PARTIALS];
-    float M = neg_inf();
-    bool padding = p.token_count != nullptr && t >= *p.token_count;
-    if (!padding) {
+    f32x4_t o[CPATTN_MAX_PARTIALS];
 #pragma unroll
-        for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
-            if (i < p.N) {
-                l[i] = p.lse_i[i][int64_t(t) * p.l_st[i] + int64_t(h) * p.l_sh[i]];
-                M = fmaxf(M, l[i]);
-            }
+    for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
+        if (i < p.N && !padding) {
+            l[i] = p.lse_i[i][int64_t(t) * p.l_st[i] + int64_t(h) * p.l_sh[i]];
+            o[i] = *reinterpret_cast<const f32x4_t*>(p.out_i[i] + int64_t(t) * p.o_st[i] + int64_t(h) * p.o_sh[i] + 4 * d4);
+        } else {
+            l[i] = neg_inf();
+            o[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         }
     }
+    float M = neg_inf();
+#pragma unroll
+    for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) M = fmaxf(M, l[i]);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lse = neg_inf();
-    if (!padding && M != neg_inf()) {
+    if (M != neg_inf()) {
         float w[CPATTN_MAX_PARTIALS];
         float tot = 0.f;
 #pragma unroll
         for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
-            if (i < p.N) {
-                w[i] = l[i] == neg_inf() ? 0.f : expf(l[i] - M);
-                tot += w[i];
-            }
+            w[i] = l[i] == neg_inf() ? 0.f : expf(l[i] - M);
+            tot += w[i];
         }
         const float inv = 1.0f / tot;
 #pragma unroll
         for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
-            if (i < p.N && w[i] != 0.f) {      // select, never multiply: an empty partial's row is not read
-                const f32x4_t o = *reinterpret_cast<const f32x4_t*>(
-                    p.out_i[i] + int64_t(t) * p.o_st[i] + int64_t(h) * p.o_sh[i] + 4 * d4);
-                const float c = w[i] * inv;
-                acc += c * o;
-            }
+            const f32x4_t c = (w[i] * inv) * o[i];
+            if (w[i] != 0.f) acc += c;
         }
         lse = M + logf(tot);
     }

@@ -12,6 +12,8 @@
 // directly; otherwise each chunk writes its unnormalised partial (o, running max, running sum) to the workspace and a
 // second small kernel merges the chunks of each item exactly. The kernel boundary orders the two, so no device-scope
 // fence is needed (such fences write back and invalidate a whole XCD L2, which costs far more than the extra launch).
+// Items are ordered kv head fastest, so the heads of one page are read at about the same time and, with the
+// hardware's round-robin of blocks over the 8 XCDs, each XCD receives an equal share of every row.
 //
 // Per step of 16 local tokens:
 //   * scores S^T[token][row] = K . Q^T with four v_mfma_f32_16x16x32_bf16 (k = 32 head dims each). Lane l feeds token
@@ -30,7 +32,6 @@
 
 namespace cpattn {
 
-constexpr int kDecodeMaxChunkPages = 520;
 
 
 struct DecodeParams {
@@ -68,21 +69,47 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // [8*(l%16), +8): sixteen lanes cover one 256-byte row and the 64 lanes four consecutive tokens, i.e. one contiguous
 // stretch of a page (a whole page of one head when page_size / P = 4). Fragmenting an instruction over several pages
 // costs a large share of HBM bandwidth, so each instruction stays inside one page wherever the page allows. K and V
-// pools share their layout, so one set of offsets serves both. Page ids come from the chunk's LDS copy of the block
-// table; tokens past the chunk end are clamped to its last page and their values are discarded.
+// pools share their layout, so one set of offsets serves both.
 //
 // Token order inside a step. The value product contracts over k = 4*(l/16) + e, which this mapping ties to step token
 // 4e + l/16. Score row m of the MFMA is therefore given token sigma(m) = 4(m mod 4) + m/4, which puts the probability
 // of token 4e + l/16 exactly where the value operand expects it.
-__device__ __forceinline__ void step_offsets(int64_t (&off)[4], const int32_t* s_pages, int32_t pg0, int32_t npg,
-                                             int32_t jb, int32_t c4, int64_t base_rg, const PoolGeom& geo) {
+//
+// Addressing. When a physical page holds four or more slots, the four tokens of an instruction share one page, so its
+// page id is the same for the whole wave: it is read from the block table with a scalar load, and the page base is
+// formed on the scalar unit; each lane only adds its fixed offset (slot l/16, dims 8*(l%16)). Smaller pages pick the
+// lane's page among two or four such bases. Page indices past the stripe's last page are clamped to it (the data of
+// those tokens is discarded), and block-table entries outside [0, num_pages) read page 0.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+struct StepBase {
+    int64_t base[4];   // element offset of instruction e's page for this lane (pool-relative)
+};
+
+template <int PPMODE>   // 2: pp >= 4, 1: pp == 2, 0: pp == 1
+__device__ __forceinline__ void step_bases(StepBase& sb, const_i32_ptr bt_row, int32_t jb, int32_t last_pidx,
+                                           int32_t c4, int64_t base_rg, const PoolGeom& geo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int32_t j = jb + 4 * e + c4;
-        const int32_t pidx = min((j >> geo.pp_shift) - pg0, npg - 1);
-        int32_t page = s_pages[pidx];
-        page = (page >= 0 && page < geo.num_pages) ? page : 0;
-        off[e] = base_rg + int64_t(page) * geo.s_page + int64_t(j & (geo.pp - 1)) * geo.s_slot;
+        const int32_t j = jb + 4 * e;                      // first token of instruction e (a multiple of 4)
+        if (PPMODE == 2) {
+            const int32_t pidx = min(j >> geo.pp_shift, last_pidx);
+            int32_t page = bt_row[pidx];
+            page = (page >= 0 && page < geo.num_pages) ? page : 0;
+            sb.base[e] = base_rg + int64_t(page) * geo.s_page + int64_t(j & (geo.pp - 1)) * geo.s_slot;
+        } else {
+            const int32_t n = PPMODE == 1 ? 2 : 4;            // pages touched by the instruction
+            int64_t cand[4];
+#pragma unroll
+            for (int q = 0; q < n; ++q) {
+                const int32_t pidx = min((j >> geo.pp_shift) + q, last_pidx);
+                int32_t page = bt_row[pidx];
+                page = (page >= 0 && page < geo.num_pages) ? page : 0;
+                cand[q] = base_rg + int64_t(page) * geo.s_page;
+            }
+            sb.base[e] = PPMODE == 1 ? (c4 >= 2 ? cand[1] : cand[0])
+                                     : (c4 == 0 ? cand[0] : c4 == 1 ? cand[1] : c4 == 2 ? cand[2] : cand[3]);
+        }
     }
 }
 
@@ -92,11 +119,11 @@ struct StepData {
 };
 
 __device__ __forceinline__ void step_load(StepData& d, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, const int64_t (&off)[4], int32_t n16) {
+                                          const uint16_t* __restrict__ vp, const StepBase& sb, uint32_t lane_off) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.k[e] = load16(kp + off[e] + 8 * n16);
+    for (int e = 0; e < 4; ++e) d.k[e] = load16(kp + sb.base[e] + lane_off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + off[e] + 8 * n16);
+    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + sb.base[e] + lane_off);
 }
 
 struct SoftmaxState {
@@ -203,14 +230,13 @@ __device__ __forceinline__ void write_lse(const DecodeParams& p, int32_t s, int3
     p.lse[s * p.l_ss + int64_t(t) * p.l_st + h] = l > 0.f ? (m_log2 + log2f(l)) * kLn2 : neg_inf();
 }
 
-template <int DEPTH>
+template <int DEPTH, int PPMODE>
 __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams p) {
-    __shared__ int32_t s_pages[kDecodeMaxChunkPages];
     __shared__ u32x4_t s_kx[256];
     const int lane = threadIdx.x;
-    const int32_t nb = gridDim.x;                 // a multiple of 8
-    const int32_t bid = blockIdx.x;
-    const int32_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+    // The hardware hands block i to XCD i mod 8. With the kv head fastest in the item order and Hkv a multiple of 8,
+    // every XCD gets the same heads of every row: equal work per XCD whatever the spread of row lengths.
+    const int32_t logical = blockIdx.x;
 
     if (logical >= p.total_items) {               // padding-token fill role
         const int32_t k = logical - p.total_items;
@@ -267,16 +293,15 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         }
     }
 
-    // Stage the chunk's page ids.
-    const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
-    const int32_t pg0 = j0 >> p.geo.pp_shift;
-    const int32_t npg = j1 > j0 ? ((j1 - 1) >> p.geo.pp_shift) - pg0 + 1 : 1;
-    for (int32_t k = lane; k < npg; k += 64) s_pages[k] = j1 > j0 ? bt_row[pg0 + k] : 0;
-    // Retire the query and block-table loads here, before the first prefetch is issued: the wait-count pass cannot
-    // tell, inside the loop, that these older loads finished, and would otherwise drain every outstanding load
-    // (the prefetched steps included) before the first use of the query operand in each iteration.
+    // Retire the query loads here, before the first prefetch is issued: the wait-count pass cannot tell, inside the
+    // loop, that these older loads finished, and would otherwise drain every outstanding load (the prefetched steps
+    // included) before the first use of the query operand in each iteration.
     wait_all_vmem();
-    __syncthreads();
+    const const_i32_ptr bt_row = (const_i32_ptr)(p.bt + int64_t(b) * p.bt_stride);
+    const int32_t last_pidx = Lr > 0 ? (Lr - 1) >> p.geo.pp_shift : 0;
+    // Lane offset inside instruction e's page run: slot within the page plus the lane's dim block.
+    const int32_t lane_slot = PPMODE == 2 ? c4 : (PPMODE == 1 ? (c4 & 1) : 0);
+    const uint32_t lane_off = uint32_t(lane_slot * p.geo.s_slot + 8 * n16);
 
     SoftmaxState st;
 #pragma unroll
@@ -293,18 +318,18 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
     StepData buf[DEPTH];
 #pragma unroll
     for (int u = 0; u < DEPTH - 1; ++u) {
-        int64_t off[4];
-        step_offsets(off, s_pages, pg0, npg, j0 + 16 * min(u, last), c4, base_rg, p.geo);
-        step_load(buf[u], p.kp, p.vp, off, n16);
+        StepBase sb;
+        step_bases<PPMODE>(sb, bt_row, j0 + 16 * min(u, last), last_pidx, c4, base_rg, p.geo);
+        step_load(buf[u], p.kp, p.vp, sb, lane_off);
     }
     for (int32_t it = 0; it < nsteps; it += DEPTH) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
             const int32_t k = it + u;
             {
-                int64_t off[4];
-                step_offsets(off, s_pages, pg0, npg, j0 + 16 * min(k + DEPTH - 1, last), c4, base_rg, p.geo);
-                step_load(buf[(u + DEPTH - 1) % DEPTH], p.kp, p.vp, off, n16);
+                StepBase sb;
+                step_bases<PPMODE>(sb, bt_row, j0 + 16 * min(k + DEPTH - 1, last), last_pidx, c4, base_rg, p.geo);
+                step_load(buf[(u + DEPTH - 1) % DEPTH], p.kp, p.vp, sb, lane_off);
             }
             if (k < nsteps) step_compute(st, buf[u], qop, s_kx, j0 + 16 * k, j1, n16, c4, p.scale_log2);
         }
@@ -356,13 +381,14 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
 
 // Exact merge of the chunk records of every item that needed more than one chunk: with M = max_c m_c,
 // o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c and lse = (M + log2 sum_c 2^(m_c - M) l_c) ln 2.
-// One wave per (row, stripe, kv head, query tile); lanes hold the same (row, dim) layout as the chunk kernel.
+// One wave per (row, stripe, query tile, kv head). Lane l handles query row 4*rg + l/16 (row groups rg of four rows)
+// and head dims [8*(l%16), +8); the records of up to 16 chunks are loaded in one round.
 __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const DecodeParams p) {
     const int lane = threadIdx.x;
-    const int32_t triple = blockIdx.x;            // (row, stripe, tile) * Hkv + kv head
+    const int32_t triple = blockIdx.x;            // ((row * S + stripe) * n_qtiles + tile) * Hkv + kv head
     const int32_t g = triple % p.Hkv;
     int32_t item = triple / p.Hkv;
-    const int32_t tile = item;                     // (row * S + stripe) * n_qtiles + tile
+    const int32_t tile = item;
     const int32_t qt = item % p.n_qtiles;
     item /= p.n_qtiles;
     const int32_t s = item % p.S;
@@ -379,113 +405,67 @@ __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const Decode
     const int32_t CH = p.chunk_steps * 16;
     const int32_t nch = (Lr + CH - 1) / CH;
     if (nch <= 1) return;                       // written directly by the chunk kernel
-    const int32_t n16 = lane & 15, c4 = lane >> 4;
+    const int32_t d8 = lane & 15, rsub = lane >> 4;
     const int32_t RR = p.rec_rows;
     const int64_t rec_floats = int64_t(RR) * 130;
     // Chunk c of this item is record ((tile * n_chunks + c) * Hkv + g).
     const float* rec0 = p.ws_rec + (int64_t(tile) * p.n_chunks * p.Hkv + g) * rec_floats;
     const int64_t rec_step = int64_t(p.Hkv) * rec_floats;
-    constexpr int kMaxUnrolled = 16;   // items with up to this many chunks keep every chunk's max and sum in registers
+    constexpr int kUnrolled = 16;
 
-    float M_o[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()}, L_o[4] = {0.f, 0.f, 0.f, 0.f};
-    float M_r = neg_inf(), L_r = 0.f;
-    float acc[4][8];
+    for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
+        const int32_t row = 4 * rg + rsub;
+        const bool active = row < tile_rows;
+        const int32_t rrow = min(row, RR - 1);
+        float M = neg_inf(), Lsum = 0.f;
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        if (nch <= kUnrolled) {
+            float mc[kUnrolled], lc[kUnrolled];
+            f32x4_t o0[kUnrolled], o1[kUnrolled];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+            for (int cc = 0; cc < kUnrolled; ++cc) {
+                const bool live = active && cc < nch;
+                const float* rc = rec0 + cc * rec_step;
+                mc[cc] = live ? rc[RR * 128 + rrow] : neg_inf();
+                lc[cc] = live ? rc[RR * 128 + RR + rrow] : 0.f;
+                o0[cc] = live ? *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                o1[cc] = live ? *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc[ii][n] = 0.f;
-
-    auto add_chunk = [&](const float* rc, const float (&mo)[4], const float (&lo)[4], float mr, float lr) {
+            for (int cc = 0; cc < kUnrolled; ++cc) M = fmaxf(M, mc[cc]);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int32_t row = 4 * c4 + ii;
-            if (row < tile_rows) {
-                const float w = exp2f(mo[ii] - M_o[ii]);
-                L_o[ii] += w * lo[ii];
-                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16);
-                const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(rc + row * 128 + 8 * n16 + 4);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    acc[ii][n] += w * a[n];
-                    acc[ii][n + 4] += w * bq[n];
-                }
+            for (int cc = 0; cc < kUnrolled; ++cc) {
+                const float w = cc < nch ? exp2f(mc[cc] - M) : 0.f;
+                Lsum += w * lc[cc];
+                a0 += w * o0[cc];
+                a1 += w * o1[cc];
+            }
+        } else {
+            for (int32_t cc = 0; cc < nch; ++cc) M = fmaxf(M, rec0[cc * rec_step + RR * 128 + rrow]);
+            for (int32_t cc = 0; cc < nch; ++cc) {
+                const float* rc = rec0 + cc * rec_step;
+                const float w = exp2f(rc[RR * 128 + rrow] - M);
+                Lsum += w * rc[RR * 128 + RR + rrow];
+                a0 += w * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
+                a1 += w * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
             }
         }
-        if (n16 < tile_rows) L_r += exp2f(mr - M_r) * lr;
-    };
-
-    if (nch <= kMaxUnrolled) {
-        // Every chunk's maxima and sums are loaded together (static indices keep them in registers).
-        float m_o[kMaxUnrolled][4], l_o[kMaxUnrolled][4], m_r[kMaxUnrolled], l_r[kMaxUnrolled];
-#pragma unroll
-        for (int cc = 0; cc < kMaxUnrolled; ++cc) {
-            const float* rc = rec0 + cc * rec_step + RR * 128;
-            const bool live = cc < nch;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int32_t row = 4 * c4 + ii;
-                const bool ok = live && row < tile_rows;
-                m_o[cc][ii] = ok ? rc[row] : neg_inf();
-                l_o[cc][ii] = ok ? rc[RR + row] : 0.f;
-            }
-            m_r[cc] = (live && n16 < tile_rows) ? rc[n16] : neg_inf();
-            l_r[cc] = (live && n16 < tile_rows) ? rc[RR + n16] : 0.f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < kMaxUnrolled; ++cc) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) M_o[ii] = fmaxf(M_o[ii], m_o[cc][ii]);
-            M_r = fmaxf(M_r, m_r[cc]);
-        }
-        // Values four chunks at a time.
-#pragma unroll
-        for (int cg = 0; cg < kMaxUnrolled; cg += 4) {
-            if (cg >= nch) break;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (cg + u < nch) add_chunk(rec0 + (cg + u) * rec_step, m_o[cg + u], l_o[cg + u], m_r[cg + u], l_r[cg + u]);
-        }
-    } else {
-        for (int32_t cc = 0; cc < nch; ++cc) {
-            const float* rc = rec0 + cc * rec_step + RR * 128;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                if (4 * c4 + ii < tile_rows) M_o[ii] = fmaxf(M_o[ii], rc[4 * c4 + ii]);
-            if (n16 < tile_rows) M_r = fmaxf(M_r, rc[n16]);
-        }
-        for (int32_t cc = 0; cc < nch; ++cc) {
-            const float* rc = rec0 + cc * rec_step;
-            float mo[4], lo[4];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int32_t row = min(4 * c4 + ii, RR - 1);
-                mo[ii] = rc[RR * 128 + row];
-                lo[ii] = rc[RR * 128 + RR + row];
-            }
-            const int32_t rr = min(n16, RR - 1);
-            add_chunk(rc, mo, lo, rc[RR * 128 + rr], rc[RR * 128 + RR + rr]);
+        if (active) {
+            const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+            const float vals[8] = {a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv,
+                                   a1[0] * inv, a1[1] * inv, a1[2] * inv, a1[3] * inv};
+            write_row(p, s, tok0, row0, g, row, d8, vals);
+            if (d8 == 0) write_lse(p, s, tok0, row0, g, row, M, Lsum);
         }
     }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const int32_t row = 4 * c4 + ii;
-        if (row < tile_rows) {
-            const float inv = L_o[ii] > 0.f ? 1.0f / L_o[ii] : 0.f;
-            float vals[8];
-#pragma unroll
-            for (int n = 0; n < 8; ++n) vals[n] = acc[ii][n] * inv;
-            write_row(p, s, tok0, row0, g, row, n16, vals);
-        }
-    }
-    if (c4 == 0 && n16 < tile_rows) write_lse(p, s, tok0, row0, g, n16, M_r, L_r);
 }
 
 static int32_t decode_chunk_steps() {
     static int32_t steps = [] {
         const char* e = std::getenv("CPATTN_DECODE_CHUNK_STEPS");
-        int v = e ? std::atoi(e) : 16;
+        int v = e ? std::atoi(e) : 64;
         if (v < 1) v = 1;
-        if (v > 32) v = 32;
+        if (v > 64) v = 64;
         return v;
     }();
     return steps;
@@ -495,7 +475,7 @@ static int32_t decode_chunk_steps() {
 static int32_t decode_depth() {
     static int32_t depth = [] {
         const char* e = std::getenv("CPATTN_DECODE_DEPTH");
-        int v = e ? std::atoi(e) : 3;
+        int v = e ? std::atoi(e) : 2;
         return v == 2 ? 2 : 3;
     }();
     return depth;
@@ -531,8 +511,6 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if ((a.out_stride_stripe | a.out_stride_token | a.out_stride_head) & 3) return false;
     const DecodeShape d = decode_shape(a);
     if (d.total_items + (a.num_tokens + 3) / 4 + 8 > (int64_t(1) << 31) - 1) return false;
-    // A chunk covers at most chunk_steps*16 tokens, so at most that many pages (+1) are staged.
-    if (int64_t(decode_chunk_steps()) * 16 / std::max(1, geo.pp) + 1 > kDecodeMaxChunkPages) return false;
     return true;
 }
 
@@ -585,10 +563,15 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     const int64_t blocks = ((d.total_items + p.pad_blocks) + 7) / 8 * 8;
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
-    if (decode_depth() == 2)
-        hipLaunchKernelGGL((gqa_decode_bf16_kernel<2>), grid, dim3(64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((gqa_decode_bf16_kernel<3>), grid, dim3(64), 0, stream, p);
+    const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
+    switch (decode_depth() * 4 + ppmode) {
+        case 8: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0>), grid, dim3(64), 0, stream, p); break;
+        case 9: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1>), grid, dim3(64), 0, stream, p); break;
+        case 10: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2>), grid, dim3(64), 0, stream, p); break;
+        case 12: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 0>), grid, dim3(64), 0, stream, p); break;
+        case 13: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 1>), grid, dim3(64), 0, stream, p); break;
+        default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 2>), grid, dim3(64), 0, stream, p); break;
+    }
     if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode)")) return st;
     if (d.n_chunks > 1 && d.triples > 0) {
         hipLaunchKernelGGL(gqa_decode_chunk_merge_kernel, dim3(uint32_t(d.triples)), dim3(64), 0, stream, p);

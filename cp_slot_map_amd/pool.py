@@ -7,6 +7,8 @@ pools live on one device, as one tensor with a leading stripe axis.
 Storage layouts:
 * GQA "hnd": [P, num_pages, Hkv, pp, D] (a page's slots of one head are contiguous), passed to the kernels as the
   [stripe, page, slot, head, dim] view ``storage.transpose(2, 3)``.
+* GQA "hnd_kv": [P, num_pages, Hkv, 2, pp, D]: the K block and the V block of one (page, kv head) are adjacent, so a
+  head's share of a page is one contiguous run (K and V views share their strides).
 * GQA "nhd": [P, num_pages, pp, Hkv, D].
 * MLA: [P, num_pages, pp, 576] latent rows.
 Slots that hold no token (the sink page 0, unused pages, tail slots) keep ``fill``: NaN for parity runs, so that any
@@ -70,6 +72,13 @@ def build_batch(wl, device="cuda", *, fill=float("nan"), layout="hnd", rows=None
         k_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim), fill, dtype=dt, device=dev)
         v_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim_v), fill, dtype=dt, device=dev)
         k_pool, v_pool = k_store.transpose(2, 3), v_store.transpose(2, 3)
+    elif layout == "hnd_kv":
+        # K and V blocks of one (page, kv head) side by side: [P, num_pages, Hkv, 2, pp, D]
+        if wl.head_dim != wl.head_dim_v:
+            raise ValueError("the paired layout needs head_dim == head_dim_v")
+        kv = torch.full((P, wl.num_pages, wl.num_kv_heads, 2, pp, wl.head_dim), fill, dtype=dt, device=dev)
+        k_store, v_store = kv, None
+        k_pool, v_pool = kv[:, :, :, 0].transpose(2, 3), kv[:, :, :, 1].transpose(2, 3)
     elif layout == "nhd":
         k_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim), fill, dtype=dt, device=dev)
         v_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim_v), fill, dtype=dt, device=dev)

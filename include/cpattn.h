@@ -263,7 +263,8 @@ typedef struct cp_merge_args {
  * vLLM compare view, FlashAttentionImpl._forward_with_dcp.
  *
  * M = max_i lse_i; M = -inf gives out = 0, lse = -inf; otherwise lse = M + log sum_i exp(lse_i - M) and
- * out = sum_i exp(lse_i - lse) * o_i. A partial with lse_i = -inf is not read (its out row may hold anything).
+ * out = sum_i exp(lse_i - lse) * o_i. A partial with lse_i = -inf contributes nothing: it is selected out, never
+ * multiplied, so its out row may hold anything (NaN included). Tokens >= *token_count are not read at all.
  * EINVAL: N outside [1, CPATTN_MAX_PARTIALS], null pointers, Dv % 4 != 0, negative sizes, out aliasing a partial.
  */
 int32_t cp_lse_merge(const cp_merge_args* args, hipStream_t stream);
