@@ -195,7 +195,7 @@ def main():
                       "merge_avg": round(float(np.mean(merge_ms)), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "cp_paged_attn_partial (gqa_decode_bf16_kernel)",
+                     "kernel": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
                      "bytes_per_launch": kv_bytes},
     }
     if flops:

@@ -112,8 +112,9 @@ def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partner
 
 
 def _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale, kind,
-                stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens):
+                stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens, fixed_splits=False):
     a = PagedArgs()
+    a.flags = _lib.CPATTN_FLAG_FIXED_SPLITS if fixed_splits else 0
     a.kind = CPATTN_MLA if kind == "mla" else CPATTN_GQA
     a.dtype = _dtype_code(q.dtype)
     if k_pool.dtype != q.dtype:
@@ -181,12 +182,14 @@ def _check_int32_dev(*ts):
 
 
 def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
-                              kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens):
+                              kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens,
+                              fixed_splits=False):
     lib = _lib_handle()
     sc = int(partners) - stripe_begin if stripe_count is None else stripe_count
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
-                    max_row_tokens=max_row_tokens, out=None, lse=None, num_tokens=q.shape[0])
+                    max_row_tokens=max_row_tokens, out=None, lse=None, num_tokens=q.shape[0],
+                    fixed_splits=fixed_splits)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     return int(n.value)
@@ -194,11 +197,12 @@ def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_tab
 
 def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                        kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len=None, max_row_tokens=None,
-                       out=None, lse=None, workspace=None, stream=None):
+                       out=None, lse=None, workspace=None, stream=None, fixed_splits=False):
     """Per-stripe partials (out [S, T, Hq, Dv] fp32, lse [S, T, Hq] fp32) of attention over the striped pool.
 
     q [T, Hq, D]; q_row_start int32 [B + 1]; ctx_len int32 [B]; block_table int32 [B, max_pages]. ``max_ctx_len``
-    and ``max_row_tokens`` are host upper bounds (read from the device with a sync when omitted).
+    and ``max_row_tokens`` are host upper bounds (read from the device with a sync when omitted). ``fixed_splits``
+    makes each row's result independent, to the bit, of the rest of the call (CPATTN_FLAG_FIXED_SPLITS).
     """
     lib = _lib_handle()
     _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
@@ -222,7 +226,7 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
         raise ValueError("out/lse must be fp32 with contiguous last dims")
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
-                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T)
+                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     if n.value > 0:

@@ -29,6 +29,7 @@
 #include "launch.h"
 
 #include <cstdlib>
+#include <string>
 
 namespace cpattn {
 
@@ -49,11 +50,13 @@ struct DecodeParams {
     float* lse;
     int64_t l_ss, l_st;
     float* ws_rec;
+    int32_t* ws_blockpref;        // persistent schedule: 64 block offsets + the total step count
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G;
     int32_t max_pages, page_size, max_row_tokens;
     int32_t n_qtiles, n_chunks, chunk_steps;
     int32_t total_items, pad_blocks, pad_tokens_per_block;
     int32_t rec_rows;
+    int32_t num_tiles, nwaves;    // persistent schedule
     float scale_log2;
 };
 
@@ -460,6 +463,371 @@ __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const Decode
     }
 }
 
+// ============================================================================================ persistent schedule
+//
+// The grid is exactly the resident wave slots. Work is the flattened space (kv head g, tile T, step) with g slowest;
+// tile T = (row, stripe, query tile) has n_T = ceil(Lr / 16) steps when it holds query rows. Every wave takes an
+// equal contiguous range of that space, so all waves stream for the same time whatever the row lengths, and none is
+// spent launching or retiring blocks. A range crosses item boundaries: only its first and last segments can be part of
+// an item, so each wave writes at most two records (slot 0: first segment, slot 1: last segment); items covered by a
+// single wave are written directly. gqa_decode_fixup_kernel merges split items, writes tiles without context and the
+// padding tokens.
+
+// Steps of tile T (0 when the tile holds no query row). Per-lane T: vector loads.
+__device__ __forceinline__ int32_t tile_steps(const DecodeParams& p, int32_t T) {
+    const int32_t qt = T % p.n_qtiles;
+    const int32_t bs = T / p.n_qtiles;
+    const int32_t s = bs % p.S;
+    const int32_t b = bs / p.S;
+    const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
+    const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
+    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P);
+    return qt * 16 < nrows ? (Lr + 15) >> 4 : 0;
+}
+
+struct Tile {
+    int32_t b, s, qt, tok0, nrows, Lr, n_steps;
+};
+
+// Wave-uniform T: scalar loads through the constant address space.
+__device__ __forceinline__ Tile load_tile(const DecodeParams& p, int32_t T) {
+    const const_i32_ptr qrs = (const_i32_ptr)p.q_row_start;
+    const const_i32_ptr cl = (const_i32_ptr)p.ctx_len;
+    Tile tl;
+    tl.qt = T % p.n_qtiles;
+    const int32_t bs = T / p.n_qtiles;
+    tl.s = bs % p.S;
+    tl.b = bs / p.S;
+    tl.tok0 = min(max(qrs[tl.b], 0), p.T);
+    const int32_t tok1 = min(max(qrs[tl.b + 1], tl.tok0), p.T);
+    tl.nrows = min(tok1 - tl.tok0, p.max_row_tokens) * p.G;
+    const int32_t L = min(max(cl[tl.b], 0), p.max_pages * p.page_size);
+    tl.Lr = stripe_length(L, p.stripe_begin + tl.s, p.P);
+    tl.n_steps = tl.qt * 16 < tl.nrows ? (tl.Lr + 15) >> 4 : 0;
+    return tl;
+}
+
+struct ItemAddr {
+    const_i32_ptr bt_row;
+    int64_t base_rg;
+    int32_t last_pidx;
+};
+
+__device__ __forceinline__ ItemAddr item_addr(const DecodeParams& p, const Tile& tl, int32_t g) {
+    ItemAddr ia;
+    ia.bt_row = (const_i32_ptr)(p.bt + int64_t(tl.b) * p.bt_stride);
+    ia.base_rg = int64_t(p.stripe_begin + tl.s) * p.geo.s_stripe + int64_t(g) * p.geo.s_head;
+    ia.last_pidx = tl.Lr > 0 ? (tl.Lr - 1) >> p.geo.pp_shift : 0;
+    return ia;
+}
+
+template <int PPMODE>
+__device__ __forceinline__ void issue_step(StepData& d, const DecodeParams& p, const ItemAddr& ia, int32_t k,
+                                           int32_t c4, uint32_t lane_off) {
+    StepBase sb;
+    step_bases<PPMODE>(sb, ia.bt_row, 16 * k, ia.last_pidx, c4, ia.base_rg, p.geo);
+    step_load(d, p.kp, p.vp, sb, lane_off);
+}
+
+// Query operand staged in LDS: slot i*64 + lane holds lane's dims [32i + 8*(l/16), +8) of query row l%16.
+__device__ __forceinline__ void stage_query(u32x4_t* __restrict__ sq, const bf16x8_t (&qop)[4], int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq[i * 64 + lane] = __builtin_bit_cast(u32x4_t, qop[i]);
+}
+
+__device__ __forceinline__ void read_query(bf16x8_t (&qop)[4], const u32x4_t* __restrict__ sq, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8(sq[i * 64 + lane]);
+}
+
+__device__ __forceinline__ void load_query(bf16x8_t (&qop)[4], const DecodeParams& p, const Tile& tl, int32_t g,
+                                           int32_t n16, int32_t c4) {
+    const int32_t rho = tl.qt * 16 + n16;
+    if (rho < tl.nrows) {
+        const uint16_t* qp = p.q + int64_t(tl.tok0 + rho / p.G) * p.q_st + int64_t(g * p.G + rho % p.G) * p.q_sh + 8 * c4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8(load16(qp + 32 * i));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8((u32x4_t){0u, 0u, 0u, 0u});
+    }
+}
+
+// s_waitcnt vmcnt(8) (other counters at their maximum): the 8 loads of the newest step may stay in flight.
+__device__ __forceinline__ void wait_vmem_8() { __builtin_amdgcn_s_waitcnt(0x0F78); }
+
+// Finish a segment: the normalised stripe partial when the segment is the whole item, else an unnormalised record.
+__device__ __forceinline__ void segment_epilogue(const DecodeParams& p, const SoftmaxState& st, const Tile& tl,
+                                                 int32_t g, int32_t n16, int32_t c4, float* rec) {
+    float lsum = st.l;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float l_o[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) l_o[ii] = __shfl(lsum, 4 * c4 + ii);
+    const int32_t row0 = tl.qt * 16;
+    const int32_t tile_rows = min(16, tl.nrows - row0);
+    if (rec == nullptr) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int32_t row = 4 * c4 + ii;
+            if (row < tile_rows) {
+                const float inv = l_o[ii] > 0.f ? 1.0f / l_o[ii] : 0.f;
+                float vals[8];
+#pragma unroll
+                for (int n = 0; n < 8; ++n) vals[n] = st.o[n][ii] * inv;
+                write_row(p, tl.s, tl.tok0, row0, g, row, n16, vals);
+            }
+        }
+        if (c4 == 0 && n16 < tile_rows) write_lse(p, tl.s, tl.tok0, row0, g, n16, st.m, lsum);
+    } else {
+        const int32_t RR = p.rec_rows;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int32_t row = 4 * c4 + ii;
+            if (row < tile_rows) {
+                float* o = rec + row * 128 + 8 * n16;
+                *reinterpret_cast<f32x4_t*>(o) = (f32x4_t){st.o[0][ii], st.o[1][ii], st.o[2][ii], st.o[3][ii]};
+                *reinterpret_cast<f32x4_t*>(o + 4) = (f32x4_t){st.o[4][ii], st.o[5][ii], st.o[6][ii], st.o[7][ii]};
+            }
+        }
+        if (c4 == 0 && n16 < tile_rows) {
+            rec[RR * 128 + n16] = st.m;
+            rec[RR * 128 + RR + n16] = lsum;        // the whole row's sum, not this lane group's share
+        }
+    }
+}
+
+// Exclusive prefix of a wave-wide per-lane value (lane 0 gets 0) and the total.
+__device__ __forceinline__ int32_t wave_exclusive_scan(int32_t v, int lane, int32_t& total) {
+    int32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    return incl - v;
+}
+
+// A value every lane holds identically, moved to a scalar register so everything derived from it stays scalar.
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int PPMODE>
+__global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeParams p) {
+    __shared__ u32x4_t s_kx[256];
+    __shared__ u32x4_t s_q[2][256];
+    const int lane = threadIdx.x;
+    const int32_t w = blockIdx.x;
+    const int32_t nw = gridDim.x;
+    const int32_t n16 = lane & 15, c4 = lane >> 4;
+    const int32_t NT = p.num_tiles;
+
+    // Step counts of every tile: lane l sums a block of K consecutive tiles; a wave scan gives block offsets.
+    const int32_t K = (NT + 63) >> 6;
+    const int32_t t_lo = min(lane * K, NT), t_hi = min(t_lo + K, NT);
+    int32_t my_sum = 0;
+    for (int32_t t = t_lo; t < t_hi; ++t) my_sum += tile_steps(p, t);
+    int32_t N = 0;
+    const int32_t my_excl = wave_exclusive_scan(my_sum, lane, N);
+    if (w == 0) {                                    // block offsets for the fix-up kernel
+        p.ws_blockpref[lane] = my_excl;
+        if (lane == 0) p.ws_blockpref[64] = N;
+    }
+    const int64_t total = int64_t(p.Hkv) * N;
+    const int64_t Q = (total + nw - 1) / nw;
+    const int64_t start = int64_t(w) * Q;
+    if (start >= total) return;
+    int64_t remaining = min(Q, total - start);
+    int32_t g = int32_t(start / N);
+    const int32_t pos = int32_t(start - int64_t(g) * N);
+
+    // The tile holding `pos`: first the lane block, then the tile inside it (one tile per lane, one scan).
+    const uint64_t owner = __ballot(pos >= my_excl && pos < my_excl + my_sum);
+    const int32_t src = uniform(int32_t(__builtin_ctzll(owner)));
+    const int32_t b_lo = uniform(__shfl(t_lo, src)), b_hi = uniform(__shfl(t_hi, src)), b_ex = uniform(__shfl(my_excl, src));
+    const int32_t tt = b_lo + lane;
+    const int32_t tn = tt < b_hi ? tile_steps(p, tt) : 0;
+    int32_t dummy;
+    const int32_t tex = b_ex + wave_exclusive_scan(tn, lane, dummy);
+    const uint64_t hit = __ballot(tt < b_hi && tn > 0 && pos >= tex && pos < tex + tn);
+    const int32_t hl = uniform(int32_t(__builtin_ctzll(hit)));
+    int32_t T = b_lo + hl;
+    int32_t seg_begin = pos - uniform(__shfl(tex, hl));
+
+    const int32_t lane_slot = PPMODE == 2 ? c4 : (PPMODE == 1 ? (c4 & 1) : 0);
+    const uint32_t lane_off = uint32_t(lane_slot * p.geo.s_slot + 8 * n16);
+    float* const rec_base = p.ws_rec + int64_t(w) * 2 * p.rec_rows * 130;
+
+    Tile tl = load_tile(p, T);
+    ItemAddr ia = item_addr(p, tl, g);
+    int32_t seg_end = int32_t(min<int64_t>(tl.n_steps, seg_begin + remaining));
+    bool first_seg = true;
+    int qbuf = 0;                                    // LDS query buffer of the current item
+    StepData da, db;
+    {
+        bf16x8_t q0[4];
+        load_query(q0, p, tl, g, n16, c4);
+        issue_step<PPMODE>(da, p, ia, seg_begin, c4, lane_off);
+        wait_vmem_8();                               // the query is in; the first step may still be in flight
+        stage_query(s_q[0], q0, lane);
+    }
+
+    for (;;) {
+        SoftmaxState st;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.o[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        st.m = neg_inf();
+        st.l = 0.f;
+        const u32x4_t* sq = s_q[qbuf];
+        int32_t k = seg_begin;
+        // Steady state: one item, unconditional loads, the next step always in flight.
+        while (k + 1 < seg_end) {
+            bf16x8_t qop[4];
+            issue_step<PPMODE>(db, p, ia, k + 1, c4, lane_off);
+            read_query(qop, sq, lane);
+            step_compute(st, da, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            ++k;
+            if (k + 1 >= seg_end) {
+                da = db;
+                break;
+            }
+            issue_step<PPMODE>(da, p, ia, k + 1, c4, lane_off);
+            read_query(qop, sq, lane);
+            step_compute(st, db, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            ++k;
+        }
+        // Last step of the segment: the next item's query and first step are issued before it is computed.
+        remaining -= seg_end - seg_begin;
+        bool more = remaining > 0;
+        Tile nt = tl;
+        ItemAddr na = ia;
+        int32_t ng = g;
+        bf16x8_t qn[4];
+        if (more) {
+            int32_t nT = T;
+            do {
+                if (++nT == NT) {
+                    nT = 0;
+                    ++ng;
+                }
+                nt = load_tile(p, nT);
+            } while (nt.n_steps == 0 && ng < p.Hkv);
+            if (ng < p.Hkv) {
+                T = nT;
+                na = item_addr(p, nt, ng);
+                load_query(qn, p, nt, ng, n16, c4);
+                issue_step<PPMODE>(db, p, na, 0, c4, lane_off);
+            } else {
+                more = false;                        // cannot happen while steps remain; never read past the heads
+            }
+        }
+        {
+            bf16x8_t qop[4];
+            read_query(qop, sq, lane);
+            step_compute(st, da, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+        }
+        if (more) {
+            wait_vmem_8();
+            stage_query(s_q[qbuf ^ 1], qn, lane);
+        }
+        const bool whole = seg_begin == 0 && seg_end == tl.n_steps;
+        segment_epilogue(p, st, tl, g, n16, c4, whole ? nullptr : rec_base + (first_seg ? 0 : p.rec_rows * 130));
+        if (!more) break;
+        tl = nt;
+        ia = na;
+        g = ng;
+        qbuf ^= 1;
+        da = db;
+        seg_begin = 0;
+        seg_end = int32_t(min<int64_t>(tl.n_steps, remaining));
+        first_seg = false;
+    }
+}
+
+// Prefix (in steps) of tile T from the published block offsets: one block walk, one tile per lane.
+__device__ __forceinline__ int32_t tile_prefix(const DecodeParams& p, int32_t T, int lane) {
+    const int32_t K = (p.num_tiles + 63) >> 6;
+    const int32_t blk = T / K;
+    const int32_t t = blk * K + lane;
+    const int32_t n = (t < T) ? tile_steps(p, t) : 0;
+    int32_t sum = n;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+    return p.ws_blockpref[blk] + sum;
+}
+
+// Items split over several waves are merged from their records; tiles with query rows but no context get (0, -inf);
+// extra blocks write padding tokens. One wave per (tile, kv head).
+__global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x;
+    const int32_t idx = blockIdx.x;
+    const int32_t n_items = p.num_tiles * p.Hkv;
+    if (idx >= n_items) {
+        const int32_t k = idx - n_items;
+        const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
+        const int32_t t0 = max(k * p.pad_tokens_per_block, first);
+        const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
+        if (t0 < t1) fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        return;
+    }
+    const int32_t T = idx / p.Hkv;
+    const int32_t g = idx % p.Hkv;
+    const Tile tl = load_tile(p, T);
+    const int32_t row0 = tl.qt * 16;
+    if (row0 >= tl.nrows) return;
+    const int32_t tile_rows = min(16, tl.nrows - row0);
+    const int32_t d8 = lane & 15, rsub = lane >> 4;
+    if (tl.n_steps == 0) {                           // no context in this stripe: (0, -inf)
+        const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
+            const int32_t row = 4 * rg + rsub;
+            if (row < tile_rows) {
+                write_row(p, tl.s, tl.tok0, row0, g, row, d8, zero);
+                if (d8 == 0) write_lse(p, tl.s, tl.tok0, row0, g, row, neg_inf(), 0.f);
+            }
+        }
+        return;
+    }
+    const int32_t N = p.ws_blockpref[64];
+    const int64_t total = int64_t(p.Hkv) * N;
+    const int64_t Q = (total + p.nwaves - 1) / p.nwaves;
+    const int64_t A = int64_t(g) * N + tile_prefix(p, T, lane);
+    const int64_t Bend = A + tl.n_steps;
+    const int64_t wA = A / Q, wB = (Bend - 1) / Q;
+    if (wA == wB) return;                            // one wave covered it and wrote it
+    const int32_t RR = p.rec_rows;
+    const int64_t rec_floats = int64_t(RR) * 130;
+    for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
+        const int32_t row = 4 * rg + rsub;
+        const bool active = row < tile_rows;
+        const int32_t rrow = min(row, RR - 1);
+        float M = neg_inf();
+        for (int64_t wv = wA; wv <= wB; ++wv) {
+            const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
+            M = fmaxf(M, rc[RR * 128 + rrow]);
+        }
+        float Lsum = 0.f;
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t wv = wA; wv <= wB; ++wv) {
+            const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
+            const float wgt = exp2f(rc[RR * 128 + rrow] - M);
+            Lsum += wgt * rc[RR * 128 + RR + rrow];
+            a0 += wgt * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
+            a1 += wgt * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
+        }
+        if (active) {
+            const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+            const float vals[8] = {a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv,
+                                   a1[0] * inv, a1[1] * inv, a1[2] * inv, a1[3] * inv};
+            write_row(p, tl.s, tl.tok0, row0, g, row, d8, vals);
+            if (d8 == 0) write_lse(p, tl.s, tl.tok0, row0, g, row, M, Lsum);
+        }
+    }
+}
+
 static int32_t decode_chunk_steps() {
     static int32_t steps = [] {
         const char* e = std::getenv("CPATTN_DECODE_CHUNK_STEPS");
@@ -471,7 +839,7 @@ static int32_t decode_chunk_steps() {
     return steps;
 }
 
-// Prefetch depth of the step ring (2 or 3 buffers of 8 KB per wave).
+// Prefetch depth of the chunked kernel's step ring (2 or 3 buffers of 8 KB per wave).
 static int32_t decode_depth() {
     static int32_t depth = [] {
         const char* e = std::getenv("CPATTN_DECODE_DEPTH");
@@ -481,8 +849,22 @@ static int32_t decode_depth() {
     return depth;
 }
 
+// Persistent schedule unless CPATTN_DECODE_SCHEDULE=chunked (kept for comparison and for very large tile counts).
+static bool decode_persistent_enabled() {
+    static bool on = [] {
+        const char* e = std::getenv("CPATTN_DECODE_SCHEDULE");
+        return !(e && std::string(e) == "chunked");
+    }();
+    return on;
+}
+
+constexpr int64_t kMaxPersistWaves = 8192;
+constexpr int64_t kMaxPersistTiles = 4096;
+constexpr int64_t kBlockPrefBytes = 512;   // 65 int32 block offsets, padded
+
 struct DecodeShape {
-    int64_t n_qtiles, n_chunks, total_items, rec_rows, triples;
+    int64_t n_qtiles, n_chunks, total_items, rec_rows, triples, num_tiles;
+    bool persistent;
 };
 
 static DecodeShape decode_shape(const cp_paged_args& a) {
@@ -490,10 +872,13 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
     const int64_t G = a.num_q_heads / a.num_kv_heads;
     const int64_t rows = int64_t(a.max_row_tokens) * G;
     d.n_qtiles = std::max<int64_t>(1, (rows + 15) / 16);
+    d.num_tiles = int64_t(a.num_rows) * a.stripe_count * d.n_qtiles;
+    d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && decode_persistent_enabled() &&
+                   d.num_tiles <= kMaxPersistTiles;
     const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
     const int64_t CH = int64_t(decode_chunk_steps()) * 16;
-    d.n_chunks = std::max<int64_t>(1, (max_lr + CH - 1) / CH);
-    d.triples = int64_t(a.num_rows) * a.stripe_count * a.num_kv_heads * d.n_qtiles;
+    d.n_chunks = d.persistent ? 1 : std::max<int64_t>(1, (max_lr + CH - 1) / CH);
+    d.triples = d.num_tiles * a.num_kv_heads;
     d.total_items = d.triples * d.n_chunks;
     const int64_t rr = std::min<int64_t>(16, rows);
     d.rec_rows = std::max<int64_t>(4, (rr + 3) / 4 * 4);
@@ -516,8 +901,27 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
 
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a) {
     const DecodeShape d = decode_shape(a);
+    if (d.persistent) return kBlockPrefBytes + kMaxPersistWaves * 2 * d.rec_rows * 130 * 4;
     if (d.n_chunks <= 1) return 0;
     return d.total_items * d.rec_rows * 130 * 4;
+}
+
+// Resident one-wave blocks of the persistent kernel on this device (cached per device and kernel variant).
+template <int PPMODE>
+static int32_t persistent_waves() {
+    static int32_t cache[64][1] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev][0] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_decode_persist_kernel<PPMODE>, 64, 0) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 8;
+        cache[dev][0] = int32_t(std::min<int64_t>(int64_t(cus) * per_cu, kMaxPersistWaves));
+    }
+    return cache[dev][0];
 }
 
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
@@ -540,7 +944,6 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.lse = a.lse;
     p.l_ss = a.lse_stride_stripe;
     p.l_st = a.lse_stride_token;
-    if (d.n_chunks > 1) p.ws_rec = static_cast<float*>(a.workspace);
     p.B = a.num_rows;
     p.T = a.num_tokens;
     p.P = a.num_partners;
@@ -559,11 +962,37 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.pad_tokens_per_block = 4;
     p.pad_blocks = (a.num_tokens + 3) / 4;
     p.rec_rows = int32_t(d.rec_rows);
+    p.num_tiles = int32_t(d.num_tiles);
     p.scale_log2 = a.scale * kLog2e;
+    const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
+
+    if (d.persistent) {
+        p.ws_blockpref = static_cast<int32_t*>(a.workspace);
+        p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + kBlockPrefBytes);
+        if (d.num_tiles > 0) {
+            int32_t nw = ppmode == 2 ? persistent_waves<2>() : ppmode == 1 ? persistent_waves<1>() : persistent_waves<0>();
+            p.nwaves = nw;
+            const dim3 grid{uint32_t(nw), 1, 1};
+            if (ppmode == 2)
+                hipLaunchKernelGGL((gqa_decode_persist_kernel<2>), grid, dim3(64), 0, stream, p);
+            else if (ppmode == 1)
+                hipLaunchKernelGGL((gqa_decode_persist_kernel<1>), grid, dim3(64), 0, stream, p);
+            else
+                hipLaunchKernelGGL((gqa_decode_persist_kernel<0>), grid, dim3(64), 0, stream, p);
+            if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode, persistent)")) return st;
+        }
+        const int64_t fix_blocks = d.num_tiles * a.num_kv_heads + p.pad_blocks;
+        if (fix_blocks > 0) {
+            hipLaunchKernelGGL(gqa_decode_fixup_kernel, dim3(uint32_t(fix_blocks)), dim3(64), 0, stream, p);
+            return check_launch("cp_paged_attn_partial (fix-up)");
+        }
+        return CPATTN_OK;
+    }
+
+    if (d.n_chunks > 1) p.ws_rec = static_cast<float*>(a.workspace);
     const int64_t blocks = ((d.total_items + p.pad_blocks) + 7) / 8 * 8;
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
-    const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
     switch (decode_depth() * 4 + ppmode) {
         case 8: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0>), grid, dim3(64), 0, stream, p); break;
         case 9: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1>), grid, dim3(64), 0, stream, p); break;

@@ -121,7 +121,7 @@ def build_batch(wl, device="cuda", *, fill=float("nan"), layout="hnd", rows=None
 
 
 def run_step(batch: Batch, *, out=None, lse=None, merged=None, merged_lse=None, own_out=None, own_lse=None,
-             out_dtype=torch.float32, workspace=None, stream=None):
+             out_dtype=torch.float32, workspace=None, stream=None, fixed_splits=False):
     """One pass of the hot path: every stripe's partial (plus the own-token partial), then the exact merge.
 
     Returns (merged_out [T, Hq, Dv], merged_lse [T, Hq], partial_out [P, T, Hq, Dv], partial_lse [P, T, Hq],
@@ -132,7 +132,7 @@ def run_step(batch: Batch, *, out=None, lse=None, merged=None, merged_lse=None, 
                                       batch.block_table, page_size=wl.page_size, partners=wl.partners,
                                       scale=wl.scale, kind=wl.kind, max_ctx_len=batch.max_ctx_len,
                                       max_row_tokens=batch.max_row_tokens, out=out, lse=lse, workspace=workspace,
-                                      stream=stream)
+                                      stream=stream, fixed_splits=fixed_splits)
     outs = [out[s] for s in range(out.shape[0])]
     lses = [lse[s] for s in range(lse.shape[0])]
     own = None
@@ -152,7 +152,7 @@ class StepPlan:
     Outputs (partials, own-token partial, merged result) are allocated once and overwritten by every run.
     """
 
-    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None):
+    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None, fixed_splits=False):
         import ctypes as C
         from . import _lib
 
@@ -171,7 +171,8 @@ class StepPlan:
         self.paged = api._paged_args(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
                                      batch.block_table, page_size=wl.page_size, partners=P, scale=wl.scale,
                                      kind=wl.kind, stripe_begin=0, stripe_count=P, max_ctx_len=batch.max_ctx_len,
-                                     max_row_tokens=batch.max_row_tokens, out=self.out, lse=self.lse, num_tokens=T)
+                                     max_row_tokens=batch.max_row_tokens, out=self.out, lse=self.lse, num_tokens=T,
+                                     fixed_splits=fixed_splits)
         n = C.c_int64(0)
         _lib.check(self.lib.cp_paged_attn_workspace_size(C.byref(self.paged), C.byref(n)))
         self.workspace_bytes = int(n.value)

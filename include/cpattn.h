@@ -51,6 +51,9 @@ extern "C" {
 /* P <= 16 stripes plus the own-token partial. */
 #define CPATTN_MAX_PARTIALS 17
 
+/* cp_paged_args.flags */
+#define CPATTN_FLAG_FIXED_SPLITS 1   /* see cp_paged_attn_partial: results independent of the rest of the call */
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* cpattn_last_error(void);
 
@@ -142,7 +145,7 @@ typedef struct cp_paged_args {
     int32_t max_ctx_len;      /* host upper bound of ctx_len[b], sizes the launch; larger device values are clamped */
     int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
     int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
-    int32_t reserved0;
+    int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */
     const int32_t* q_row_start;  /* device int32 [num_rows + 1], non-decreasing, q_row_start[num_rows] <= num_tokens */
     const int32_t* ctx_len;      /* device int32 [num_rows]: context tokens of row b in the pool (all stripes) */
     const int32_t* block_table;  /* device int32 [num_rows, bt_stride]: logical page ids */
@@ -177,7 +180,15 @@ typedef struct cp_paged_args {
  * context (no mask). Rows with ctx_len[b] <= r give (0, -inf). Padding tokens get out = 0 and lse = -inf and their
  * queries are not read.
  *
- * EINVAL: a null args/pointer, Hq % Hkv != 0, page_size % P != 0, a stripe range outside [0, P), negative sizes or
+ * Rounding. A stripe's keys may be split into pieces that are merged exactly; only the rounding of the result depends
+ * on where the splits fall. By default the bf16 head_dim-128 decode path balances the whole call's work over the
+ * device's resident waves, so split points, and the last bits of a row's result, depend on the rest of the call (other
+ * rows, the stripe range) and on the device's compute-unit count; identical calls on one device give identical bits.
+ * With CPATTN_FLAG_FIXED_SPLITS the splits fall at fixed key offsets of each stripe, so a row's result is the same to
+ * the bit whatever else the call holds (e.g. one stripe alone equals that stripe of an all-stripes call), at some cost
+ * in speed when context lengths vary widely.
+ *
+ * EINVAL: a null args/pointer, unknown flag bits, Hq % Hkv != 0, page_size % P != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
  * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
  * (128, 128); MLA bf16 with (576, 512).

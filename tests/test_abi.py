@@ -89,6 +89,8 @@ def _paged(**kw):
     (dict(q=0), _lib.CPATTN_EINVAL),
     (dict(num_rows=-1), _lib.CPATTN_EINVAL),
     (dict(kv_stride_page=-8), _lib.CPATTN_EINVAL),
+    (dict(flags=2), _lib.CPATTN_EINVAL),
+    (dict(flags=-1), _lib.CPATTN_EINVAL),
 ])
 def test_paged_refusals(lib, bad, code):
     a = _paged(**bad)
@@ -115,6 +117,14 @@ def test_paged_workspace_size_is_host_only(lib):
     assert "workspace" in _err(lib)
     b = _paged(dtype=0)
     assert lib.cp_paged_attn_workspace_size(C.byref(b), C.byref(n)) == _lib.CPATTN_OK and n.value == 0
+    # fixed splits: chunks of 64 steps (1024 keys) of a stripe; 4096 context tokens over 4 stripes fit one chunk
+    f = _paged(flags=_lib.CPATTN_FLAG_FIXED_SPLITS, max_ctx_len=4096, kv_stride_slot=128, kv_stride_head=512,
+               kv_stride_page=4096, kv_stride_stripe=40960, q_stride_token=4096, q_stride_head=128,
+               out_stride_stripe=8192, out_stride_token=4096, out_stride_head=128, lse_stride_stripe=64,
+               lse_stride_token=32)
+    assert lib.cp_paged_attn_workspace_size(C.byref(f), C.byref(n)) == _lib.CPATTN_OK and n.value == 0
+    f.max_ctx_len = 4 * 16 * 64 + 1          # one stripe now needs a second chunk
+    assert lib.cp_paged_attn_workspace_size(C.byref(f), C.byref(n)) == _lib.CPATTN_OK and n.value > 0
 
 
 def test_own_token_refusals(lib):
