@@ -168,10 +168,11 @@ def main():
         if rec.get("kernel_hash") == kernel_source_hash() and rec.get("workload") == wl.name:
             traffic = rec.get("bytes_per_launch")
 
-    flops = None
-    if wl.kind == "gqa":
-        flops = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64)) * wl.num_q_heads * 2 * (
-            wl.head_dim + wl.head_dim_v)
+    # Algorithmic flops of the partial: every (query token, context token) pair costs Hq * 2 * (D + Dv).
+    flops = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64)) * wl.num_q_heads * 2 * (
+        wl.head_dim + wl.head_dim_v)
+    kernel_names = {"gqa": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
+                    "mla": "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel)"}
     result = {
         "metric": "striped paged-attention decode: KV GB/s (% of HBM peak) and query tokens/s",
         "value": round(value, 2),
@@ -195,11 +196,13 @@ def main():
                       "merge_avg": round(float(np.mean(merge_ms)), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
+                     "kernel": kernel_names.get(wl.kind, "cp_paged_attn_partial"),
                      "bytes_per_launch": kv_bytes},
     }
     if flops:
-        result["tflops_partial"] = round(flops / (part_avg * 1e-3) / 1e12, 3)
+        tflops = flops / (part_avg * 1e-3) / 1e12
+        result["tflops_partial"] = round(tflops, 3)
+        result["mfma_frac_partial"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

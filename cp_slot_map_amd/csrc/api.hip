@@ -78,6 +78,7 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
 
 static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
     if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes(a);
+    if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
     return 0;
 }
 
@@ -115,6 +116,7 @@ extern "C" int32_t cp_paged_attn_partial(const cp_paged_args* a, hipStream_t str
                     (long long)a->workspace_bytes);
     if (a->num_tokens == 0) return CPATTN_OK;
     if (decode_bf16_eligible(*a, geo)) return launch_paged_decode_bf16(*a, geo, stream);
+    if (mla_decode_eligible(*a, geo)) return launch_mla_decode(*a, geo, stream);
     return launch_paged_generic(*a, geo, stream);
 }
 

@@ -15,6 +15,12 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
 
+// Specialised bf16 MLA partial (one latent head of 576, values its first 512; 16, 32, 64 or 128 query heads) with MFMA
+// score and value products over latent tiles staged in LDS.
+bool mla_decode_eligible(const cp_paged_args& a, const PoolGeom& geo);
+int64_t mla_decode_workspace_bytes(const cp_paged_args& a);
+int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+
 // (0, -inf) for the padding tokens [q_row_start[num_rows], num_tokens) of all S partials.
 int32_t launch_pad_partials(const cp_paged_args& a, hipStream_t stream);
 
