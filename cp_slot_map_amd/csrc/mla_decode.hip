@@ -5,32 +5,38 @@
 // one latent head of MLA shared by all query heads (mstar PR #1124, "Context / Sequence Parallel 1/5", PR description:
 // the context-parallel decode covers MLA's single latent head as well as GQA).
 //
-// Work decomposition. A unit is (row b, stripe s, query token, chunk of the stripe's local tokens). It runs on one
-// workgroup of NW <= 4 waves per group of 16 NW query heads (two workgroups for 128 heads); each wave owns 16 heads.
-// The latent rows of the unit stream through LDS in tiles of 32 tokens (three buffers, two tiles in flight), loaded
-// straight from global memory into LDS, and every wave reads each tile twice: as the key operand of the score product
-// and as the value operand of the output product. 16 heads per wave keeps the query operand (72 VGPRs) and the output
-// accumulators (128) in registers at one wave per SIMD; 32 heads per wave would halve the LDS reads but does not fit.
-// A small plan kernel orders the units longest first, so the hardware's in-order dispatch packs long and short units
-// onto the same compute unit. A stripe longer than one chunk leaves one unnormalised record per chunk and a merge
-// kernel combines them exactly.
+// Work decomposition. A unit is (row b, stripe s, query token, chunk of the stripe's local tokens). One workgroup of
+// Hq / 16 waves (eight for 128 heads, two per SIMD) serves all query heads of a unit, so each latent tile is fetched
+// once; each wave owns 16 heads. The latent rows stream through LDS in tiles of 32 tokens (four buffers, three tiles
+// in flight), loaded straight from global memory into LDS, and every wave reads each tile twice: as the key operand of
+// the score product and as the value operand of the output product. 16 heads per wave keeps the query operand (72
+// VGPRs) and the output accumulators (128) in registers; 32 heads per wave would halve the LDS reads but does not fit.
+// The chunk's page ids are staged in LDS when a unit starts. A small plan kernel orders the units longest first, so
+// the hardware's in-order dispatch packs long and short units onto the same compute unit. A stripe longer than one
+// chunk leaves one unnormalised record per chunk and a merge kernel combines them exactly.
 //
 // Per tile and wave (16 heads x 32 tokens):
 //   * scores S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_bf16: A = latent rows (token per lane, 8 dims per
 //     lane group), B = the wave's query heads, held in registers for the whole unit. 36 MFMAs.
-//   * online softmax in log2 units with a lazily moved running max (moved only when a tile maximum exceeds it by more
-//     than 8). The running sum adds the fp32 probabilities, so the lse keeps fp32 accuracy; the value product takes
+//   * softmax in log2 units against a fixed per-head reference, the maximum of the unit's first tile; later scores
+//     may exceed it by up to 64 without rescaling anything (a unit whose scores rise further is repeated with the
+//     exact maximum as reference). The accumulators are thus written only by MFMAs and stay in the accumulation
+//     registers. The running sum adds the fp32 probabilities, so the lse keeps fp32 accuracy; the value product takes
 //     them rounded to bf16 (a relative change of at most 2^-9 per weight, which averages out over a stripe's tokens).
 //   * out += P . V with v_mfma_f32_16x16x32_bf16: the score layout left by the first product is already the A-operand
 //     layout (k index 8c + e of lane group c is tile token 16 (e / 4) + 4c + e % 4), and the B operand of each 16-dim
 //     output tile comes from two transposed LDS reads (ds_read_b64_tr_b16), so no register staging or permutes are
 //     needed. 32 MFMAs into 128 accumulator registers.
 //
-// LDS layout of a tile: token t's 72 16-byte pieces at [72t, 72t + 72), piece p stored at 72t + (p ^ g(t)) with
-// g(t) = (t ^ (t >> 2)) & 7. Measured on gfx950, both read patterns (sixteen tokens at one piece for the score operand,
-// the transposed reads of four tokens for the value operand) then run at the full rate of their instruction; without
-// the swizzle the score reads run at a quarter and the value reads at half of it.
+// LDS layout of a tile (37,888 bytes; three buffers): the value dims [0, 512) of token t in a row of 1056 bytes at
+// 1056 t (1024 bytes of data, 32 of padding), the rope dims [512, 576) in a 128-byte row at 33,792 + 128 t whose eight
+// 16-byte pieces are stored XOR g(t) = (t ^ (t >> 2)) & 7. Measured on gfx950, the three read patterns (sixteen
+// tokens at one 16-byte piece for the score operand, in either region, and the transposed reads of four tokens for
+// the value operand) then run at the full rate of their instruction; with unpadded 1024-byte rows they run at an
+// eighth of it.
 #include "launch.h"
+
+#include <type_traits>
 
 namespace cpattn {
 
@@ -39,9 +45,13 @@ namespace {
 constexpr int kD = 576;                        // latent row (key) length
 constexpr int kDv = 512;                       // value length
 constexpr int kTile = 32;                      // tokens per LDS tile
-constexpr int kPieces = kD / 8;                // 16-byte pieces per latent row
-constexpr int kTileChunks = kTile * kPieces;   // 16-byte pieces per tile
-constexpr int kBufs = 3;
+constexpr int kRowV = 1056;                    // LDS bytes per token for dims [0, 512): 1024 + 32 of padding
+constexpr int kRegionV = kTile * kRowV;        // value-dim region of a tile
+constexpr int kRowR = 128;                     // LDS bytes per token for the rope dims [512, 576)
+constexpr int kTileBytes = kRegionV + kTile * kRowR;
+constexpr int kBufs = 4;                       // LDS tile buffers: three tiles in flight while one is computed
+constexpr int kAhead = kBufs - 1;
+constexpr int kMaxChunkPages = 1024;           // page ids of one chunk staged in LDS
 constexpr int kKSteps = kD / 32;               // k-steps of the score product
 constexpr int kMaxPlanUnits = 1024;            // units sorted by the plan kernel (block order above)
 constexpr int kTargetUnits = 512;              // about two units per compute unit before chunks are split
@@ -49,6 +59,8 @@ constexpr int kTargetUnits = 512;              // about two units per compute un
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+typedef __attribute__((address_space(3))) char* lds_char_ptr;
+typedef const __attribute__((address_space(3))) int32_t* lds_i32_ptr;
 
 struct MlaParams {
     const uint16_t* q;
@@ -65,6 +77,8 @@ struct MlaParams {
     int64_t l_ss, l_st;
     float* ws_rec;          // n_units records of rec_floats when n_chunks > 1
     int32_t* order;         // unit of each block, longest first; null: block order
+    int32_t* ws_redo;       // per (unit, head group): 1 when the workgroup's scores outgrew its reference
+    float* ws_max;          // per (unit, query head): exact score maximum (log2 units) of a unit to redo
     int64_t rec_floats;
     int32_t B, T, P, stripe_begin, S, Hq, max_pages, page_size, max_row_tokens;
     int32_t n_chunks, chunk_tokens, n_units, pad_blocks, pad_tokens_per_block;
@@ -72,7 +86,7 @@ struct MlaParams {
     float scale_log2;
 };
 
-__device__ __forceinline__ int swz(int t) { return (t ^ (t >> 2)) & 7; }
+__device__ __forceinline__ int swz(int t) { return (t ^ (t >> 2)) & 7; }   // rope-region piece swizzle
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -122,40 +136,52 @@ __device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
     return max(0, min(Lr - c * p.chunk_tokens, p.chunk_tokens));
 }
 
-// Page ids of a tile, one per lane: lane L holds the block-table entry of tile token L % 32 (tokens past the chunk end
-// take its last token). Loaded an iteration before the tile's own loads are issued; checked where used.
-__device__ __forceinline__ int32_t load_tile_pages(const MlaParams& p, const int32_t* __restrict__ bt_row,
-                                                   int32_t tile0, int32_t j_last, int lane) {
+// Byte address of tile token L % 32's latent row in lane L, from the chunk's page ids staged in LDS (tokens past the
+// chunk end take its last token, whose values are masked out; invalid page ids read page 0).
+__device__ __forceinline__ uint64_t token_rows(const MlaParams& p, lds_i32_ptr s_pages, int32_t pidx0, int32_t tile0,
+                                               int32_t j_last, const char* kv_r, int lane) {
     const int32_t j = min(tile0 + (lane & 31), j_last);
-    return bt_row[j >> p.geo.pp_shift];
+    int32_t page = s_pages[(j >> p.geo.pp_shift) - pidx0];
+    page = (page >= 0 && page < p.geo.num_pages) ? page : 0;
+    const int64_t row = int64_t(page) * p.geo.s_page + int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot;   // elements
+    return reinterpret_cast<uint64_t>(kv_r) + uint64_t(row) * 2u;
 }
 
-// Issue the direct-to-LDS loads of one tile: wave w's instruction k fills pieces [64 (NW k + w), +64) of the buffer.
-// The 64 pieces of one instruction belong to at most two tokens; their page ids come from the tile's page vector with
-// readlane, so the page bases are formed on the scalar unit. Tokens past the chunk end re-read its last token (their
-// values are masked out).
+// Issue the direct-to-LDS loads of one tile.
+//   * value dims [0, 512): wave w takes tokens [T w, T w + T) with T = 32 / NW, one instruction per token: 64 lanes x
+//     16 bytes = the token's 1024 bytes, written to its padded LDS row. The row address is moved to scalar registers
+//     with readlane, so each lane adds only its fixed 16-byte offset.
+//   * rope dims [512, 576): 4-byte loads, 32 lanes per token, two tokens per instruction (16 per tile, shared evenly
+//     by the waves, so every wave issues the same loads and no lane is masked); lane l fills dword l % 32 of its
+//     token's rope row, i.e. stored piece (l % 32) / 4, with the matching dword of logical piece ((l % 32) / 4) ^ g(t).
 template <int NW>
-__device__ __forceinline__ void issue_tile(const MlaParams& p, int32_t pages, int64_t base_r, int32_t tile0,
-                                           int32_t j_last, u32x4_t* buf, int32_t w, int lane) {
-    constexpr int kInstr = kTileChunks / (64 * NW);
+__device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int32_t w, int lane) {
+    constexpr int kTpw = kTile / NW;
+    const uint32_t alo = uint32_t(rows), ahi = uint32_t(rows >> 32);
 #pragma unroll
-    for (int k = 0; k < kInstr; ++k) {
-        const int32_t c0 = 64 * (NW * k + w);                  // wave-uniform
-        const int32_t ta = c0 / kPieces;
-        const int32_t tb = (c0 + 63) / kPieces;
-        int32_t pa = __builtin_amdgcn_readlane(pages, ta);
-        int32_t pb = __builtin_amdgcn_readlane(pages, tb);
-        pa = (pa >= 0 && pa < p.geo.num_pages) ? pa : 0;
-        pb = (pb >= 0 && pb < p.geo.num_pages) ? pb : 0;
-        const uint16_t* base_a = p.kv + base_r + int64_t(pa) * p.geo.s_page;
-        const uint16_t* base_b = p.kv + base_r + int64_t(pb) * p.geo.s_page;
-        const int32_t c = c0 + lane;
-        const int32_t t = c / kPieces;
-        const int32_t piece = (c - t * kPieces) ^ swz(t);
-        const int32_t j = min(tile0 + t, j_last);
-        const uint16_t* src = (t == ta ? base_a : base_b) + int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot + 8 * piece;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(buf + c0), 16, 0, 0);
+    for (int i = 0; i < kTpw; ++i) {
+        const int32_t t = kTpw * w + i;                                          // wave-uniform
+        const uint64_t base = (uint64_t(uint32_t(__builtin_amdgcn_readlane(ahi, t))) << 32) |
+                              uint32_t(__builtin_amdgcn_readlane(alo, t));
+        const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * lane);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t), 16, 0, 0);
     }
+    constexpr int kRInstr = (kTile / 2) / NW;                                    // 256-byte instructions
+#pragma unroll
+    for (int i = 0; i < kRInstr; ++i) {
+        const int32_t pair = kRInstr * w + i;                                    // tokens 2 pair, 2 pair + 1
+        const int32_t t = 2 * pair + (lane >> 5);
+        const int32_t q = lane & 31;                                             // dword of the 128-byte rope row
+        const uint64_t base = (uint64_t(uint32_t(__shfl(int32_t(ahi), t))) << 32) | uint32_t(__shfl(int32_t(alo), t));
+        const char* src = reinterpret_cast<const char*>(base) + 1024 + 16 * ((q >> 2) ^ swz(t)) + 4 * (q & 3);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRegionV + kRowR * 2 * pair), 4, 0, 0);
+    }
+}
+
+// Direct-to-LDS loads a wave issues per tile (the same for every wave).
+template <int NW>
+__device__ __forceinline__ constexpr int tile_loads() {
+    return kTile / NW + (kTile / 2) / NW;
 }
 
 // s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
@@ -163,6 +189,28 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most the loads of kAhead - 1 tiles are outstanding (the counter saturates at 63: with one or two
+// waves a little more than the oldest tile is waited for).
+template <int NW>
+__device__ __forceinline__ void wait_tile() {
+    constexpr int kN = (kAhead - 1) * tile_loads<NW>();
+    wait_vmcnt<(kN < 63 ? kN : 63)>();
+}
+
+// Scheduling groups: AHEAD LDS reads first, then (one MFMA, R reads) until the N MFMAs of the region are placed.
+// Only shapes the order the compiler picks; every dependence is still honoured.
+template <int N, int R, int AHEAD>
+__device__ __forceinline__ void sched_pipeline() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N - AHEAD / R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD / R, 0);
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (those would drain the tiles in flight); the empty
@@ -193,14 +241,22 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const MlaParams p) {
 }
 
 // One workgroup per (unit, group of 16 NW heads); wave w of group hg owns heads hg 16 NW + 16 w + [0, 16).
-template <int NW>
+template <int NW, bool REDO>
 __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams p) {
-    __shared__ u32x4_t s_buf[kBufs][kTileChunks];
+    // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
+    // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
+    __shared__ __attribute__((aligned(16))) char s_tile0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile2[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile3[kTileBytes];
+    __shared__ int32_t s_pages[kMaxChunkPages];
+    __shared__ int32_t s_over[NW];
     const int lane = threadIdx.x & 63;
     const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t blk = blockIdx.x;
 
     if (blk >= p.work_blocks) {                             // padding-token fill role
+        if (REDO) return;
         const int32_t k = blk - p.work_blocks;
         const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
         const int32_t t0 = max(k * p.pad_tokens_per_block, first);
@@ -210,13 +266,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
                          blockDim.x);
         return;
     }
-    // Block -> (unit rank, head group). With two head groups, the groups of one unit are 8 blocks apart: the same XCD
-    // (blocks go round-robin over the 8 XCDs), so the second group's tile reads hit that XCD's L2.
-    int32_t rank = blk, hg = 0;
-    if (p.head_groups == 2) {
-        rank = (blk >> 4) * 8 + (blk & 7);
-        hg = (blk >> 3) & 1;
-    }
+    const int32_t rank = blk, hg = 0;                       // one workgroup serves all query heads of a unit
     if (rank >= p.n_units) return;
     const int32_t u = p.order ? __builtin_amdgcn_readfirstlane(((const_i32_ptr)p.order)[rank]) : rank;
     const Unit x = decode_unit(p, u);
@@ -236,7 +286,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     }
 
     const int32_t r = p.stripe_begin + x.s;
-    const int64_t base_r = int64_t(r) * p.geo.s_stripe;
+    const char* kv_r = reinterpret_cast<const char*>(p.kv + int64_t(r) * p.geo.s_stripe);
     const int32_t* bt_row = p.bt + int64_t(x.b) * p.bt_stride;
     const int32_t j_last = x.j1 - 1;
     const int32_t ntiles = (x.j1 - x.j0 + kTile - 1) / kTile;
@@ -249,125 +299,174 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
     }
 
-    // Two tiles in flight before the loop; every iteration issues the page ids of tile kt + 3, then the loads of tile
-    // kt + 2 (tile indices past the end re-read the last tile into a buffer nobody reads). The wait at the top of an
-    // iteration leaves exactly the newest tile's loads outstanding: tile kt and the page ids of tile kt + 2 are in.
-    constexpr int kInstr = kTileChunks / (64 * NW);
-    const int32_t last_tile0 = x.j0 + (ntiles - 1) * kTile;
-    int32_t pages_next;
+    // The chunk's page ids, staged once in LDS (at most kMaxChunkPages by the choice of chunk length). The barrier's
+    // wait also retires the query loads above, so nothing but tile loads is outstanding inside the loop (the
+    // wait-count pass would otherwise drain every tile load in flight before the first use of the query operand).
+    const int32_t pidx0 = x.j0 >> p.geo.pp_shift;
     {
-        const int32_t pg0 = load_tile_pages(p, bt_row, x.j0, j_last, lane);
-        const int32_t pg1 = load_tile_pages(p, bt_row, min(x.j0 + kTile, last_tile0), j_last, lane);
-        pages_next = load_tile_pages(p, bt_row, min(x.j0 + 2 * kTile, last_tile0), j_last, lane);
-        issue_tile<NW>(p, pg0, base_r, x.j0, j_last, s_buf[0], w, lane);
-        issue_tile<NW>(p, pg1, base_r, min(x.j0 + kTile, last_tile0), j_last, s_buf[1], w, lane);
+        const int32_t npages = (j_last >> p.geo.pp_shift) - pidx0 + 1;
+        for (int32_t i = threadIdx.x; i < npages; i += 64 * NW) s_pages[i] = bt_row[pidx0 + i];
+        __syncthreads();
     }
 
-    f32x4_t o[32];                                   // o[b][i]: head hw + 4 c4 + i, dim 16 b + n16 (unnormalised)
-#pragma unroll
-    for (int b = 0; b < 32; ++b) o[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float m = neg_inf(), l = 0.f;
-
-    // Per-lane LDS piece offsets. Score operand: token 16 tb + n16, piece 4 ks + c4 -> 4 ks ^ (c4 ^ g(t)).
-    int32_t kofs_even[2], kofs_odd[2];
+    // Per-lane LDS byte offsets inside a tile (each read adds a compile-time immediate):
+    //   score operand, dims [0, 512): token 16 tb + n16, bytes 64 ks + 16 c4 of its row;
+    //   score operand, rope dims: token 16 tb + n16, stored piece (4 k' + c4) ^ g(t) of its rope row (k' = ks - 16);
+    //   value operand through transposed reads (ds_read_b64_tr_b16): in each 16-lane group, lane s supplies four
+    //   consecutive values of one row and lane q receives element q % 4 of rows q / 4, 4 + q / 4, 8 + q / 4, 12 + q / 4.
+    //   Lane s of group c4 points at token 16 r + 4 c4 + s / 4, dims 16 b + 4 (s % 4) (read r = 0, 1 of dim block b),
+    //   so lane q receives dim 16 b + q of tokens 8 c4 + e in k order: the B operand, with no permutes.
+    int32_t kofs_v[2], kofs_r[2][2], vofs[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         const int32_t t = 16 * tb + n16;
-        const int32_t xg = c4 ^ swz(t);
-        kofs_even[tb] = kPieces * t + xg;          // ks even: 4 ks + xg
-        kofs_odd[tb] = kPieces * t + (xg ^ 4) - 4; // ks odd: 4 ks - 4 + (xg ^ 4)
+        kofs_v[tb] = kRowV * t + 16 * c4;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) kofs_r[tb][k] = kRegionV + kRowR * t + 16 * ((4 * k + c4) ^ swz(t));
     }
-    // Value operand through transposed LDS reads (ds_read_b64_tr_b16): in each 16-lane group, lane s supplies four
-    // consecutive values of one row and lane q receives element q % 4 of rows q / 4, 4 + q / 4, 8 + q / 4, 12 + q / 4.
-    // Lane s of group c4 points at token 16 r + 4 c4 + s / 4, dims 16 b + 4 (s % 4) (read r = 0, 1 of dim block b),
-    // so lane q of the group receives dim 16 b + q of tokens 8 c4 + e in k order: the B operand, with no permutes.
-    // Byte offset: token t's piece (2 b + (s / 2) % 2) ^ g(t), plus 8 (s % 2); the dim block enters as 2 b ^ y with
-    // y = (s / 2) % 2 ^ g(t), which splits into a lane part for b % 4 and an immediate 128 (b / 4).
-    int32_t vbase[2][4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int32_t t = 16 * r + 4 * c4 + (n16 >> 2);
-        const int32_t y = ((n16 >> 1) & 1) ^ swz(t);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vbase[r][k] = 16 * (kPieces * t + ((2 * k) ^ y)) + 8 * (n16 & 1);
-    }
-    const lds_s16x4_ptr lds_bytes0 = (lds_s16x4_ptr)(s_buf[0]);
+    for (int r = 0; r < 2; ++r) vofs[r] = kRowV * (16 * r + 4 * c4 + (n16 >> 2)) + 8 * (n16 & 3);
+    // Buffer b of the ring, b a compile-time constant.
+    auto tile_buf = [&](auto bc) __attribute__((always_inline)) -> lds_char_ptr {
+        constexpr int b = decltype(bc)::value % kBufs;
+        return b == 0 ? (lds_char_ptr)s_tile0 : b == 1 ? (lds_char_ptr)s_tile1 : b == 2 ? (lds_char_ptr)s_tile2
+                                                                                   : (lds_char_ptr)s_tile3;
+    };
 
-    for (int32_t kt = 0; kt < ntiles; ++kt) {
-        wait_vmcnt<kInstr>();                       // this wave's pieces of tile kt are in LDS
-        lds_barrier();                              // ... and every wave's; tile kt - 1's buffer is free
-        {
-            const int32_t pages = pages_next;
-            pages_next = load_tile_pages(p, bt_row, min(x.j0 + (kt + 3) * kTile, last_tile0), j_last, lane);
-            issue_tile<NW>(p, pages, base_r, min(x.j0 + (kt + 2) * kTile, last_tile0), j_last,
-                           s_buf[(kt + 2) % kBufs], w, lane);
-        }
-        const u32x4_t* buf = s_buf[kt % kBufs];
-        const int32_t tile0 = x.j0 + kt * kTile;
-        const bool tail = tile0 + kTile > x.j1;
+    const int32_t last_tile0 = x.j0 + (ntiles - 1) * kTile;
 
-        // Scores S^T[token 16 tb + 4 c4 + i][head n16].
-        f32x4_t sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // Softmax reference. Each head's probabilities are taken relative to a fixed reference m: the maximum of the
+    // unit's first tile. Later tiles may exceed it by up to kRefSlack (log2 units) without any rescaling of the
+    // accumulators (p <= 2^64 and sums of such values stay far inside the fp32 and bf16 range), so they are written
+    // only by MFMAs and stay in the accumulation registers. Should a head's scores rise further, the workgroup leaves
+    // its outputs unwritten, records the exact maxima and a redo flag, and the REDO launch of this kernel computes the
+    // unit again with the exact maxima as references.
+    constexpr float kRefSlack = 64.0f;
+    if (REDO && !p.ws_redo[int64_t(u) * p.head_groups + hg]) return;
+    float m = REDO ? p.ws_max[int64_t(u) * p.Hq + hw + n16] : neg_inf();
+    float m_seen = neg_inf(), l = 0.f;
+    bool over = false;
+    f32x4_t o[32];                                   // o[b][i]: head hw + 4 c4 + i, dim 16 b + n16 (unnormalised)
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
+    for (int b = 0; b < 32; ++b) o[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    {
+        // kAhead tiles in flight before the loop; every iteration issues one more (tile indices past the end re-read
+        // the last tile into a buffer nobody reads), so the wait at the top of an iteration leaves exactly the
+        // kAhead - 1 newest tiles' loads outstanding.
+        const lds_i32_ptr pages = (lds_i32_ptr)s_pages;
+        issue_tile<NW>(token_rows(p, pages, pidx0, x.j0, j_last, kv_r, lane), tile_buf(std::integral_constant<int, 0>{}),
+                       w, lane);
+        issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + kTile, last_tile0), j_last, kv_r, lane),
+                       tile_buf(std::integral_constant<int, 1>{}), w, lane);
+        issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + 2 * kTile, last_tile0), j_last, kv_r, lane),
+                       tile_buf(std::integral_constant<int, 2>{}), w, lane);
+        static_assert(kAhead == 3 && kBufs == 4, "ring");
+
+        // Compute tile kt from `tile`.
+        auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
+            const int32_t tile0 = x.j0 + kt * kTile;
+            const bool tail = tile0 + kTile > x.j1;
+            // This tile's lane base addresses, formed once so that every read below carries its remaining offset as
+            // an instruction immediate.
+            lds_char_ptr kb_v[2], kb_r[2][2], vb[2];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                const int32_t pos = (ks & 1) ? kofs_odd[tb] + 4 * ks : kofs_even[tb] + 4 * ks;
-                sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf[pos]), as_bf16x8(qreg[ks]), sacc[tb],
-                                                                   0, 0, 0);
+                kb_v[tb] = tile + kofs_v[tb];
+                kb_r[tb][0] = tile + kofs_r[tb][0];
+                kb_r[tb][1] = tile + kofs_r[tb][1];
             }
-        }
+            vb[0] = tile + vofs[0];
+            vb[1] = tile + vofs[1];
 
-        // Online softmax.
-        float sv[8];
+            // Scores S^T[token 16 tb + 4 c4 + i][head n16].
+            f32x4_t sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = sacc[e >> 2][e & 3] * p.scale_log2;
-            if (tail && tile0 + 16 * (e >> 2) + 4 * c4 + (e & 3) >= x.j1) v = neg_inf();
-            sv[e] = v;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m + 8.0f)) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = exp2f(m - m_new);     // 0 on the first tile (m = -inf)
-            l *= alpha;
-            m = m_new;
-            float a_o[4];
+            for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a_o[i] = __shfl(alpha, 4 * c4 + i);
-#pragma unroll
-            for (int b = 0; b < 32; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[b][i] *= a_o[i];
-        }
-        u32x4_t pa;
-        {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sv[e] - m);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) pa[d] = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
-            l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        }
-
-        // Values: 32 output tiles of 16 dims, each from two transposed reads.
-        {
-            const int32_t buf_bytes = (kt % kBufs) * kTileChunks * 16;
-#pragma unroll
-            for (int b = 0; b < 32; ++b) {
-                const int32_t imm = buf_bytes + 128 * (b >> 2);
-                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)((__attribute__((address_space(3))) char*)lds_bytes0 + vbase[0][b & 3] + imm));
-                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)((__attribute__((address_space(3))) char*)lds_bytes0 + vbase[1][b & 3] + imm));
-                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), bop, o[b], 0, 0, 0);
+                for (int tb = 0; tb < 2; ++tb) {
+                    const lds_char_ptr a = ks < 16 ? kb_v[tb] + 64 * ks : kb_r[tb][ks - 16];
+                    const u32x4_t kv = *(const __attribute__((address_space(3))) u32x4_t*)a;
+                    sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qreg[ks]), sacc[tb],
+                                                                       0, 0, 0);
+                }
             }
+            sched_pipeline<kKSteps * 2, 1, 6>();     // six operand reads ahead, then one read per MFMA
+
+            // Probabilities against the fixed reference.
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = sacc[e >> 2][e & 3] * p.scale_log2;
+                if (tail && tile0 + 16 * (e >> 2) + 4 * c4 + (e & 3) >= x.j1) v = neg_inf();
+                sv[e] = v;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_seen = fmaxf(m_seen, mx);
+            if (!REDO && kt == 0) m = mx;           // the first tile always holds a real token
+            over |= mx > m + kRefSlack;
+            u32x4_t pa;
+            {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fminf(sv[e] - m, kRefSlack));
+#pragma unroll
+                for (int d = 0; d < 4; ++d) pa[d] = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
+                l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+            }
+
+            // Values: 32 output tiles of 16 dims, each from two transposed reads.
+            {
+#pragma unroll
+                for (int b = 0; b < 32; ++b) {
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb[0] + 32 * b));
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb[1] + 32 * b));
+                    const bf16x8_t bop =
+                        __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                    o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), bop, o[b], 0, 0, 0);
+                }
+                sched_pipeline<32, 2, 8>();         // four output tiles' operands ahead
+            }
+        };
+
+        // One iteration with buffer b (compile time): wait for tile kt, issue the loads of tile kt + kAhead into
+        // buffer b + kAhead, compute tile kt from buffer b.
+        auto step = [&](auto bc, int32_t kt) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            // This wave's pieces of tile kt are in LDS: the loads of the kAhead - 1 newer tiles may stay in flight.
+            wait_tile<NW>();
+            lds_barrier();                          // ... and every wave's; tile kt - 1's buffer is free
+            const int32_t tn0 = min(x.j0 + (kt + kAhead) * kTile, last_tile0);
+            issue_tile<NW>(token_rows(p, pages, pidx0, tn0, j_last, kv_r, lane),
+                           tile_buf(std::integral_constant<int, b + kAhead>{}), w, lane);
+            tile_compute(tile_buf(std::integral_constant<int, b>{}), kt);
+        };
+        for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
+            step(std::integral_constant<int, 0>{}, kt);
+            if (kt + 1 >= ntiles) break;
+            step(std::integral_constant<int, 1>{}, kt + 1);
+            if (kt + 2 >= ntiles) break;
+            step(std::integral_constant<int, 2>{}, kt + 2);
+            if (kt + 3 >= ntiles) break;
+            step(std::integral_constant<int, 3>{}, kt + 3);
+        }
+        wait_vmcnt<0>();                            // the over-issued tail loads land before the waves retire
+    }
+    if (!REDO) {
+        // A workgroup-wide decision, so that every wave takes the same path.
+        if (lane == 0) s_over[w] = __any(over) ? 1 : 0;
+        __syncthreads();
+        int32_t any_over = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) any_over |= s_over[v];
+        if (threadIdx.x == 0) p.ws_redo[int64_t(u) * p.head_groups + hg] = any_over;
+        if (any_over) {
+            if (c4 == 0) p.ws_max[int64_t(u) * p.Hq + hw + n16] = m_seen;
+            return;
         }
     }
-    wait_vmcnt<0>();                                // the over-issued tail loads land before the waves retire
 
     // Epilogue: row sums over the four lane groups, then the normalised partial or this chunk's record.
     const bool split = p.n_chunks > 1 && x.Lr > p.chunk_tokens;
@@ -445,14 +544,17 @@ MlaShape mla_shape(const cp_paged_args& a) {
     }
     int64_t ch = std::max<int64_t>(kTile, (max_lr + nch - 1) / nch);
     ch = (ch + kTile - 1) / kTile * kTile;
+    // A chunk's page ids must fit the LDS staging area: at most kMaxChunkPages pages of page_size / P slots.
+    const int64_t pp = std::max<int64_t>(1, a.page_size / std::max(1, a.num_partners));
+    ch = std::min<int64_t>(ch, (kMaxChunkPages - 1) * pp / kTile * kTile);
     d.chunk_tokens = ch;
     d.n_chunks = std::max<int64_t>(1, (max_lr + ch - 1) / ch);
     d.n_units = d.n_items * d.n_chunks;
     d.rec_floats = int64_t(a.num_q_heads) * (kDv + 2);
     d.plan = d.n_units <= kMaxPlanUnits;
-    d.nw = std::min<int64_t>(4, a.num_q_heads / 16);
-    d.head_groups = d.nw > 0 ? a.num_q_heads / (16 * d.nw) : 1;
-    d.work_blocks = d.head_groups == 2 ? (d.n_units + 7) / 8 * 16 : d.n_units;
+    d.nw = std::min<int64_t>(8, a.num_q_heads / 16);
+    d.head_groups = 1;
+    d.work_blocks = d.n_units;
     return d;
 }
 
@@ -473,11 +575,24 @@ bool mla_decode_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     return true;
 }
 
+// Workspace: [unit order (plan)] [chunk records (split stripes)] [redo flags] [score maxima of units to redo].
+struct MlaWorkspace {
+    int64_t order, rec, redo, max, total;
+};
+
+MlaWorkspace mla_workspace(const MlaShape& d, int64_t hq) {
+    MlaWorkspace w{};
+    w.order = 0;
+    w.rec = d.plan ? align256(4 * d.n_units) : 0;
+    w.redo = w.rec + (d.n_chunks > 1 ? align256(d.n_units * d.rec_floats * 4) : 0);
+    w.max = w.redo + align256(4 * d.n_units * d.head_groups);
+    w.total = w.max + align256(4 * d.n_units * hq);
+    return w;
+}
+
 int64_t mla_decode_workspace_bytes(const cp_paged_args& a) {
     const MlaShape d = mla_shape(a);
-    int64_t bytes = d.plan ? align256(4 * d.n_units) : 0;
-    if (d.n_chunks > 1) bytes += d.n_units * d.rec_floats * 4;
-    return bytes;
+    return d.n_units > 0 ? mla_workspace(d, a.num_q_heads).total : 0;
 }
 
 int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
@@ -500,8 +615,11 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.l_ss = a.lse_stride_stripe;
     p.l_st = a.lse_stride_token;
     char* ws = static_cast<char*>(a.workspace);
-    p.order = d.plan && d.n_units > 0 ? reinterpret_cast<int32_t*>(ws) : nullptr;
-    p.ws_rec = d.n_chunks > 1 ? reinterpret_cast<float*>(ws + (d.plan ? align256(4 * d.n_units) : 0)) : nullptr;
+    const MlaWorkspace wl = mla_workspace(d, a.num_q_heads);
+    p.order = d.plan && d.n_units > 0 ? reinterpret_cast<int32_t*>(ws + wl.order) : nullptr;
+    p.ws_rec = d.n_chunks > 1 ? reinterpret_cast<float*>(ws + wl.rec) : nullptr;
+    p.ws_redo = d.n_units > 0 ? reinterpret_cast<int32_t*>(ws + wl.redo) : nullptr;
+    p.ws_max = d.n_units > 0 ? reinterpret_cast<float*>(ws + wl.max) : nullptr;
     p.rec_floats = d.rec_floats;
     p.B = a.num_rows;
     p.T = a.num_tokens;
@@ -529,11 +647,22 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     if (blocks > 0) {
         const dim3 grid{uint32_t(blocks), 1, 1};
         switch (d.nw) {
-            case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, grid, dim3(64), 0, stream, p); break;
-            case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, grid, dim3(128), 0, stream, p); break;
-            default: hipLaunchKernelGGL(mla_decode_kernel<4>, grid, dim3(256), 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((mla_decode_kernel<1, false>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((mla_decode_kernel<2, false>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((mla_decode_kernel<4, false>), grid, dim3(256), 0, stream, p); break;
+            default: hipLaunchKernelGGL((mla_decode_kernel<8, false>), grid, dim3(512), 0, stream, p); break;
         }
         if (int32_t st = check_launch("cp_paged_attn_partial (MLA decode)")) return st;
+    }
+    if (d.work_blocks > 0) {                         // workgroups whose scores outgrew their reference, if any
+        const dim3 grid{uint32_t(d.work_blocks), 1, 1};
+        switch (d.nw) {
+            case 1: hipLaunchKernelGGL((mla_decode_kernel<1, true>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((mla_decode_kernel<2, true>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((mla_decode_kernel<4, true>), grid, dim3(256), 0, stream, p); break;
+            default: hipLaunchKernelGGL((mla_decode_kernel<8, true>), grid, dim3(512), 0, stream, p); break;
+        }
+        if (int32_t st = check_launch("cp_paged_attn_partial (MLA redo)")) return st;
     }
     if (d.n_chunks > 1 && d.n_items > 0) {
         hipLaunchKernelGGL(mla_chunk_merge_kernel, dim3(uint32_t(d.n_items * (a.num_q_heads / 2))), dim3(256), 0,

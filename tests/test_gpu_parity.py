@@ -166,6 +166,32 @@ def test_stripe_subset_matches_all_stripes(fixed_splits):
         check_lse(pl[:, :t], fl[:, :t].double().cpu().numpy(), "balanced vs fixed lse")
 
 
+def test_mla_late_score_jump():
+    """A late latent row aligned with one query head scores far above everything in the stripe's first tile. The MLA
+    kernel takes its softmax reference from a unit's first tile, so this case makes it repeat the unit with the exact
+    maximum; the partials must still match the oracle."""
+    wl = workloads.make("mla", batch=2, ctx_lengths=[300, 1000])
+    say("mla late score jump")
+    batch = pool.build_batch(wl, DEV)
+    b, c = 1, 1000
+    rv = workloads.row_values(wl, b, DEV)
+    lat = rv.k_ctx.clone()
+    lat[c - 3, 0] = (6.0 * torch.sign(rv.q[0, 0].float())).to(lat.dtype)   # about +100 in log2 units for head 0
+    slots = pool.logical_slots(batch.block_table[b], c, wl.page_size)
+    api.kv_write(slots, lat, None, batch.k_pool, None, wl.page_size, wl.partners, kind="mla")
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    parts, _ = oracle.row_partials(rv.q.cpu(), lat.cpu(), lat[..., :wl.head_dim_v].cpu(), wl.partners, wl.scale)
+    full = oracle.row_attention(rv.q.cpu(), lat.cpu(), lat[..., :wl.head_dim_v].cpu(), wl.scale)
+    t0 = int(wl.q_row_start[b])
+    for r in range(wl.partners):
+        check_out(res[2][r, t0:t0 + 1], parts[r][0], f"stripe {r} out")
+        check_lse(res[3][r, t0:t0 + 1], parts[r][1], f"stripe {r} lse")
+    check_out(res[0][t0:t0 + 1], full[0], "merged out")
+    check_lse(res[1][t0:t0 + 1], full[1], "merged lse")
+    compare_rows(wl, batch, res, [0], DEV)                # the other row is untouched
+
+
 @pytest.mark.parametrize("fixed_splits", [False, True], ids=["balanced", "fixed"])
 def test_repeat_calls_are_deterministic(fixed_splits):
     """Split items merged from their records give the same bits on every call, with the workspace reused."""
