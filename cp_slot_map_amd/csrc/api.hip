@@ -77,6 +77,7 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
 }
 
 static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
+    if (extend_bf16_eligible(a, geo)) return 0;
     if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes(a);
     if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
     return 0;
@@ -115,6 +116,7 @@ extern "C" int32_t cp_paged_attn_partial(const cp_paged_args* a, hipStream_t str
         return fail(CPATTN_EINVAL, "workspace of %lld bytes needed (got %lld)", (long long)need,
                     (long long)a->workspace_bytes);
     if (a->num_tokens == 0) return CPATTN_OK;
+    if (extend_bf16_eligible(*a, geo)) return launch_paged_extend_bf16(*a, geo, stream);
     if (decode_bf16_eligible(*a, geo)) return launch_paged_decode_bf16(*a, geo, stream);
     if (mla_decode_eligible(*a, geo)) return launch_mla_decode(*a, geo, stream);
     return launch_paged_generic(*a, geo, stream);
@@ -136,5 +138,6 @@ extern "C" int32_t cp_own_token_attn(const cp_own_args* pa, hipStream_t stream) 
     if (a.bucket_tokens == 0) return CPATTN_OK;
     if (!a.cu_seqlens || !a.out || !a.lse) return fail(CPATTN_EINVAL, "null device pointer");
     if (a.num_rows > 0 && (!a.q || !a.k || !a.v)) return fail(CPATTN_EINVAL, "null device pointer");
+    if (own_bf16_eligible(a)) return launch_own_token_bf16(a, stream);
     return launch_own_token_generic(a, stream);
 }

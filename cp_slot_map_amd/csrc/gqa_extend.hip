@@ -1,0 +1,548 @@
+// bf16 GQA attention of many query rows per kv head (head_dim = head_dim_v = 128), built for gfx950 MFMA: the
+// per-stripe partial of rows that bring several tokens in a step (context part), and the causal attention of a row's
+// in-step tokens over one another (own-token part).
+//
+// What it computes. Context part: each query token of a row attends the stripe's prior context positions and the
+// partial is returned with its natural-log lse (mstar PR #1124, "Context / Sequence Parallel 1/5", PR description;
+// every in-step query sees the whole prior context). Own-token part: query i of a row attends the row's in-step keys
+// 0..i, taken from the K/V the layer hands over (same PR; the own-token call in the vLLM compare view
+// "[Core] Add explicit layer parallel plans" passes the query offsets as the key offsets).
+//
+// Work decomposition. A unit is (row b, stripe s, kv head g, block of 256 query rows); query rows of a kv head are
+// (token, head-in-group) pairs, so a block holds 256 / G tokens. One workgroup of eight waves (two per SIMD) runs a
+// unit; wave w owns rows [32w, 32w + 32) as two MFMA row blocks and keeps their query operand (32 VGPRs) and output
+// accumulators (64 VGPRs) in registers. K and V stream through LDS in tiles of 32 tokens (16 KB; four buffers, three
+// tiles in flight), loaded straight from global memory into LDS: each wave issues one K and one V instruction per tile,
+// 64 lanes covering four tokens' 256-byte rows. Every K read and every V read from LDS serves both row blocks of the
+// wave, so the LDS traffic per MFMA is a quarter of what a 16-row wave would need.
+//
+// Per tile and wave (32 rows x 32 tokens):
+//   * scores S^T[token][row] = K . Q^T with v_mfma_f32_16x16x32_bf16 (16 MFMAs): A = K rows from LDS, B = query rows.
+//   * online softmax with a lazily moved running max (moved when a tile maximum exceeds it by more than 8 in log2
+//     units; the scale enters each exponent through one fused multiply-add); keys past the end and, in the own-token
+//     part, keys after the query's own token are masked (only on the tiles that reach them).
+//   * out += P . V with the same MFMA: the score layout is the A-operand layout (k index 8c + e of lane group c is tile
+//     token 16 (e / 4) + 4c + e % 4), the B operand of a 16-dim output tile comes from two transposed LDS reads
+//     (ds_read_b64_tr_b16). P enters as a bf16 pair hi + lo (about 16 significant bits), so a softmax peaked on a few
+//     keys keeps fp32-level accuracy (32 MFMAs).
+//
+// LDS layout of a tile: K rows of 256 bytes at 256 t, V rows at 8192 + 256 t; the sixteen 16-byte pieces of token t
+// are stored XOR f(t) = 2t mod 16. Measured on gfx950, the score reads (sixteen tokens at one piece) and the transposed
+// value reads then run at the full rate of their instruction; without the swizzle they run at an eighth of it.
+#include "launch.h"
+
+#include <type_traits>
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kTile = 32;                       // keys per LDS tile
+constexpr int kRowBytes = kD * 2;               // one token's K (or V) row
+constexpr int kVOff = kTile * kRowBytes;        // V region of a tile
+constexpr int kTileBytes = 2 * kTile * kRowBytes;
+constexpr int kBufs = 4;
+constexpr int kAhead = kBufs - 1;
+constexpr int kNW = 8;                          // waves per workgroup
+constexpr int kRowsPerWave = 32;
+constexpr int kBlockRows = kNW * kRowsPerWave;  // query rows per unit
+constexpr int kMaxPages = 1024;                 // page ids of a stripe staged in LDS
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) char* lds_char_ptr;
+typedef const __attribute__((address_space(3))) int32_t* lds_i32_ptr;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+enum { kFromPool = 0, kFromOwn = 1 };
+
+struct ExtParams {
+    const uint16_t* q;
+    int64_t q_st, q_sh;
+    const uint16_t* kp;            // pool mode: the stripe pools; own mode: the in-step keys and values
+    const uint16_t* vp;
+    PoolGeom geo;                  // pool mode
+    int64_t kv_st, kv_sh;          // own mode: token and head strides of k and v
+    const int32_t* row_start;      // q_row_start (pool mode) or cu_seqlens (own mode)
+    const int32_t* ctx_len;        // pool mode
+    const int32_t* bt;
+    int64_t bt_stride;
+    float* out;
+    int64_t o_ss, o_st, o_sh;
+    float* lse;
+    int64_t l_ss, l_st;
+    int32_t B, T, P, stripe_begin, S, Hq, Hkv, G, max_pages, page_size, max_row_tokens;
+    int32_t n_qblocks, n_units, pad_tokens_per_block;
+    float scale_log2;
+};
+
+__device__ __forceinline__ int swz(int t) { return (2 * t) & 15; }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (those would drain the tiles in flight); the empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scheduling groups: AHEAD LDS reads first, then (one MFMA, R reads) until the N MFMAs of the region are placed.
+template <int N, int R, int AHEAD>
+__device__ __forceinline__ void sched_pipeline() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N - AHEAD / R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD / R, 0);
+}
+
+// Element offset (from the K or V base) of key j's row for kv head g.
+template <int MODE>
+__device__ __forceinline__ int64_t key_row(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
+                                           int32_t j) {
+    if (MODE == kFromPool) {
+        int32_t page = s_pages[j >> p.geo.pp_shift];
+        page = (page >= 0 && page < p.geo.num_pages) ? page : 0;
+        return int64_t(r) * p.geo.s_stripe + int64_t(page) * p.geo.s_page + int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot +
+               int64_t(g) * p.geo.s_head;
+    } else {
+        return int64_t(tok0 + j) * p.kv_st + int64_t(g) * p.kv_sh;
+    }
+}
+
+// Issue the direct-to-LDS loads of one tile: wave w loads tokens 4w .. 4w + 3 of K and of V, lane l filling stored
+// piece l % 16 of token 4w + l / 16 with its logical piece (l % 16) ^ f(t). `rows` holds, in lane L, the element
+// offset of tile token L % 32's row (keys past the end take the last key's row; their values are masked out).
+__device__ __forceinline__ void issue_tile(const uint16_t* kp, const uint16_t* vp, int64_t rows, lds_char_ptr tile,
+                                           int32_t w, int lane) {
+    const int32_t t = 4 * w + (lane >> 4);
+    const int64_t off = (int64_t(uint32_t(__shfl(int32_t(uint64_t(rows) >> 32), t))) << 32) |
+                        uint32_t(__shfl(int32_t(rows), t));
+    const int32_t piece = (lane & 15) ^ swz(t);
+    __builtin_amdgcn_global_load_lds((const void*)(kp + off + 8 * piece), (lds_ptr)(tile + 1024 * w), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vp + off + 8 * piece), (lds_ptr)(tile + kVOff + 1024 * w), 16, 0, 0);
+}
+
+}  // namespace
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
+    // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
+    // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
+    __shared__ __attribute__((aligned(16))) char s_tile0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile2[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_tile3[kTileBytes];
+    __shared__ int32_t s_pages[kMaxPages];
+    const int lane = threadIdx.x & 63;
+    const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t blk = blockIdx.x;
+
+    if (blk >= p.n_units) {                                 // padding-token fill role
+        const int32_t k = blk - p.n_units;
+        const int32_t first = min(max(p.row_start[p.B], 0), p.T);
+        const int32_t t0 = max(k * p.pad_tokens_per_block, first);
+        const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
+        if (t0 < t1)
+            fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, kD, t0, t1, threadIdx.x,
+                         blockDim.x);
+        return;
+    }
+
+    // Unit: block of 256 query rows, kv head, stripe, row (block fastest).
+    int32_t v = blk;
+    const int32_t qb = v % p.n_qblocks;
+    v /= p.n_qblocks;
+    const int32_t g = v % p.Hkv;
+    v /= p.Hkv;
+    const int32_t s = v % p.S;
+    const int32_t b = v / p.S;
+    const const_i32_ptr rs = (const_i32_ptr)p.row_start;
+    const int32_t tok0 = min(max(rs[b], 0), p.T);
+    const int32_t tok1 = min(max(rs[b + 1], tok0), p.T);
+    const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
+    const int32_t nrows = ntok * p.G;
+    const int32_t row0 = qb * kBlockRows;
+    if (row0 >= nrows) return;
+    const int32_t r = p.stripe_begin + s;
+    int32_t nkeys;
+    if (MODE == kFromPool) {
+        const int32_t L = min(max(((const_i32_ptr)p.ctx_len)[b], 0), p.max_pages * p.page_size);
+        nkeys = stripe_length(L, r, p.P);
+    } else {
+        nkeys = min(ntok, (min(row0 + kBlockRows, nrows) - 1) / p.G + 1);   // keys up to the block's last token
+    }
+    const int32_t n16 = lane & 15, c4 = lane >> 4;
+    const int32_t wrow0 = row0 + kRowsPerWave * w;          // first query row of this wave
+    const bool wave_live = wrow0 < nrows;                   // wave-uniform
+
+    if (nkeys == 0) {                                       // no key: (0, -inf) for this wave's rows
+        if (wave_live) {
+            for (int32_t rr = 0; rr < kRowsPerWave; ++rr) {
+                const int32_t rho = wrow0 + rr;
+                if (rho >= nrows) break;
+                const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
+                float* o = p.out + int64_t(s) * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh;
+                for (int32_t d = lane; d < kD; d += 64) o[d] = 0.f;
+                if (lane == 0) p.lse[int64_t(s) * p.l_ss + int64_t(t) * p.l_st + h] = neg_inf();
+            }
+        }
+        return;
+    }
+    const int32_t ntiles = (nkeys + kTile - 1) / kTile;
+    const int32_t last_key = nkeys - 1;
+
+    // Query operand: rows wrow0 + 16 rb + n16, dims [32 ks + 8 c4, +8); rows past the end read zeros.
+    u32x4_t qreg[2][4];
+    int32_t qtok[2];                                        // the row's token within the row (for the causal mask)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int32_t rho = wrow0 + 16 * rb + n16;
+        qtok[rb] = rho / p.G;
+        if (rho < nrows) {
+            const uint16_t* qp = p.q + int64_t(tok0 + rho / p.G) * p.q_st + int64_t(g * p.G + rho % p.G) * p.q_sh + 8 * c4;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qreg[rb][ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qreg[rb][ks] = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+    }
+
+    // The stripe's page ids, staged once in LDS (at most kMaxPages by the eligibility check). The barrier's wait also
+    // retires the query loads above, so nothing but tile loads is outstanding inside the loop.
+    if (MODE == kFromPool) {
+        const int32_t npages = (last_key >> p.geo.pp_shift) + 1;
+        const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
+        for (int32_t i = threadIdx.x; i < npages; i += blockDim.x) s_pages[i] = bt_row[i];
+    }
+    __syncthreads();
+    const lds_i32_ptr pages = (lds_i32_ptr)s_pages;
+
+    // Per-lane LDS byte offsets inside a tile (reads add the buffer address as an immediate):
+    //   score operand: token 16 tb + n16, logical piece 4 ks + c4;
+    //   value operand through transposed reads: in each 16-lane group, lane s supplies four consecutive values of one
+    //   row and lane q receives element q % 4 of rows q / 4, 4 + q / 4, 8 + q / 4, 12 + q / 4. Lane s of group c4
+    //   points at token 16 rr + 4 c4 + s / 4, dims 16 db + 4 (s % 4), so lane q receives dim 16 db + q of tokens
+    //   8 c4 + e in k order: the B operand of dim block db.
+    int32_t kofs[2][4], vofs[2][8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int32_t t = 16 * tb + n16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kofs[tb][ks] = kRowBytes * t + 16 * ((4 * ks + c4) ^ swz(t));
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int32_t t = 16 * rr + 4 * c4 + (n16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            vofs[rr][db] = kVOff + kRowBytes * t + 16 * ((2 * db + ((n16 >> 1) & 1)) ^ swz(t)) + 8 * (n16 & 1);
+    }
+
+    auto tile_buf = [&](auto bc) __attribute__((always_inline)) -> lds_char_ptr {
+        constexpr int bb = decltype(bc)::value % kBufs;
+        return bb == 0 ? (lds_char_ptr)s_tile0 : bb == 1 ? (lds_char_ptr)s_tile1 : bb == 2 ? (lds_char_ptr)s_tile2
+                                                                                     : (lds_char_ptr)s_tile3;
+    };
+    auto rows_of = [&](int32_t tile0) __attribute__((always_inline)) {
+        return key_row<MODE>(p, pages, r, g, tok0, min(tile0 + (lane & 31), last_key));
+    };
+
+    f32x4_t o[2][8];                                        // o[rb][db][i]: row 16 rb + 4 c4 + i, dim 16 db + n16
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[rb][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float m[2] = {neg_inf(), neg_inf()}, l[2] = {0.f, 0.f};
+
+    // kAhead tiles in flight before the loop; every iteration issues one more (tile indices past the end re-read the
+    // last tile into a buffer nobody reads), so the wait at the top of an iteration leaves exactly the kAhead - 1
+    // newest tiles' loads (two instructions each) outstanding.
+    issue_tile(p.kp, p.vp, rows_of(0), tile_buf(std::integral_constant<int, 0>{}), w, lane);
+    issue_tile(p.kp, p.vp, rows_of(min(kTile, (ntiles - 1) * kTile)), tile_buf(std::integral_constant<int, 1>{}), w, lane);
+    issue_tile(p.kp, p.vp, rows_of(min(2 * kTile, (ntiles - 1) * kTile)), tile_buf(std::integral_constant<int, 2>{}), w,
+               lane);
+    static_assert(kAhead == 3 && kBufs == 4, "ring");
+
+    auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
+        const int32_t tile0 = kt * kTile;
+        // Masking is needed on the last tile and, for the own-token part, on tiles reaching past this wave's first
+        // query token (wave-uniform conditions).
+        const bool mask = tile0 + kTile > nkeys || (MODE == kFromOwn && tile0 + kTile - 1 > wrow0 / p.G);
+
+        // Scores S^T[key 16 tb + 4 c4 + i][row 16 rb + n16].
+        f32x4_t sacc[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) sacc[rb][tb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const u32x4_t kv = *(const __attribute__((address_space(3))) u32x4_t*)(tile + kofs[tb][ks]);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    sacc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qreg[rb][ks]),
+                                                                           sacc[rb][tb], 0, 0, 0);
+            }
+        }
+        sched_pipeline<16, 1, 4>();
+
+        // Softmax in raw score units: m is the running max of raw scores and p = 2^((s - m) * scale_log2), one fused
+        // multiply-add per score (scale_log2 > 0 keeps the order of the scores).
+        const float c = p.scale_log2;
+        u32x4_t phi[2], plo[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[rb][e >> 2][e & 3];
+            if (mask) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int32_t j = tile0 + 16 * (e >> 2) + 4 * c4 + (e & 3);
+                    if (j >= nkeys || (MODE == kFromOwn && j > qtok[rb])) sv[e] = neg_inf();
+                }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // The running max moves only when a tile maximum exceeds it by more than 8 (log2 units), so after the
+            // first tiles the rescale is rare and kept out of the common path.
+            if (__builtin_expect(__any((mx - m[rb]) * c > 8.0f), 0)) {
+                const float m_new = fmaxf(m[rb], mx);
+                const float alpha = m_new == neg_inf() ? 1.0f : exp2f((m[rb] - m_new) * c);   // 0 on the first tile
+                l[rb] *= alpha;
+                m[rb] = m_new;
+                float a_o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a_o[i] = __shfl(alpha, 4 * c4 + i);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[rb][db][i] *= a_o[i];
+            }
+            const float mc = -m[rb] * c;
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, mc));
+            l[rb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+            // P as a bf16 pair: hi = bf16(p), lo = bf16(p - hi).
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t hw = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
+                phi[rb][d] = hw;
+                plo[rb][d] = pack2_bf16(pv[2 * d] - __uint_as_float(hw << 16), pv[2 * d + 1] - __uint_as_float(hw & 0xffff0000u));
+            }
+        }
+
+        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads.
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[1][db]));
+            const bf16x8_t bop =
+                __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop, o[rb][db], 0, 0, 0);
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop, o[rb][db], 0, 0, 0);
+            }
+        }
+        sched_pipeline<32, 2, 8>();
+    };
+
+    // One iteration with buffer bb (compile time): wait for tile kt, issue the loads of tile kt + kAhead into buffer
+    // bb + kAhead, compute tile kt from buffer bb.
+    // Waves past the last query row still load their share of every tile; they run the same loop (same barriers)
+    // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
+    auto step = [&](auto bc, auto live, int32_t kt) __attribute__((always_inline)) {
+        constexpr int bb = decltype(bc)::value;
+        wait_vmcnt<(kAhead - 1) * 2>();                     // this wave's pieces of tile kt are in LDS
+        lds_barrier();                                      // ... and every wave's; tile kt - 1's buffer is free
+        issue_tile(p.kp, p.vp, rows_of(min((kt + kAhead) * kTile, (ntiles - 1) * kTile)),
+                   tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
+        if constexpr (decltype(live)::value) tile_compute(tile_buf(std::integral_constant<int, bb>{}), kt);
+    };
+    auto run = [&](auto live) __attribute__((always_inline)) {
+        for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
+            step(std::integral_constant<int, 0>{}, live, kt);
+            if (kt + 1 >= ntiles) break;
+            step(std::integral_constant<int, 1>{}, live, kt + 1);
+            if (kt + 2 >= ntiles) break;
+            step(std::integral_constant<int, 2>{}, live, kt + 2);
+            if (kt + 3 >= ntiles) break;
+            step(std::integral_constant<int, 3>{}, live, kt + 3);
+        }
+    };
+    if (wave_live)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+    wait_vmcnt<0>();                                        // the over-issued tail loads land before the waves retire
+    if (!wave_live) return;
+
+    // Epilogue: row sums over the four lane groups, then the normalised rows and their lse.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float ls = l[rb];
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t rho = wrow0 + 16 * rb + 4 * c4 + i;
+            const float li = __shfl(ls, 4 * c4 + i);
+            if (rho < nrows) {
+                const float inv = li > 0.f ? 1.0f / li : 0.f;
+                const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
+                float* dst = p.out + int64_t(s) * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + n16;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) dst[16 * db] = o[rb][db][i] * inv;
+            }
+        }
+        const int32_t rho = wrow0 + 16 * rb + n16;
+        if (c4 == 0 && rho < nrows) {
+            const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
+            p.lse[int64_t(s) * p.l_ss + int64_t(t) * p.l_st + h] =
+                ls > 0.f ? (m[rb] * p.scale_log2 + log2f(ls)) * kLn2 : neg_inf();
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------ host
+namespace {
+
+bool al16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
+    const int64_t rows = int64_t(std::max(1, p.max_row_tokens)) * p.G;
+    p.n_qblocks = int32_t((rows + kBlockRows - 1) / kBlockRows);
+    const int64_t units = int64_t(p.B) * p.S * p.Hkv * p.n_qblocks;
+    p.n_units = int32_t(units);
+    p.pad_tokens_per_block = 4;
+    const int64_t blocks = units + (p.T + 3) / 4;
+    if (blocks == 0) return CPATTN_OK;
+    const dim3 grid{uint32_t(blocks), 1, 1};
+    if (mode == kFromPool)
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool>), grid, dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn>), grid, dim3(512), 0, stream, p);
+    return check_launch(mode == kFromPool ? "cp_paged_attn_partial (bf16 extend)" : "cp_own_token_attn (bf16)");
+}
+
+}  // namespace
+
+bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
+    if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kD) return false;
+    const int32_t G = a.num_q_heads / a.num_kv_heads;
+    if (kBlockRows % G != 0) return false;
+    if (int64_t(a.max_row_tokens) * G <= 16) return false;   // decode-shaped: the decode kernel serves it
+    if (geo.pp_shift < 0) return false;
+    const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
+    if ((max_lr + geo.pp - 1) / geo.pp > kMaxPages) return false;
+    if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool)) return false;
+    if ((a.q_stride_token | a.q_stride_head | a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot |
+         a.kv_stride_head) & 7)
+        return false;
+    if (int64_t(a.num_rows) * a.stripe_count * a.num_kv_heads * ((int64_t(a.max_row_tokens) * G + kBlockRows - 1) /
+                                                                  kBlockRows) + (a.num_tokens + 3) / 4 >
+        (int64_t(1) << 31) - 1)
+        return false;
+    return true;
+}
+
+int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
+    ExtParams p{};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.q_st = a.q_stride_token;
+    p.q_sh = a.q_stride_head;
+    p.kp = static_cast<const uint16_t*>(a.k_pool);
+    p.vp = static_cast<const uint16_t*>(a.v_pool);
+    p.geo = geo;
+    p.row_start = a.q_row_start;
+    p.ctx_len = a.ctx_len;
+    p.bt = a.block_table;
+    p.bt_stride = a.bt_stride;
+    p.out = a.out;
+    p.o_ss = a.out_stride_stripe;
+    p.o_st = a.out_stride_token;
+    p.o_sh = a.out_stride_head;
+    p.lse = a.lse;
+    p.l_ss = a.lse_stride_stripe;
+    p.l_st = a.lse_stride_token;
+    p.B = a.num_rows;
+    p.T = a.num_tokens;
+    p.P = a.num_partners;
+    p.stripe_begin = a.stripe_begin;
+    p.S = a.stripe_count;
+    p.Hq = a.num_q_heads;
+    p.Hkv = a.num_kv_heads;
+    p.G = a.num_q_heads / a.num_kv_heads;
+    p.max_pages = a.max_pages;
+    p.page_size = a.page_size;
+    p.max_row_tokens = a.max_row_tokens;
+    p.scale_log2 = a.scale * kLog2e;
+    return launch_extend(p, kFromPool, stream);
+}
+
+bool own_bf16_eligible(const cp_own_args& a) {
+    if (a.dtype != CPATTN_BF16 || a.head_dim != kD) return false;
+    const int32_t G = a.num_q_heads / a.num_kv_heads;
+    if (kBlockRows % G != 0) return false;
+    if (!al16(a.q) || !al16(a.k) || !al16(a.v)) return false;
+    if ((a.q_stride_token | a.q_stride_head | a.kv_stride_token | a.kv_stride_head) & 7) return false;
+    if (int64_t(a.num_rows) * a.num_kv_heads * ((int64_t(std::max(1, a.max_row_tokens)) * G + kBlockRows - 1) /
+                                                 kBlockRows) + (a.bucket_tokens + 3) / 4 >
+        (int64_t(1) << 31) - 1)
+        return false;
+    return true;
+}
+
+int32_t launch_own_token_bf16(const cp_own_args& a, hipStream_t stream) {
+    ExtParams p{};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.q_st = a.q_stride_token;
+    p.q_sh = a.q_stride_head;
+    p.kp = static_cast<const uint16_t*>(a.k);
+    p.vp = static_cast<const uint16_t*>(a.v);
+    p.kv_st = a.kv_stride_token;
+    p.kv_sh = a.kv_stride_head;
+    p.row_start = a.cu_seqlens;
+    p.out = a.out;
+    p.o_ss = 0;
+    p.o_st = a.out_stride_token;
+    p.o_sh = a.out_stride_head;
+    p.lse = a.lse;
+    p.l_ss = 0;
+    p.l_st = a.lse_stride_token;
+    p.B = a.num_rows;
+    p.T = a.bucket_tokens;
+    p.P = 1;
+    p.S = 1;
+    p.Hq = a.num_q_heads;
+    p.Hkv = a.num_kv_heads;
+    p.G = a.num_q_heads / a.num_kv_heads;
+    p.max_pages = 0;
+    p.page_size = 1;
+    p.max_row_tokens = a.max_row_tokens;
+    p.scale_log2 = a.scale * kLog2e;
+    return launch_extend(p, kFromOwn, stream);
+}
+
+}  // namespace cpattn

@@ -15,6 +15,13 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
 
+// Specialised bf16 GQA partial for rows that bring many query tokens (head_dim = head_dim_v = 128): 256 query rows per
+// workgroup, K/V tiles staged in LDS, MFMA score and value products. The same kernel serves the own-token part.
+bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
+int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+bool own_bf16_eligible(const cp_own_args& a);
+int32_t launch_own_token_bf16(const cp_own_args& a, hipStream_t stream);
+
 // Specialised bf16 MLA partial (one latent head of 576, values its first 512; 16, 32, 64 or 128 query heads) with MFMA
 // score and value products over latent tiles staged in LDS.
 bool mla_decode_eligible(const cp_paged_args& a, const PoolGeom& geo);
