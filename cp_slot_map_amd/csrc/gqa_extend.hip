@@ -8,19 +8,21 @@
 // 0..i, taken from the K/V the layer hands over (same PR; the own-token call in the vLLM compare view
 // "[Core] Add explicit layer parallel plans" passes the query offsets as the key offsets).
 //
-// Work decomposition. A unit is (row b, stripe s, kv head g, block of 256 query rows); query rows of a kv head are
-// (token, head-in-group) pairs, so a block holds 256 / G tokens. One workgroup of eight waves (two per SIMD) runs a
-// unit; wave w owns rows [32w, 32w + 32) as two MFMA row blocks and keeps their query operand (32 VGPRs) and output
-// accumulators (64 VGPRs) in registers. K and V stream through LDS in tiles of 32 tokens (16 KB; four buffers, three
-// tiles in flight), loaded straight from global memory into LDS: each wave issues one K and one V instruction per tile,
-// 64 lanes covering four tokens' 256-byte rows. Every K read and every V read from LDS serves both row blocks of the
+// Work decomposition. A unit is (row b, stripe s, kv head g, block of 128 query rows); query rows of a kv head are
+// (token, head-in-group) pairs, so a block holds 128 / G tokens. One workgroup of four waves (one per SIMD) runs a
+// unit and two workgroups share a CU, so that one workgroup's softmax overlaps the other's matrix products; wave w
+// owns rows [32w, 32w + 32) as two MFMA row blocks and keeps their query operand (32 VGPRs) and output accumulators
+// (64 VGPRs) in registers. K and V stream through LDS in tiles of 32 tokens (16 KB; four buffers, three tiles in
+// flight), loaded straight from global memory into LDS: each wave issues two K and two V instructions per tile, 64
+// lanes covering four tokens' 256-byte rows. Every K read and every V read from LDS serves both row blocks of the
 // wave, so the LDS traffic per MFMA is a quarter of what a 16-row wave would need.
 //
 // Per tile and wave (32 rows x 32 tokens):
 //   * scores S^T[token][row] = K . Q^T with v_mfma_f32_16x16x32_bf16 (16 MFMAs): A = K rows from LDS, B = query rows.
 //   * online softmax with a lazily moved running max (moved when a tile maximum exceeds it by more than 8 in log2
-//     units; the scale enters each exponent through one fused multiply-add); keys past the end and, in the own-token
-//     part, keys after the query's own token are masked (only on the tiles that reach them).
+//     units; the scale enters each exponent through one fused multiply-add; row maxima and sums over the four lane
+//     groups use the gfx950 lane swaps); keys past the end and, in the own-token part, keys after the query's own
+//     token are masked (only on the tiles that reach them).
 //   * out += P . V with the same MFMA: the score layout is the A-operand layout (k index 8c + e of lane group c is tile
 //     token 16 (e / 4) + 4c + e % 4), the B operand of a 16-dim output tile comes from two transposed LDS reads
 //     (ds_read_b64_tr_b16). P enters as a bf16 pair hi + lo (about 16 significant bits), so a softmax peaked on a few
@@ -44,10 +46,12 @@ constexpr int kVOff = kTile * kRowBytes;        // V region of a tile
 constexpr int kTileBytes = 2 * kTile * kRowBytes;
 constexpr int kBufs = 4;
 constexpr int kAhead = kBufs - 1;
-constexpr int kNW = 8;                          // waves per workgroup
+constexpr int kNW = 4;                          // waves per workgroup (two workgroups per CU)
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockRows = kNW * kRowsPerWave;  // query rows per unit
-constexpr int kMaxPages = 1024;                 // page ids of a stripe staged in LDS
+constexpr int kMaxPages = 2048;                 // page ids of a stripe staged in LDS
+constexpr int kTokPerWave = kTile / kNW;        // tokens of a tile each wave loads
+constexpr int kLoadsPerTile = 2 * (kTokPerWave / 4);   // direct-to-LDS instructions per wave and tile (K and V)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) char* lds_char_ptr;
@@ -123,23 +127,43 @@ __device__ __forceinline__ int64_t key_row(const ExtParams& p, lds_i32_ptr s_pag
     }
 }
 
-// Issue the direct-to-LDS loads of one tile: wave w loads tokens 4w .. 4w + 3 of K and of V, lane l filling stored
-// piece l % 16 of token 4w + l / 16 with its logical piece (l % 16) ^ f(t). `rows` holds, in lane L, the element
-// offset of tile token L % 32's row (keys past the end take the last key's row; their values are masked out).
-__device__ __forceinline__ void issue_tile(const uint16_t* kp, const uint16_t* vp, int64_t rows, lds_char_ptr tile,
-                                           int32_t w, int lane) {
-    const int32_t t = 4 * w + (lane >> 4);
-    const int64_t off = (int64_t(uint32_t(__shfl(int32_t(uint64_t(rows) >> 32), t))) << 32) |
-                        uint32_t(__shfl(int32_t(rows), t));
-    const int32_t piece = (lane & 15) ^ swz(t);
-    __builtin_amdgcn_global_load_lds((const void*)(kp + off + 8 * piece), (lds_ptr)(tile + 1024 * w), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vp + off + 8 * piece), (lds_ptr)(tile + kVOff + 1024 * w), 16, 0, 0);
+// Issue the direct-to-LDS loads of one tile: wave w loads tokens [kTokPerWave w, kTokPerWave (w + 1)) of K and of V,
+// four tokens (64 lanes x 16 bytes) an instruction; lane l fills stored piece l % 16 of its token with logical piece
+// (l % 16) ^ f(t). Keys past the end take the last key's row (their scores are masked out).
+template <int MODE>
+__device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
+                                           int32_t tile0, int32_t last_key, lds_char_ptr tile, int32_t w, int lane) {
+#pragma unroll
+    for (int i = 0; i < kTokPerWave / 4; ++i) {
+        const int32_t t = kTokPerWave * w + 4 * i + (lane >> 4);
+        const int64_t off = key_row<MODE>(p, s_pages, r, g, tok0, min(tile0 + t, last_key)) + 8 * ((lane & 15) ^ swz(t));
+        const int32_t dst = kRowBytes * (kTokPerWave * w + 4 * i);
+        __builtin_amdgcn_global_load_lds((const void*)(p.kp + off), (lds_ptr)(tile + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(p.vp + off), (lds_ptr)(tile + kVOff + dst), 16, 0, 0);
+    }
+}
+
+// Reductions over the four 16-lane groups (lanes n, n + 16, n + 32, n + 48) through the gfx950 lane swaps, which stay
+// in the vector unit: swapping a register with itself by 32 lanes pairs each lane with its partner in the other half,
+// and by 16 lanes within each half.
+__device__ __forceinline__ float group_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
+__global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams p) {
     // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
     // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
     __shared__ __attribute__((aligned(16))) char s_tile0[kTileBytes];
@@ -162,12 +186,15 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
         return;
     }
 
-    // Unit: block of 256 query rows, kv head, stripe, row (block fastest).
+    // Unit order: kv head fastest, then query block, stripe, row. The hardware hands block i to XCD i mod 8, so with
+    // 8 kv heads (or a multiple) every XCD gets one head of every (row, stripe, block): equal work per XCD whatever
+    // the mix of row lengths, and the query blocks of one (row, stripe, kv head), which read the same K/V tiles, run
+    // on one XCD close together in time and share its L2.
     int32_t v = blk;
-    const int32_t qb = v % p.n_qblocks;
-    v /= p.n_qblocks;
     const int32_t g = v % p.Hkv;
     v /= p.Hkv;
+    const int32_t qb = v % p.n_qblocks;
+    v /= p.n_qblocks;
     const int32_t s = v % p.S;
     const int32_t b = v / p.S;
     const const_i32_ptr rs = (const_i32_ptr)p.row_start;
@@ -258,10 +285,6 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
         return bb == 0 ? (lds_char_ptr)s_tile0 : bb == 1 ? (lds_char_ptr)s_tile1 : bb == 2 ? (lds_char_ptr)s_tile2
                                                                                      : (lds_char_ptr)s_tile3;
     };
-    auto rows_of = [&](int32_t tile0) __attribute__((always_inline)) {
-        return key_row<MODE>(p, pages, r, g, tok0, min(tile0 + (lane & 31), last_key));
-    };
-
     f32x4_t o[2][8];                                        // o[rb][db][i]: row 16 rb + 4 c4 + i, dim 16 db + n16
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -272,10 +295,11 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
     // kAhead tiles in flight before the loop; every iteration issues one more (tile indices past the end re-read the
     // last tile into a buffer nobody reads), so the wait at the top of an iteration leaves exactly the kAhead - 1
     // newest tiles' loads (two instructions each) outstanding.
-    issue_tile(p.kp, p.vp, rows_of(0), tile_buf(std::integral_constant<int, 0>{}), w, lane);
-    issue_tile(p.kp, p.vp, rows_of(min(kTile, (ntiles - 1) * kTile)), tile_buf(std::integral_constant<int, 1>{}), w, lane);
-    issue_tile(p.kp, p.vp, rows_of(min(2 * kTile, (ntiles - 1) * kTile)), tile_buf(std::integral_constant<int, 2>{}), w,
-               lane);
+    issue_tile<MODE>(p, pages, r, g, tok0, 0, last_key, tile_buf(std::integral_constant<int, 0>{}), w, lane);
+    issue_tile<MODE>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
+                     tile_buf(std::integral_constant<int, 1>{}), w, lane);
+    issue_tile<MODE>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
+                     tile_buf(std::integral_constant<int, 2>{}), w, lane);
     static_assert(kAhead == 3 && kBufs == 4, "ring");
 
     auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
@@ -321,8 +345,7 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
             }
             float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                              fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = group_max(mx);
             // The running max moves only when a tile maximum exceeds it by more than 8 (log2 units), so after the
             // first tiles the rescale is rare and kept out of the common path.
             if (__builtin_expect(__any((mx - m[rb]) * c > 8.0f), 0)) {
@@ -352,20 +375,24 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
             }
         }
 
-        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads.
+        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads. The hi products
+        // of all sixteen accumulators go first and the lo products after them, so no MFMA waits on the one before.
+        bf16x8_t bop[8];
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[1][db]));
-            const bf16x8_t bop =
-                __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            bop[db] = __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop, o[rb][db], 0, 0, 0);
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop, o[rb][db], 0, 0, 0);
-            }
+            for (int rb = 0; rb < 2; ++rb)
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop[db], o[rb][db], 0, 0, 0);
         }
-        sched_pipeline<32, 2, 8>();
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop[db], o[rb][db], 0, 0, 0);
+        sched_pipeline<16, 2, 4>();
     };
 
     // One iteration with buffer bb (compile time): wait for tile kt, issue the loads of tile kt + kAhead into buffer
@@ -374,10 +401,10 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
     // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
     auto step = [&](auto bc, auto live, int32_t kt) __attribute__((always_inline)) {
         constexpr int bb = decltype(bc)::value;
-        wait_vmcnt<(kAhead - 1) * 2>();                     // this wave's pieces of tile kt are in LDS
+        wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile kt are in LDS
         lds_barrier();                                      // ... and every wave's; tile kt - 1's buffer is free
-        issue_tile(p.kp, p.vp, rows_of(min((kt + kAhead) * kTile, (ntiles - 1) * kTile)),
-                   tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
+        issue_tile<MODE>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
+                         tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
         if constexpr (decltype(live)::value) tile_compute(tile_buf(std::integral_constant<int, bb>{}), kt);
     };
     auto run = [&](auto live) __attribute__((always_inline)) {
@@ -402,8 +429,7 @@ __global__ __launch_bounds__(512, 1) void gqa_extend_kernel(const ExtParams p) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         float ls = l[rb];
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
+        ls = group_sum(ls);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int32_t rho = wrow0 + 16 * rb + 4 * c4 + i;
@@ -440,9 +466,9 @@ int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
     if (mode == kFromPool)
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool>), grid, dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool>), grid, dim3(64 * kNW), 0, stream, p);
     else
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn>), grid, dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn>), grid, dim3(64 * kNW), 0, stream, p);
     return check_launch(mode == kFromPool ? "cp_paged_attn_partial (bf16 extend)" : "cp_own_token_attn (bf16)");
 }
 

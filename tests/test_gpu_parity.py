@@ -204,6 +204,20 @@ def test_repeat_calls_are_deterministic(fixed_splits):
         assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
 
 
+@pytest.mark.parametrize("ctx_lengths", [[32768, 30001, 20000], [32769, 64, 5000]], ids=["at_limit", "past_limit"])
+def test_extend_rows_at_page_staging_limit(ctx_lengths):
+    """Multi-token rows whose stripes hold 2048 pages (the most the bf16 extend kernel stages in LDS), and a batch one
+    token past that (served by the generic kernel)."""
+    wl = workloads.make("mixed", batch=3, new_lengths=[3, 40, 150], ctx_lengths=ctx_lengths, pad_rows=1)
+    say(f"extend at page limit: ctx={list(wl.ctx_len)} new={list(wl.new_len)}")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV, check_partials=True)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
 def test_empty_batch_and_empty_context():
     wl = workloads.make("llama8b", batch=3, ctx_lengths=[0, 0, 2])
     batch = pool.build_batch(wl, DEV)
