@@ -143,14 +143,22 @@ __device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pag
     }
 }
 
+// Maximum of three floats in one instruction. fmaxf would first quiet each operand (IEEE mode), one extra instruction
+// per operand; scores and their maxima are never signalling NaNs, so that step is not needed here.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Reductions over the four 16-lane groups (lanes n, n + 16, n + 32, n + 48) through the gfx950 lane swaps, which stay
 // in the vector unit: swapping a register with itself by 32 lanes pairs each lane with its partner in the other half,
 // and by 16 lanes within each half.
 __device__ __forceinline__ float group_max(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max3(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max3(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float group_sum(float x) {
@@ -286,30 +294,48 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
                                                                                      : (lds_char_ptr)s_tile3;
     };
     f32x4_t o[2][8];                                        // o[rb][db][i]: row 16 rb + 4 c4 + i, dim 16 db + n16
+    // m: softmax reference of each row in raw score units (p = 2^((s - m) * scale_log2)); l: the rows' sums of p.
+    float m[2], l[2];
+    auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[rb][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float m[2] = {neg_inf(), neg_inf()}, l[2] = {0.f, 0.f};
+            for (int db = 0; db < 8; ++db) o[rb][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            m[rb] = neg_inf();
+            l[rb] = 0.f;
+        }
+    };
 
     // kAhead tiles in flight before the loop; every iteration issues one more (tile indices past the end re-read the
     // last tile into a buffer nobody reads), so the wait at the top of an iteration leaves exactly the kAhead - 1
-    // newest tiles' loads (two instructions each) outstanding.
-    issue_tile<MODE>(p, pages, r, g, tok0, 0, last_key, tile_buf(std::integral_constant<int, 0>{}), w, lane);
-    issue_tile<MODE>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
-                     tile_buf(std::integral_constant<int, 1>{}), w, lane);
-    issue_tile<MODE>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
-                     tile_buf(std::integral_constant<int, 2>{}), w, lane);
+    // newest tiles' loads (kLoadsPerTile instructions each) outstanding.
+    //
+    // The prologue's loads take their LDS address through an opaque copy of the buffer pointer. The compiler's
+    // wait-count pass then does not track them against the buffer arrays; tracked, their state merged into the loop
+    // header's and made it wait for every load in flight there (a full drain every fourth tile). The explicit wait
+    // and barrier at the top of each step order these loads before the reads of their tiles all the same.
+    auto opaque = [](lds_char_ptr t) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    auto prologue = [&]() __attribute__((always_inline)) {
+        issue_tile<MODE>(p, pages, r, g, tok0, 0, last_key, opaque(tile_buf(std::integral_constant<int, 0>{})), w,
+                         lane);
+        issue_tile<MODE>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
+                         opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
+        issue_tile<MODE>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
+                         opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
+    };
     static_assert(kAhead == 3 && kBufs == 4, "ring");
 
-    auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
+    // Raw scores of tile kt for this wave's rows, sv[rb][e] = S[row 16 rb + n16][key 16 (e / 4) + 4 c4 + e % 4], with
+    // keys past the end and (own-token part) keys after the row's token set to -inf.
+    auto tile_scores = [&](lds_char_ptr tile, int32_t kt, float (&sv)[2][8]) __attribute__((always_inline)) {
         const int32_t tile0 = kt * kTile;
         // Masking is needed on the last tile and, for the own-token part, on tiles reaching past this wave's first
         // query token (wave-uniform conditions).
         const bool mask = tile0 + kTile > nkeys || (MODE == kFromOwn && tile0 + kTile - 1 > wrow0 / p.G);
-
-        // Scores S^T[key 16 tb + 4 c4 + i][row 16 rb + n16].
-        f32x4_t sacc[2][2];
+        f32x4_t sacc[2][2];                                 // S^T[key 16 tb + 4 c4 + i][row 16 rb + n16]
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -326,47 +352,38 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
             }
         }
         sched_pipeline<16, 1, 4>();
-
-        // Softmax in raw score units: m is the running max of raw scores and p = 2^((s - m) * scale_log2), one fused
-        // multiply-add per score (scale_log2 > 0 keeps the order of the scores).
-        const float c = p.scale_log2;
-        u32x4_t phi[2], plo[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            float sv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sv[e] = sacc[rb][e >> 2][e & 3];
+            for (int e = 0; e < 8; ++e) sv[rb][e] = sacc[rb][e >> 2][e & 3];
             if (mask) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int32_t j = tile0 + 16 * (e >> 2) + 4 * c4 + (e & 3);
-                    if (j >= nkeys || (MODE == kFromOwn && j > qtok[rb])) sv[e] = neg_inf();
+                    if (j >= nkeys || (MODE == kFromOwn && j > qtok[rb])) sv[rb][e] = neg_inf();
                 }
             }
-            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            mx = group_max(mx);
-            // The running max moves only when a tile maximum exceeds it by more than 8 (log2 units), so after the
-            // first tiles the rescale is rare and kept out of the common path.
-            if (__builtin_expect(__any((mx - m[rb]) * c > 8.0f), 0)) {
-                const float m_new = fmaxf(m[rb], mx);
-                const float alpha = m_new == neg_inf() ? 1.0f : exp2f((m[rb] - m_new) * c);   // 0 on the first tile
-                l[rb] *= alpha;
-                m[rb] = m_new;
-                float a_o[4];
+        }
+    };
+    auto row_max = [&](const float (&sv)[8]) __attribute__((always_inline)) {
+        return group_max(max3(max3(sv[0], sv[1], sv[2]), max3(sv[3], sv[4], sv[5]), max3(sv[6], sv[7], sv[7])));
+    };
+
+    // One tile: scores, probabilities relative to the row references m, out += P . V.
+    auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
+        float sv[2][8];
+        tile_scores(tile, kt, sv);
+        const float c = p.scale_log2;
+        // p = 2^((s - m) * scale_log2): one fused multiply-add per score (the launch requires scale_log2 > 0, which
+        // keeps the order of the scores); P as a bf16 pair hi = bf16(p), lo = bf16(p - hi).
+        u32x4_t phi[2], plo[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a_o[i] = __shfl(alpha, 4 * c4 + i);
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[rb][db][i] *= a_o[i];
-            }
+        for (int rb = 0; rb < 2; ++rb) {
             const float mc = -m[rb] * c;
             float pv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, mc));
+            for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][e], c, mc));
             l[rb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-            // P as a bf16 pair: hi = bf16(p), lo = bf16(p - hi).
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t hw = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
@@ -375,79 +392,119 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
             }
         }
 
-        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads. The hi products
-        // of all sixteen accumulators go first and the lo products after them, so no MFMA waits on the one before.
-        bf16x8_t bop[8];
+        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads. The lo product
+        // follows the hi product into the same accumulator; the matrix core forwards the accumulator between them.
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[1][db]));
-            bop[db] = __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8_t bop =
+                __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop[db], o[rb][db], 0, 0, 0);
+            for (int rb = 0; rb < 2; ++rb) {
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop, o[rb][db], 0, 0, 0);
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop, o[rb][db], 0, 0, 0);
+            }
         }
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop[db], o[rb][db], 0, 0, 0);
-        sched_pipeline<16, 2, 4>();
+        sched_pipeline<32, 2, 8>();
     };
 
     // One iteration with buffer bb (compile time): wait for tile kt, issue the loads of tile kt + kAhead into buffer
     // bb + kAhead, compute tile kt from buffer bb.
     // Waves past the last query row still load their share of every tile; they run the same loop (same barriers)
     // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
-    auto step = [&](auto bc, auto live, int32_t kt) __attribute__((always_inline)) {
+    auto step = [&](auto bc, auto live, auto maxonly, int32_t kt) __attribute__((always_inline)) {
         constexpr int bb = decltype(bc)::value;
         wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile kt are in LDS
         lds_barrier();                                      // ... and every wave's; tile kt - 1's buffer is free
         issue_tile<MODE>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
                          tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
-        if constexpr (decltype(live)::value) tile_compute(tile_buf(std::integral_constant<int, bb>{}), kt);
-    };
-    auto run = [&](auto live) __attribute__((always_inline)) {
-        for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
-            step(std::integral_constant<int, 0>{}, live, kt);
-            if (kt + 1 >= ntiles) break;
-            step(std::integral_constant<int, 1>{}, live, kt + 1);
-            if (kt + 2 >= ntiles) break;
-            step(std::integral_constant<int, 2>{}, live, kt + 2);
-            if (kt + 3 >= ntiles) break;
-            step(std::integral_constant<int, 3>{}, live, kt + 3);
-        }
-    };
-    if (wave_live)
-        run(std::true_type{});
-    else
-        run(std::false_type{});
-    wait_vmcnt<0>();                                        // the over-issued tail loads land before the waves retire
-    if (!wave_live) return;
-
-    // Epilogue: row sums over the four lane groups, then the normalised rows and their lse.
+        if constexpr (decltype(live)::value) {
+            if constexpr (decltype(maxonly)::value) {
+                float sv[2][8];
+                tile_scores(tile_buf(std::integral_constant<int, bb>{}), kt, sv);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        float ls = l[rb];
-        ls = group_sum(ls);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int32_t rho = wrow0 + 16 * rb + 4 * c4 + i;
-            const float li = __shfl(ls, 4 * c4 + i);
-            if (rho < nrows) {
-                const float inv = li > 0.f ? 1.0f / li : 0.f;
-                const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
-                float* dst = p.out + int64_t(s) * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + n16;
-#pragma unroll
-                for (int db = 0; db < 8; ++db) dst[16 * db] = o[rb][db][i] * inv;
+                for (int rb = 0; rb < 2; ++rb) m[rb] = fmaxf(m[rb], row_max(sv[rb]));
+            } else {
+                tile_compute(tile_buf(std::integral_constant<int, bb>{}), kt);
             }
         }
-        const int32_t rho = wrow0 + 16 * rb + n16;
-        if (c4 == 0 && rho < nrows) {
-            const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
-            p.lse[int64_t(s) * p.l_ss + int64_t(t) * p.l_st + h] =
-                ls > 0.f ? (m[rb] * p.scale_log2 + log2f(ls)) * kLn2 : neg_inf();
+    };
+    auto run = [&](auto live, auto maxonly) __attribute__((always_inline)) {
+        for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
+            step(std::integral_constant<int, 0>{}, live, maxonly, kt);
+            if (kt + 1 >= ntiles) break;
+            step(std::integral_constant<int, 1>{}, live, maxonly, kt + 1);
+            if (kt + 2 >= ntiles) break;
+            step(std::integral_constant<int, 2>{}, live, maxonly, kt + 2);
+            if (kt + 3 >= ntiles) break;
+            step(std::integral_constant<int, 3>{}, live, maxonly, kt + 3);
         }
+        wait_vmcnt<0>();                                    // the over-issued tail loads land
+    };
+
+    // Epilogue: row sums over the four lane groups, then the normalised rows and their lse. Returns true when a sum or
+    // an accumulator is inf or NaN.
+    auto store = [&]() __attribute__((always_inline)) -> bool {
+        float z = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float ls = l[rb];
+            ls = group_sum(ls);
+            z += 0.f * ls;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t rho = wrow0 + 16 * rb + 4 * c4 + i;
+                const float li = __shfl(ls, 4 * c4 + i);
+#pragma unroll
+                for (int db = 0; db < 8; ++db) z += 0.f * o[rb][db][i];
+                if (rho < nrows) {
+                    const float inv = li > 0.f ? 1.0f / li : 0.f;
+                    const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
+                    float* dst = p.out + int64_t(s) * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + n16;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) dst[16 * db] = o[rb][db][i] * inv;
+                }
+            }
+            const int32_t rho = wrow0 + 16 * rb + n16;
+            if (c4 == 0 && rho < nrows) {
+                const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
+                p.lse[int64_t(s) * p.l_ss + int64_t(t) * p.l_st + h] =
+                    ls > 0.f ? (m[rb] * p.scale_log2 + log2f(ls)) * kLn2 : neg_inf();
+            }
+        }
+        return !(z == 0.f);
+    };
+
+    // The reference m of each row is the maximum of its first tile's scores (key 0 is valid for every row, so it is
+    // finite), and the loop never moves it. A later score above the reference by more than about 128 (log2 units)
+    // overflows p, the sums or the accumulators to inf or NaN; the workgroup then finds the exact row maxima with a
+    // scores-only pass and runs the loop once more (every p now at most 1), overwriting the rows it stored. Any other
+    // outcome is the same softmax with a different reference.
+    reset();
+    prologue();
+    wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
+    lds_barrier();
+    if (wave_live) {
+        float sv[2][8];
+        tile_scores(tile_buf(std::integral_constant<int, 0>{}), 0, sv);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) m[rb] = row_max(sv[rb]);
+    }
+    for (int32_t attempt = 0;; ++attempt) {
+        if (wave_live)
+            run(std::true_type{}, std::false_type{});
+        else
+            run(std::false_type{}, std::false_type{});
+        const bool bad = wave_live && store();
+        if (attempt > 0 || !__syncthreads_or(bad)) return;
+        reset();
+        prologue();
+        if (wave_live)
+            run(std::true_type{}, std::true_type{});
+        else
+            run(std::false_type{}, std::true_type{});
+        prologue();
     }
 }
 
@@ -476,6 +533,7 @@ int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
 
 bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kD) return false;
+    if (!(a.scale > 0.f && a.scale < INFINITY)) return false;   // the softmax tracks the max of unscaled scores
     const int32_t G = a.num_q_heads / a.num_kv_heads;
     if (kBlockRows % G != 0) return false;
     if (int64_t(a.max_row_tokens) * G <= 16) return false;   // decode-shaped: the decode kernel serves it
@@ -529,6 +587,7 @@ int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
 
 bool own_bf16_eligible(const cp_own_args& a) {
     if (a.dtype != CPATTN_BF16 || a.head_dim != kD) return false;
+    if (!(a.scale > 0.f && a.scale < INFINITY)) return false;
     const int32_t G = a.num_q_heads / a.num_kv_heads;
     if (kBlockRows % G != 0) return false;
     if (!al16(a.q) || !al16(a.k) || !al16(a.v)) return false;

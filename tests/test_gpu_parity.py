@@ -192,6 +192,39 @@ def test_mla_late_score_jump():
     compare_rows(wl, batch, res, [0], DEV)                # the other row is untouched
 
 
+def test_extend_late_score_jump():
+    """A late key aligned with one query head scores over 200 (log2 units) above every key of its tile-0, once among a
+    row's context keys and once among its in-step keys. The bf16 extend kernel takes its softmax reference from a
+    unit's first tile, so p overflows here and the unit repeats with the exact maxima; partials, the own-token part
+    and the merge must still match the oracle."""
+    wl = workloads.make("mixed", batch=2, new_lengths=[40, 3], ctx_lengths=[3000, 500])
+    say("extend late score jump")
+    batch = pool.build_batch(wl, DEV)
+    b, c, n, h = 0, 3000, 40, 5
+    g = h // (wl.num_q_heads // wl.num_kv_heads)
+    rv = workloads.row_values(wl, b, DEV)
+    k_ctx = rv.k_ctx.clone()
+    k_ctx[c - 3, g] = (16.0 * torch.sign(rv.q[0, h].float())).to(k_ctx.dtype)     # context key 2997 (stripe 1)
+    slots = pool.logical_slots(batch.block_table[b], c, wl.page_size)
+    api.kv_write(slots, k_ctx, rv.v_ctx, batch.k_pool, batch.v_pool, wl.page_size, wl.partners)
+    k_new = rv.k_new.clone()
+    k_new[n - 2, g] = (16.0 * torch.sign(rv.q[n - 1, h].float())).to(k_new.dtype)  # in-step key 38, second tile
+    t0 = int(wl.q_row_start[b])
+    batch.k_new[t0:t0 + n] = k_new
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    parts, merged = oracle.row_partials(rv.q.cpu(), k_ctx.cpu(), rv.v_ctx.cpu(), wl.partners, wl.scale,
+                                        k_new.cpu(), rv.v_new.cpu())
+    for r in range(wl.partners):
+        check_out(res[2][r, t0:t0 + n], parts[r][0], f"stripe {r} out")
+        check_lse(res[3][r, t0:t0 + n], parts[r][1], f"stripe {r} lse")
+    check_out(res[4][0][t0:t0 + n], parts[-1][0], "own out")
+    check_lse(res[4][1][t0:t0 + n], parts[-1][1], "own lse")
+    check_out(res[0][t0:t0 + n], merged[0], "merged out")
+    check_lse(res[1][t0:t0 + n], merged[1], "merged lse")
+    compare_rows(wl, batch, res, [1], DEV)                # the other row is untouched
+
+
 @pytest.mark.parametrize("fixed_splits", [False, True], ids=["balanced", "fixed"])
 def test_repeat_calls_are_deterministic(fixed_splits):
     """Split items merged from their records give the same bits on every call, with the workspace reused."""
