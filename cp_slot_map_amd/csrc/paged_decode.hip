@@ -92,15 +92,32 @@ struct StepBase {
 template <int PPMODE>   // 2: pp >= 4, 1: pp == 2, 0: pp == 1
 __device__ __forceinline__ void step_bases(StepBase& sb, const_i32_ptr bt_row, int32_t jb, int32_t last_pidx,
                                            int32_t c4, int64_t base_rg, const PoolGeom& geo) {
+    if (PPMODE == 2) {
+        // The step's 16 tokens lie on pages p0 .. p0 + 3 at most (pp >= 4). Away from the end of the row the four
+        // block-table entries are read together (one scalar load, one wait); at the end each index is clamped.
+        const int32_t p0 = jb >> geo.pp_shift;
+        int32_t pg[4];
+        if (p0 + 3 <= last_pidx) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pg[q] = bt_row[p0 + q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pg[q] = bt_row[min(p0 + q, last_pidx)];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int32_t j = jb + 4 * e;                  // first token of instruction e (a multiple of 4)
+            const int32_t q = (j >> geo.pp_shift) - p0;
+            int32_t page = q == 0 ? pg[0] : q == 1 ? pg[1] : q == 2 ? pg[2] : pg[3];
+            page = (page >= 0 && page < geo.num_pages) ? page : 0;
+            sb.base[e] = base_rg + int64_t(page) * geo.s_page + int64_t(j & (geo.pp - 1)) * geo.s_slot;
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int32_t j = jb + 4 * e;                      // first token of instruction e (a multiple of 4)
-        if (PPMODE == 2) {
-            const int32_t pidx = min(j >> geo.pp_shift, last_pidx);
-            int32_t page = bt_row[pidx];
-            page = (page >= 0 && page < geo.num_pages) ? page : 0;
-            sb.base[e] = base_rg + int64_t(page) * geo.s_page + int64_t(j & (geo.pp - 1)) * geo.s_slot;
-        } else {
+        {
             const int32_t n = PPMODE == 1 ? 2 : 4;            // pages touched by the instruction
             int64_t cand[4];
 #pragma unroll
@@ -526,8 +543,16 @@ __device__ __forceinline__ ItemAddr item_addr(const DecodeParams& p, const Tile&
 template <int PPMODE>
 __device__ __forceinline__ void issue_step(StepData& d, const DecodeParams& p, const ItemAddr& ia, int32_t k,
                                            int32_t c4, uint32_t lane_off) {
+    // Step index, last page index and block-table row are wave-uniform; the compiler cannot always prove it inside the
+    // persistent loop, and then reads the page ids with vector loads, whose wait also drains the previous step's
+    // K/V loads. Moved to scalar registers, the page ids come through scalar loads and the K/V loads stay in flight.
+    const int32_t ku = __builtin_amdgcn_readfirstlane(k);
+    const int32_t lp = __builtin_amdgcn_readfirstlane(ia.last_pidx);
+    const uint64_t bt = reinterpret_cast<uint64_t>(ia.bt_row);
+    const uint64_t btu = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int32_t(bt >> 32)))) << 32) |
+                         uint32_t(__builtin_amdgcn_readfirstlane(int32_t(bt)));
     StepBase sb;
-    step_bases<PPMODE>(sb, ia.bt_row, 16 * k, ia.last_pidx, c4, ia.base_rg, p.geo);
+    step_bases<PPMODE>(sb, reinterpret_cast<const_i32_ptr>(btu), 16 * ku, lp, c4, ia.base_rg, p.geo);
     step_load(d, p.kp, p.vp, sb, lane_off);
 }
 
