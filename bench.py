@@ -171,8 +171,23 @@ def main():
     # Algorithmic flops of the partial: every (query token, context token) pair costs Hq * 2 * (D + Dv).
     flops = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64)) * wl.num_q_heads * 2 * (
         wl.head_dim + wl.head_dim_v)
-    kernel_names = {"gqa": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
-                    "mla": "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel)"}
+    kernel_names = {"llama8b": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
+                    "longctx": "cp_paged_attn_partial (gqa_decode_persist_kernel + gqa_decode_fixup_kernel)",
+                    "mla": "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel)",
+                    "mixed": "cp_paged_attn_partial + cp_own_token_attn (gqa_extend_kernel, context and own-token)",
+                    "tiny": "cp_paged_attn_partial (paged_generic_kernel)"}
+    # The roofline that bounds the partial: HBM below the ridge point (peak flops / peak bytes), MFMA above it.
+    mfma_bound = flops / kv_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) if kv_bytes else False
+    if mfma_bound:
+        tf = flops / (part_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": kernel_names.get(wl.name, "cp_paged_attn_partial"), "flops_per_launch": flops,
+                "hbm_achieved_GBs": round(achieved, 2)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": kernel_names.get(wl.name, "cp_paged_attn_partial"), "bytes_per_launch": kv_bytes}
     result = {
         "metric": "striped paged-attention decode: KV GB/s (% of HBM peak) and query tokens/s",
         "value": round(value, 2),
@@ -194,10 +209,7 @@ def main():
         "query_tokens_per_s": round(qtok / (ms_per_step * 1e-3), 1),
         "kernel_ms": {"partial_avg": round(part_avg, 5), "partial_min": round(float(np.min(part_ms)), 5),
                       "merge_avg": round(float(np.mean(merge_ms)), 5)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": kernel_names.get(wl.kind, "cp_paged_attn_partial"),
-                     "bytes_per_launch": kv_bytes},
+        "roofline": roof,
     }
     if flops:
         tflops = flops / (part_avg * 1e-3) / 1e12

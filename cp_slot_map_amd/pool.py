@@ -211,6 +211,10 @@ class StepPlan:
         m.out, m.out_stride_token, m.out_stride_head = self.merged.data_ptr(), self.merged.stride(0), \
             self.merged.stride(1)
         m.lse_out, m.lse_out_stride_token = self.merged_lse.data_ptr(), self.merged_lse.stride(0)
+        # The bucket's real token count (last entry of q_row_start): padding tokens are written as (0, -inf) without
+        # reading their partials.
+        self._token_count = batch.q_row_start[-1:]
+        m.token_count = self._token_count.data_ptr()
         self.merge = m
         self._check = _lib.check
         self.stream = stream

@@ -251,6 +251,24 @@ def test_extend_rows_at_page_staging_limit(ctx_lengths):
     say(f"  worst errors {w}")
 
 
+@pytest.mark.parametrize("name,kw", [SMALL[1], SMALL[4]], ids=["llama8b", "mixed"])
+def test_step_plan_matches_run_step(name, kw):
+    """The prepared step the benchmark times (argument structs built once, the merge told the real token count) gives
+    the same bits as the plain calls, padding tokens included."""
+    wl = workloads.make(name, **kw)
+    batch = pool.build_batch(wl, DEV)
+    mo, ml, po, pl, own = pool.run_step(batch)
+    plan = pool.StepPlan(batch)
+    plan.out.fill_(7.0)
+    plan.merged.fill_(7.0)
+    pm, pml = plan.run()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.out, po) and torch.equal(plan.lse, pl)
+    assert torch.equal(pm, mo) and torch.equal(pml, ml)
+    if own is not None:
+        assert torch.equal(plan.own_out, own[0]) and torch.equal(plan.own_lse, own[1])
+
+
 def test_empty_batch_and_empty_context():
     wl = workloads.make("llama8b", batch=3, ctx_lengths=[0, 0, 2])
     batch = pool.build_batch(wl, DEV)
