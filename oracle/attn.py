@@ -83,14 +83,15 @@ def gqa_attention(q, k, v, scale: float, visible=None):
     return out, lse
 
 
-def stripe_partial(q, k_ctx, v_ctx, P: int, r: int, scale: float):
-    """Partner r's partial: attention of every query over the context positions t with t mod P == r.
+def stripe_partial(q, k_ctx, v_ctx, P: int, r: int, scale: float, interleave: int = 1):
+    """Partner r's partial: attention of every query over the context positions t with floor(t / I) mod P == r
+    (I = interleave; I = 1 is the PR's t mod P == r).
 
     q [m, Hq, D]; k_ctx [c, Hkv, D], v_ctx [c, Hkv, Dv] are the row's logical (unstriped) context.
     Returns out [m, Hq, Dv], lse [m, Hq]; an empty stripe gives (0, -inf).
     """
     k_ctx, v_ctx = _f64(k_ctx), _f64(v_ctx)
-    keep = np.array([t % P == r for t in range(k_ctx.shape[0])], dtype=bool)
+    keep = np.array([(t // interleave) % P == r for t in range(k_ctx.shape[0])], dtype=bool)
     return gqa_attention(q, k_ctx[keep], v_ctx[keep], scale)
 
 
@@ -138,13 +139,13 @@ def row_attention(q, k_ctx, v_ctx, scale: float, k_new=None, v_new=None):
     return gqa_attention(q, k_all, v_all, scale, visible=vis)
 
 
-def row_partials(q, k_ctx, v_ctx, P: int, scale: float, k_new=None, v_new=None):
+def row_partials(q, k_ctx, v_ctx, P: int, scale: float, k_new=None, v_new=None, interleave: int = 1):
     """The method's steps for one row: P stripe partials (plus the own-token partial), then the exact merge.
 
     Returns (partials, (out, lse)) where partials is a list of (out, lse) pairs in stripe order, the own-token
     partial last when present.
     """
-    parts = [stripe_partial(q, k_ctx, v_ctx, P, r, scale) for r in range(P)]
+    parts = [stripe_partial(q, k_ctx, v_ctx, P, r, scale, interleave) for r in range(P)]
     if k_new is not None:
         parts.append(own_token_partial(q, k_new, v_new, scale))
     merged = merge([p[0] for p in parts], [p[1] for p in parts])

@@ -10,7 +10,8 @@ What pins what:
 * closed forms and hand-worked values (tests/golden/*.txt, each citing its passage);
 * invariants the pages state: merging the partials of any split of the keys gives the unsplit result; one stripe is
   plain attention; an empty partial changes nothing; with no context only the own-token partial remains; the slot
-  rule is a bijection whose inverse is phys * P + partner.
+  rule is a bijection whose inverse is phys * P + partner;
+* the interleaved placement against an independent dealing of each page's slots, run by run.
 """
 from __future__ import annotations
 
@@ -298,4 +299,83 @@ def check_stripes(stripe_positions):
         got = list(stripe_positions(L, P, r))
         if got != pos or len(got) != cnt:
             fails.append(f"stripe (L={L}, P={P}, r={r}) = {got}, expected {pos}")
+    return fails
+
+
+# ------------------------------------------------------------------------------------------------ interleave
+def deal_page(page, page_size, P, I):
+    """Independent construction of the interleaved placement of one page: walk its slots in order, hand each run of I
+    slots to the next partner in turn, and let every partner fill its own physical slots of the page in arrival
+    order. Returns {logical slot: (partner, phys)}."""
+    pp = page_size // P
+    filled = [0] * P
+    out = {}
+    for off in range(page_size):
+        run = off // I
+        partner = run - (run // P) * P                 # runs go to partners 0, 1, ..., P-1, 0, ...
+        out[page * page_size + off] = (partner, page * pp + filled[partner])
+        filled[partner] += 1
+    return out
+
+
+def check_interleave_slot_map(slot_map):
+    """slot_map(s, page_size, P, I) against hand-dealt golden values and the dealing construction."""
+    fails = []
+    for row in read_golden("slot_map_interleave.txt"):
+        ps, P, I, s, partner, phys = (int(x) for x in row.split())
+        a, b = slot_map([s], ps, P, I)
+        if (int(a[0]), int(b[0])) != (partner, phys):
+            fails.append(f"golden slot {s} (page_size {ps}, P {P}, I {I}): got {(int(a[0]), int(b[0]))}")
+    for ps, P, I in ((8, 2, 2), (16, 4, 2), (16, 2, 4), (32, 4, 4), (64, 4, 16), (16, 1, 4), (12, 3, 2)):
+        for page in (0, 1, 5):
+            dealt = deal_page(page, ps, P, I)
+            slots = sorted(dealt)
+            a, b = slot_map(slots, ps, P, I)
+            got = {s: (int(x), int(y)) for s, x, y in zip(slots, a, b)}
+            if got != dealt:
+                fails.append(f"placement differs from the dealing (page_size {ps}, P {P}, I {I}, page {page})")
+    return fails
+
+
+def check_interleave_stripes(stripe_positions, stripe_len):
+    """Membership against hand-worked lists, and the count against its closed form
+    L_r = floor(L / (I P)) * I + min(max(L mod (I P) - r I, 0), I)."""
+    fails = []
+    for row in read_golden("stripes_interleave.txt"):
+        head, _, tail = row.partition(":")
+        L, P, I, r, cnt = (int(x) for x in head.split())
+        pos = [int(x) for x in tail.split()]
+        got = list(stripe_positions(L, P, r, I))
+        if got != pos or len(got) != cnt:
+            fails.append(f"stripe (L={L}, P={P}, I={I}, r={r}) = {got}, expected {pos}")
+    for L in (0, 1, 5, 16, 37, 100):
+        for P, I in ((2, 2), (4, 2), (3, 4), (1, 8)):
+            for r in range(P):
+                closed = (L // (I * P)) * I + min(max(L % (I * P) - r * I, 0), I)
+                if stripe_len(L, P, r, I) != closed:
+                    fails.append(f"stripe length (L={L}, P={P}, I={I}, r={r}) is not the closed form")
+    return fails
+
+
+def check_interleave_stripe_partial(stripe_partial, gather_stripe, place_logical_rows, gqa_attention, seed=8):
+    """With interleave, partner r's partial equals attention over the keys found in r's pool by physical addressing."""
+    fails = []
+    rng = np.random.default_rng(seed)
+    for page_size, P, I in ((8, 2, 2), (16, 4, 2), (16, 2, 4)):
+        hkv, hq, d, L = 2, 4, 3, 45
+        npg = (L + page_size - 1) // page_size
+        num_pages = 1 + npg + 2
+        bt = np.concatenate([rng.permutation(np.arange(1, num_pages))[:npg], [0, 0]])
+        k = rng.standard_normal((L, hkv, d))
+        v = rng.standard_normal((L, hkv, d))
+        q = rng.standard_normal((2, hq, d))
+        kp = place_logical_rows([k], [bt], [L], page_size, P, num_pages, interleave=I)
+        vp = place_logical_rows([v], [bt], [L], page_size, P, num_pages, interleave=I)
+        for r in range(P):
+            kr = gather_stripe(kp[r], bt, L, page_size, P, r, I)
+            vr = gather_stripe(vp[r], bt, L, page_size, P, r, I)
+            ref_o, ref_l = gqa_attention(q, kr, vr, 0.5)
+            o, l = stripe_partial(q, k, v, P, r, 0.5, I)
+            if np.max(np.abs(o - ref_o)) > 1e-13 or np.max(np.abs(l - ref_l)) > 1e-13:
+                fails.append(f"stripe {r} (page_size {page_size}, P {P}, I {I}) does not attend its pool's keys")
     return fails

@@ -155,3 +155,40 @@ def test_slot_map_mistakes_are_caught():
 
 def test_stripe_membership_mistake_is_caught():
     assert pins.check_stripes(_stripes_from_one)
+
+
+def _slot_map_interleave_dense_phys(s, ps, P, I=1):
+    a, _ = S.slot_map(s, ps, P, I)                  # right partner, physical slot as if I were 1
+    s = np.asarray(s, dtype=np.int64)
+    return a, np.where(s >= 0, s // P, -1)
+
+
+def _slot_map_interleave_ignored(s, ps, P, I=1):
+    return S.slot_map(s, ps, P)
+
+
+def _slot_map_interleave_runs_per_partner(s, ps, P, I=1):
+    s = np.asarray(s, dtype=np.int64)              # runs of P slots to I "partners": the two sizes swapped
+    return np.where(s >= 0, (s // P) % I if I > 1 else s % P, -1), np.where(s >= 0, (s // (I * P)) * I + s % I, -1)
+
+
+def _stripes_interleave_ignored(L, P, r, I=1):
+    return S.stripe_positions(L, P, r)
+
+
+def _stripe_len_interleave_ignored(L, P, r, I=1):
+    return S.stripe_len(L, P, r)
+
+
+def _stripe_partial_interleave_ignored(q, k_ctx, v_ctx, P, r, scale, I=1):
+    return A.stripe_partial(q, k_ctx, v_ctx, P, r, scale)
+
+
+def test_interleave_mistakes_are_caught():
+    assert pins.check_interleave_slot_map(_slot_map_interleave_dense_phys)
+    assert pins.check_interleave_slot_map(_slot_map_interleave_ignored)
+    assert pins.check_interleave_slot_map(_slot_map_interleave_runs_per_partner)
+    assert pins.check_interleave_stripes(_stripes_interleave_ignored, S.stripe_len)
+    assert pins.check_interleave_stripes(S.stripe_positions, _stripe_len_interleave_ignored)
+    assert pins.check_interleave_stripe_partial(_stripe_partial_interleave_ignored, oracle.gather_stripe,
+                                                oracle.place_logical_rows, oracle.gqa_attention)

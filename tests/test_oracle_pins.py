@@ -207,3 +207,10 @@ def test_workload_recipes():
     r1 = workloads.row_values(t, 2)
     r2 = workloads.row_values(t, 2)
     assert np.array_equal(r1.k_ctx.numpy(), r2.k_ctx.numpy())
+
+
+def test_interleaved_placement_is_pinned():
+    assert pins.check_interleave_slot_map(oracle.slot_map) == []
+    assert pins.check_interleave_stripes(oracle.stripe_positions, oracle.stripe_len) == []
+    assert pins.check_interleave_stripe_partial(oracle.stripe_partial, oracle.gather_stripe, oracle.place_logical_rows,
+                                                oracle.gqa_attention) == []
