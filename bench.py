@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "longctx", "mla", "mixed"])
+    ap.add_argument("--interleave", type=int, default=1,
+                    help="KV-cache interleave size of the pool (runs of that many slots per partner; 1 = plain rule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -99,7 +101,7 @@ def cpu_baseline(wl, budget_s):
         vn = rv.v_new.cpu() if rv.v_new is not None else None
         del rv
         t0 = time.perf_counter()
-        oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn)
+        oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn, interleave=wl.interleave)
         spent += time.perf_counter() - t0
         kv_bytes += int(wl.ctx_len[b]) * per_token
         tokens += int(wl.new_len[b])
@@ -131,7 +133,7 @@ def main():
         copy_calibration()
         return
     torch.cuda.set_device(0)
-    wl = workloads.make(args.workload)
+    wl = workloads.make(args.workload, interleave=args.interleave)
     batch = pool.build_batch(wl, "cuda", fill=0.0)
     plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
@@ -204,7 +206,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "page_size": wl.page_size, "partners": wl.partners,
                    "ctx_tokens": int(wl.ctx_len.astype(np.int64).sum()), "query_tokens": qtok, "seed": wl.seed,
-                   "kv_bytes": kv_bytes},
+                   "kv_bytes": kv_bytes, "interleave": wl.interleave},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "query_tokens_per_s": round(qtok / (ms_per_step * 1e-3), 1),
         "kernel_ms": {"partial_avg": round(part_avg, 5), "partial_min": round(float(np.min(part_ms)), 5),

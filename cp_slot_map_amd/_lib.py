@@ -27,7 +27,7 @@ class PagedArgs(C.Structure):
         ("stripe_begin", _i32), ("stripe_count", _i32), ("page_size", _i32), ("num_pages", _i32),
         ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32), ("head_dim_v", _i32),
         ("scale", C.c_float), ("max_ctx_len", _i32), ("max_row_tokens", _i32), ("max_pages", _i32),
-        ("flags", _i32),
+        ("flags", _i32), ("interleave", _i32),
         ("q_row_start", _p), ("ctx_len", _p), ("block_table", _p), ("bt_stride", _i64),
         ("q", _p), ("q_stride_token", _i64), ("q_stride_head", _i64),
         ("k_pool", _p), ("v_pool", _p),
@@ -65,16 +65,16 @@ EXPORTS = {
     "cpattn_last_error": (C.c_char_p, []),
     "cpattn_version": (C.c_char_p, []),
     "cpattn_struct_size": (_i64, [_i32]),
-    "cp_slot_map": (_i32, [_p, _i64, _i32, _i32, _p, _p, _p]),
-    "cp_slot_map_rank": (_i32, [_p, _i64, _i32, _i32, _i32, _i64, _p, _p]),
+    "cp_slot_map": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
+    "cp_slot_map_rank": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i64, _p, _p]),
     "cp_kv_write": (_i32, [_p, _i64, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _i64, _i64, _i64, _i64,
-                           _i32, _i32, _i32, _i32, _i32, _i64, _p]),
+                           _i32, _i32, _i32, _i32, _i32, _i32, _i64, _p]),
     "cp_paged_attn_partial": (_i32, [C.POINTER(PagedArgs), _p]),
     "cp_paged_attn_workspace_size": (_i32, [C.POINTER(PagedArgs), C.POINTER(_i64)]),
     "cp_own_token_attn": (_i32, [C.POINTER(OwnArgs), _p]),
     "cp_lse_merge": (_i32, [C.POINTER(MergeArgs), _p]),
     "cp_debug_gather_stripe": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32,
-                                      _i32, _p, _p]),
+                                      _i32, _i32, _p, _p]),
 }
 
 _LIB = None

@@ -52,26 +52,27 @@ def version():
     return _lib_handle().cpattn_version().decode()
 
 
-def slot_map(logical_slot: torch.Tensor, page_size: int, partners: int, stream=None):
+def slot_map(logical_slot: torch.Tensor, page_size: int, partners: int, stream=None, *, interleave: int = 1):
     """(partner int32, physical slot int64) for each logical slot (int64; < 0 = padding -> -1, -1)."""
     lib = _lib_handle()
     _need_cuda(logical_slot)
     s = logical_slot.to(torch.int64).contiguous()
     partner = torch.empty(s.shape, dtype=torch.int32, device=s.device)
     phys = torch.empty(s.shape, dtype=torch.int64, device=s.device)
-    _lib.check(lib.cp_slot_map(_ptr(s), s.numel(), int(page_size), int(partners), _ptr(partner), _ptr(phys),
-                               _stream(stream)))
+    _lib.check(lib.cp_slot_map(_ptr(s), s.numel(), int(page_size), int(partners), int(interleave), _ptr(partner),
+                               _ptr(phys), _stream(stream)))
     return partner, phys
 
 
-def slot_map_rank(logical_slot: torch.Tensor, page_size: int, partners: int, rank: int, sink_slot: int, stream=None):
+def slot_map_rank(logical_slot: torch.Tensor, page_size: int, partners: int, rank: int, sink_slot: int, stream=None,
+                  *, interleave: int = 1):
     """Per-rank write slot: physical slot if `rank` owns the token, else `sink_slot`; -1 for padding."""
     lib = _lib_handle()
     _need_cuda(logical_slot)
     s = logical_slot.to(torch.int64).contiguous()
     out = torch.empty(s.shape, dtype=torch.int64, device=s.device)
-    _lib.check(lib.cp_slot_map_rank(_ptr(s), s.numel(), int(page_size), int(partners), int(rank), int(sink_slot),
-                                    _ptr(out), _stream(stream)))
+    _lib.check(lib.cp_slot_map_rank(_ptr(s), s.numel(), int(page_size), int(partners), int(interleave), int(rank),
+                                    int(sink_slot), _ptr(out), _stream(stream)))
     return out
 
 
@@ -86,7 +87,7 @@ def _pool_strides(pool, kind):
 
 
 def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partners: int, *, kind="gqa",
-             stripe_begin=0, stripe_count=None, sink_slot=-1, stream=None):
+             stripe_begin=0, stripe_count=None, sink_slot=-1, stream=None, interleave: int = 1):
     """Write rows k_src [n, Hkv, D] (v_src [n, Hkv, Dv] or None) into the stripe pools through the slot map."""
     lib = _lib_handle()
     _need_cuda(logical_slot, k_src, v_src, k_pool, v_pool)
@@ -108,13 +109,16 @@ def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partner
                                _dtype_code(k_src.dtype), hkv, k_src.shape[2],
                                0 if v_src is None else v_src.shape[2], _ptr(k_pool),
                                _ptr(v_pool if v_pool is not None else k_pool), ss, sp, sl, sh, int(page_size), P,
-                               k_pool.shape[1], int(stripe_begin), sc, int(sink_slot), _stream(stream)))
+                               int(interleave), k_pool.shape[1], int(stripe_begin), sc, int(sink_slot),
+                               _stream(stream)))
 
 
 def _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale, kind,
-                stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens, fixed_splits=False):
+                stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens, fixed_splits=False,
+                interleave=1):
     a = PagedArgs()
     a.flags = _lib.CPATTN_FLAG_FIXED_SPLITS if fixed_splits else 0
+    a.interleave = int(interleave)
     a.kind = CPATTN_MLA if kind == "mla" else CPATTN_GQA
     a.dtype = _dtype_code(q.dtype)
     if k_pool.dtype != q.dtype:
@@ -183,13 +187,13 @@ def _check_int32_dev(*ts):
 
 def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                               kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens,
-                              fixed_splits=False):
+                              fixed_splits=False, interleave=1):
     lib = _lib_handle()
     sc = int(partners) - stripe_begin if stripe_count is None else stripe_count
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
                     max_row_tokens=max_row_tokens, out=None, lse=None, num_tokens=q.shape[0],
-                    fixed_splits=fixed_splits)
+                    fixed_splits=fixed_splits, interleave=interleave)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     return int(n.value)
@@ -197,12 +201,13 @@ def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_tab
 
 def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                        kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len=None, max_row_tokens=None,
-                       out=None, lse=None, workspace=None, stream=None, fixed_splits=False):
+                       out=None, lse=None, workspace=None, stream=None, fixed_splits=False, interleave=1):
     """Per-stripe partials (out [S, T, Hq, Dv] fp32, lse [S, T, Hq] fp32) of attention over the striped pool.
 
     q [T, Hq, D]; q_row_start int32 [B + 1]; ctx_len int32 [B]; block_table int32 [B, max_pages]. ``max_ctx_len``
     and ``max_row_tokens`` are host upper bounds (read from the device with a sync when omitted). ``fixed_splits``
     makes each row's result independent, to the bit, of the rest of the call (CPATTN_FLAG_FIXED_SPLITS).
+    ``interleave`` is the KV-cache interleave size the pool was written with (runs of that many slots per partner).
     """
     lib = _lib_handle()
     _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
@@ -226,7 +231,8 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
         raise ValueError("out/lse must be fp32 with contiguous last dims")
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
-                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits)
+                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits,
+                    interleave=interleave)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     if n.value > 0:
@@ -309,7 +315,7 @@ def lse_merge(outs, lses, *, out_dtype=torch.float32, out=None, lse_out=None, to
 
 
 def debug_gather_stripe(k_pool, block_table_row, ctx_len: int, page_size: int, partners: int, r: int, *,
-                        kind="gqa", stream=None):
+                        kind="gqa", stream=None, interleave: int = 1):
     """Stripe r's keys of one row in local order, read with the kernels' own addressing: [Lr, Hkv, D]."""
     lib = _lib_handle()
     _need_cuda(k_pool, block_table_row)
@@ -318,9 +324,10 @@ def debug_gather_stripe(k_pool, block_table_row, ctx_len: int, page_size: int, p
     hkv = 1 if kind == "mla" else k_pool.shape[3]
     D = k_pool.shape[-1]
     P = int(partners)
-    Lr = max(0, -(-(int(ctx_len) - r) // P))
+    I, L = int(interleave), int(ctx_len)
+    Lr = (L // (I * P)) * I + min(max(L % (I * P) - r * I, 0), I) if I >= 1 else 0   # output rows to allocate
     dst = torch.empty((Lr, hkv, D), dtype=k_pool.dtype, device=k_pool.device)
     _lib.check(lib.cp_debug_gather_stripe(_ptr(k_pool), _dtype_code(k_pool.dtype), ss, sp, sl, sh, k_pool.shape[1],
-                                          _ptr(block_table_row), int(ctx_len), int(page_size), P, int(r), hkv, D,
-                                          _ptr(dst), _stream(stream)))
+                                          _ptr(block_table_row), int(ctx_len), int(page_size), P, I, int(r), hkv,
+                                          D, _ptr(dst), _stream(stream)))
     return dst

@@ -43,8 +43,11 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
         return fail(CPATTN_EINVAL, "negative size");
     if (a.num_partners < 1 || a.num_partners > 16)
         return fail(CPATTN_EINVAL, "num_partners = %d outside [1, 16]", a.num_partners);
-    if (a.page_size < 1 || a.page_size % a.num_partners)
-        return fail(CPATTN_EINVAL, "num_partners = %d must divide page_size = %d", a.num_partners, a.page_size);
+    if (a.interleave < 0 || a.interleave > 65536) return fail(CPATTN_EINVAL, "interleave = %d outside [0, 65536]", a.interleave);
+    const int32_t ilv = interleave_of(a);
+    if (a.page_size < 1 || a.page_size % (a.num_partners * ilv))
+        return fail(CPATTN_EINVAL, "num_partners * interleave = %d must divide page_size = %d", a.num_partners * ilv,
+                    a.page_size);
     if (a.stripe_count < 1 || a.stripe_begin < 0 || a.stripe_begin + a.stripe_count > a.num_partners)
         return fail(CPATTN_EINVAL, "stripes [%d, %d) outside [0, %d)", a.stripe_begin, a.stripe_begin + a.stripe_count,
                     a.num_partners);
@@ -72,7 +75,7 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
     if (a.num_tokens > 0 && !a.q_row_start) return fail(CPATTN_EINVAL, "q_row_start is null");
     const int32_t pp = a.page_size / a.num_partners;
     *geo = PoolGeom{a.kv_stride_stripe, a.kv_stride_page, a.kv_stride_slot, a.kv_stride_head, pp, ilog2_exact(pp),
-                    a.num_pages, 0};
+                    a.num_pages, ilv};
     return CPATTN_OK;
 }
 

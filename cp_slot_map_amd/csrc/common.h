@@ -55,15 +55,17 @@ struct PoolGeom {
     int32_t pp;          // slots per physical page = page_size / P
     int32_t pp_shift;    // log2(pp) if pp is a power of two, else -1
     int32_t num_pages;   // valid page ids are [0, num_pages); others read page 0
-    int32_t pad_;
+    int32_t interleave;  // I >= 1: runs of I consecutive logical slots go to one partner (I = 1: slot s to s mod P)
 };
 
 // Element offset of local token i of stripe r (kv head g) inside the pool set.
 //
-// Local token i of partner r is the row's context position i*P + r. By the slot rule its logical slot is
-// page * page_size + (i*P + r) mod page_size, so it sits on logical page block_table[(i*P + r) / page_size] =
-// block_table[i / pp] at physical slot (i*P + r) mod page_size / P = i mod pp of r's pool: each stripe is an ordinary
-// paged cache of page size pp sharing the logical block table. Every kernel that reads the pool goes through this.
+// Placement with interleave I (I = 1 is the slot rule of the PR): logical slot s goes to partner floor(s / I) mod P at
+// physical slot floor(s / (I P)) * I + s mod I. With I P dividing page_size, local token i of partner r is the row's
+// context position t = floor(i / I) * I * P + r * I + i mod I; its slot page * page_size + t mod page_size lands on
+// logical page block_table[t / page_size] = block_table[i / pp] at physical slot i mod pp of r's pool (pp = page_size
+// / P, a multiple of I): each stripe is an ordinary paged cache of page size pp sharing the logical block table, for
+// every I. Every kernel that reads the pool goes through this.
 __device__ __forceinline__ int64_t stripe_token_offset(const int32_t* __restrict__ bt_row, int32_t i, int32_t r,
                                                        int32_t g, const PoolGeom& geo) {
     int32_t pidx, slot;
@@ -88,9 +90,22 @@ __device__ __forceinline__ int64_t page_slot_offset(int32_t page, int32_t slot, 
            int64_t(g) * geo.s_head;
 }
 
-// Tokens partner r holds of a row with L context tokens: positions t < L with t mod P == r.
-__device__ __forceinline__ int32_t stripe_length(int32_t L, int32_t r, int32_t P) {
-    return L > r ? (L - r + P - 1) / P : 0;
+// Tokens partner r holds of a row with L context tokens: positions t < L with floor(t / I) mod P == r, i.e. I tokens
+// of every full cycle of I P positions plus those of the last, partial cycle.
+__host__ __device__ __forceinline__ int32_t stripe_length(int32_t L, int32_t r, int32_t P, int32_t I) {
+    if (L <= 0) return 0;
+    const int32_t IP = I * P;
+    const int32_t full = L / IP;
+    const int32_t rest = L - full * IP - r * I;
+    return full * I + (rest < 0 ? 0 : rest > I ? I : rest);
+}
+
+// Partner and physical slot of logical slot s >= 0 under interleave I.
+__device__ __forceinline__ void place_slot(int64_t s, int64_t P, int64_t I, int32_t& partner, int64_t& phys) {
+    const int64_t run = s / I;
+    const int64_t cycle = run / P;
+    partner = int32_t(run - cycle * P);
+    phys = cycle * I + (s - run * I);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     int32_t nkeys;
     if (MODE == kFromPool) {
         const int32_t L = min(max(((const_i32_ptr)p.ctx_len)[b], 0), p.max_pages * p.page_size);
-        nkeys = stripe_length(L, r, p.P);
+        nkeys = stripe_length(L, r, p.P, p.geo.interleave);
     } else {
         nkeys = min(ntok, (min(row0 + kBlockRows, nrows) - 1) / p.G + 1);   // keys up to the block's last token
     }
@@ -538,7 +538,7 @@ bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (kBlockRows % G != 0) return false;
     if (int64_t(a.max_row_tokens) * G <= 16) return false;   // decode-shaped: the decode kernel serves it
     if (geo.pp_shift < 0) return false;
-    const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
+    const int64_t max_lr = max_stripe_length(a);
     if ((max_lr + geo.pp - 1) / geo.pp > kMaxPages) return false;
     if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool)) return false;
     if ((a.q_stride_token | a.q_stride_head | a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot |

@@ -2,8 +2,9 @@
 //
 // Every write goes through the placement (mstar PR #1124, "Context / Sequence Parallel 1/5", PR description and commit
 // message): logical slot s belongs to partner s mod P at physical slot floor(s / P), i.e. page floor(s / P) / pp and
-// slot floor(s / P) mod pp of that partner's pool (pp = page_size / P). Non-owners write the sink slot when one is
-// given. The review thread on resident planning is the counter-example: addressing at the logical page size writes
+// slot floor(s / P) mod pp of that partner's pool (pp = page_size / P); with interleave I, partner floor(s / I) mod P
+// at physical slot floor(s / (I P)) * I + s mod I (the placement of cp_slot_map). Non-owners write the sink slot when
+// one is given. The review thread on resident planning is the counter-example: addressing at the logical page size writes
 // every token on every rank at offsets the smaller physical pages do not have.
 //
 // One 64-lane wave per (token, stripe in range): lanes copy the head rows with 16-byte (or narrower) accesses.
@@ -20,7 +21,7 @@ struct KvWriteParams {
     uint8_t* vp;
     int64_t s_stripe, s_page, s_slot, s_head;   // bytes
     int64_t n;
-    int64_t P, pp, num_pages, sink;
+    int64_t P, I, pp, num_pages, sink;
     int32_t stripe_begin, stripe_count, Hkv, row_k_bytes, row_v_bytes;
 };
 
@@ -41,8 +42,9 @@ __global__ __launch_bounds__(64) void kv_write_kernel(const KvWriteParams p) {
     if (i >= p.n) return;
     const int64_t s = p.slot[i];
     if (s < 0) return;
-    const int64_t owner = s % p.P;
-    int64_t phys = s / p.P;
+    int32_t owner;
+    int64_t phys;
+    place_slot(s, p.P, p.I, owner, phys);
     if (owner != r) {
         if (p.sink < 0) return;
         phys = p.sink;
@@ -66,11 +68,14 @@ extern "C" int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const voi
                                int64_t src_stride_token, int64_t src_stride_head, int32_t dtype, int32_t num_kv_heads,
                                int32_t head_dim, int32_t head_dim_v, void* k_pool, void* v_pool,
                                int64_t kv_stride_stripe, int64_t kv_stride_page, int64_t kv_stride_slot,
-                               int64_t kv_stride_head, int32_t page_size, int32_t num_partners, int32_t num_pages,
-                               int32_t stripe_begin, int32_t stripe_count, int64_t sink_slot, hipStream_t stream) {
+                               int64_t kv_stride_head, int32_t page_size, int32_t num_partners, int32_t interleave,
+                               int32_t num_pages, int32_t stripe_begin, int32_t stripe_count, int64_t sink_slot,
+                               hipStream_t stream) {
     if (n < 0) return fail(CPATTN_EINVAL, "n = %lld is negative", (long long)n);
-    if (num_partners < 1 || page_size < 1 || page_size % num_partners)
-        return fail(CPATTN_EINVAL, "num_partners = %d must divide page_size = %d", num_partners, page_size);
+    if (num_partners < 1 || interleave < 1 || page_size < 1 || page_size % num_partners ||
+        (page_size / num_partners) % interleave)
+        return fail(CPATTN_EINVAL, "num_partners * interleave = %lld must divide page_size = %d",
+                    (long long)num_partners * interleave, page_size);
     if (stripe_count < 1 || stripe_begin < 0 || stripe_begin + stripe_count > num_partners)
         return fail(CPATTN_EINVAL, "stripes [%d, %d) outside [0, %d)", stripe_begin, stripe_begin + stripe_count,
                     num_partners);
@@ -101,6 +106,7 @@ extern "C" int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const voi
     p.s_head = kv_stride_head * el;
     p.n = n;
     p.P = num_partners;
+    p.I = interleave;
     p.pp = pp;
     p.num_pages = num_pages;
     p.sink = sink_slot;

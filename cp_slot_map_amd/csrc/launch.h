@@ -5,6 +5,13 @@
 
 namespace cpattn {
 
+// Interleave size of a call (0 in the struct means 1) and the longest stripe of a row with max_ctx_len tokens (stripe
+// 0 holds the most); host-side bounds size launches and workspaces from it.
+inline int32_t interleave_of(const cp_paged_args& a) { return a.interleave > 1 ? a.interleave : 1; }
+inline int64_t max_stripe_length(const cp_paged_args& a) {
+    return stripe_length(a.max_ctx_len > 0 ? a.max_ctx_len : 0, 0, a.num_partners, interleave_of(a));
+}
+
 // Generic per-stripe partial: any built (dtype, head_dim, head_dim_v), any pp. One wave per (row, stripe, kv head,
 // block of query rows) streams the whole stripe; used for fp32 pools, MLA until its own kernel takes over, and any
 // shape the specialised kernels do not cover.
@@ -15,7 +22,7 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
 
-// Specialised bf16 GQA partial for rows that bring many query tokens (head_dim = head_dim_v = 128): 256 query rows per
+// Specialised bf16 GQA partial for rows that bring many query tokens (head_dim = head_dim_v = 128): 128 query rows per
 // workgroup, K/V tiles staged in LDS, MFMA score and value products. The same kernel serves the own-token part.
 bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);

@@ -114,7 +114,7 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     x.live = x.qtok < ntok;
     x.t = tok0 + x.qtok;
     const int32_t L = min(max(cl[x.b], 0), p.max_pages * p.page_size);
-    x.Lr = stripe_length(L, p.stripe_begin + x.s, p.P);
+    x.Lr = stripe_length(L, p.stripe_begin + x.s, p.P, p.geo.interleave);
     x.j0 = x.c * p.chunk_tokens;
     x.j1 = min(x.j0 + p.chunk_tokens, x.Lr);
     return x;
@@ -132,7 +132,7 @@ __device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
     const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
     if (qtok >= min(tok1 - tok0, p.max_row_tokens)) return 0;
     const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
-    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P);
+    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     return max(0, min(Lr - c * p.chunk_tokens, p.chunk_tokens));
 }
 
@@ -536,7 +536,7 @@ MlaShape mla_shape(const cp_paged_args& a) {
     MlaShape d{};
     const int64_t mrt = std::max<int64_t>(1, a.max_row_tokens);
     d.n_items = int64_t(a.num_rows) * a.stripe_count * mrt;
-    const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
+    const int64_t max_lr = max_stripe_length(a);
     int64_t nch = 1;
     if (d.n_items > 0 && d.n_items < kTargetUnits && max_lr > 256) {
         nch = std::min<int64_t>((kTargetUnits + d.n_items - 1) / d.n_items, (max_lr + 255) / 256);

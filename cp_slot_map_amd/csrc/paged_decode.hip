@@ -289,7 +289,7 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
 
     const int32_t r = p.stripe_begin + s;
     const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
-    const int32_t Lr = stripe_length(L, r, p.P);
+    const int32_t Lr = stripe_length(L, r, p.P, p.geo.interleave);
     const int32_t CH = p.chunk_steps * 16;
     const int32_t nch = (Lr + CH - 1) / CH;
     if (c >= max(nch, 1)) return;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const Decode
     if (row0 >= nrows) return;
     const int32_t tile_rows = min(16, nrows - row0);
     const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
-    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P);
+    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     const int32_t CH = p.chunk_steps * 16;
     const int32_t nch = (Lr + CH - 1) / CH;
     if (nch <= 1) return;                       // written directly by the chunk kernel
@@ -500,7 +500,7 @@ __device__ __forceinline__ int32_t tile_steps(const DecodeParams& p, int32_t T) 
     const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
     const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
     const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
-    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P);
+    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     return qt * 16 < nrows ? (Lr + 15) >> 4 : 0;
 }
 
@@ -521,7 +521,7 @@ __device__ __forceinline__ Tile load_tile(const DecodeParams& p, int32_t T) {
     const int32_t tok1 = min(max(qrs[tl.b + 1], tl.tok0), p.T);
     tl.nrows = min(tok1 - tl.tok0, p.max_row_tokens) * p.G;
     const int32_t L = min(max(cl[tl.b], 0), p.max_pages * p.page_size);
-    tl.Lr = stripe_length(L, p.stripe_begin + tl.s, p.P);
+    tl.Lr = stripe_length(L, p.stripe_begin + tl.s, p.P, p.geo.interleave);
     tl.n_steps = tl.qt * 16 < tl.nrows ? (tl.Lr + 15) >> 4 : 0;
     return tl;
 }
@@ -900,7 +900,7 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
     d.num_tiles = int64_t(a.num_rows) * a.stripe_count * d.n_qtiles;
     d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && decode_persistent_enabled() &&
                    d.num_tiles <= kMaxPersistTiles;
-    const int64_t max_lr = (int64_t(std::max(a.max_ctx_len, 0)) + a.num_partners - 1) / a.num_partners;
+    const int64_t max_lr = max_stripe_length(a);
     const int64_t CH = int64_t(decode_chunk_steps()) * 16;
     d.n_chunks = d.persistent ? 1 : std::max<int64_t>(1, (max_lr + CH - 1) / CH);
     d.triples = d.num_tiles * a.num_kv_heads;

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p
 
     const int32_t r = p.stripe_begin + s;
     const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
-    const int32_t Lr = stripe_length(L, r, p.P);
+    const int32_t Lr = stripe_length(L, r, p.P, p.geo.interleave);
     const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
     const T* Q = static_cast<const T*>(p.q);
     const T* K = static_cast<const T*>(p.kp);
@@ -228,21 +228,23 @@ using namespace cpattn;
 extern "C" int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe,
                                           int64_t kv_stride_page, int64_t kv_stride_slot, int64_t kv_stride_head,
                                           int32_t num_pages, const int32_t* block_table_row, int32_t ctx_len,
-                                          int32_t page_size, int32_t num_partners, int32_t r, int32_t num_kv_heads,
-                                          int32_t head_dim, void* dst, hipStream_t stream) {
-    if (num_partners < 1 || page_size < 1 || page_size % num_partners)
-        return fail(CPATTN_EINVAL, "bad geometry (page_size=%d, P=%d)", page_size, num_partners);
+                                          int32_t page_size, int32_t num_partners, int32_t interleave, int32_t r,
+                                          int32_t num_kv_heads, int32_t head_dim, void* dst, hipStream_t stream) {
+    if (num_partners < 1 || interleave < 1 || page_size < 1 || page_size % num_partners ||
+        (page_size / num_partners) % interleave)
+        return fail(CPATTN_EINVAL, "bad geometry (page_size=%d, P=%d, interleave=%d)", page_size, num_partners,
+                    interleave);
     if (r < 0 || r >= num_partners) return fail(CPATTN_EINVAL, "stripe %d outside [0, %d)", r, num_partners);
     if (ctx_len < 0 || num_kv_heads < 1 || head_dim < 1 || num_pages < 1)
         return fail(CPATTN_EINVAL, "negative or zero size");
     if (kv_stride_stripe < 0 || kv_stride_page < 0 || kv_stride_slot < 0 || kv_stride_head < 0)
         return fail(CPATTN_EINVAL, "negative stride");
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d unknown", dtype);
-    const int32_t Lr = ctx_len > r ? (ctx_len - r + num_partners - 1) / num_partners : 0;
+    const int32_t Lr = stripe_length(ctx_len, r, num_partners, interleave);
     if (Lr == 0) return CPATTN_OK;
     if (!k_pool || !block_table_row || !dst) return fail(CPATTN_EINVAL, "cp_debug_gather_stripe: null pointer");
     PoolGeom geo{kv_stride_stripe, kv_stride_page, kv_stride_slot, kv_stride_head, page_size / num_partners,
-                 ilog2_exact(page_size / num_partners), num_pages, 0};
+                 ilog2_exact(page_size / num_partners), num_pages, interleave};
     const int64_t total = int64_t(Lr) * num_kv_heads * head_dim;
     const dim3 grid(uint32_t(std::min<int64_t>((total + 255) / 256, 65536)));
     if (dtype == CPATTN_F32)

@@ -108,9 +108,10 @@ def build_batch(wl, device="cuda", *, fill=float("nan"), layout="hnd", rows=None
         if c:
             s = logical_slots(bt[b], c, ps)
             if wl.kind == "mla":
-                api.kv_write(s, rv.k_ctx.reshape(c, 1, -1), None, k_pool, None, ps, P, kind="mla")
+                api.kv_write(s, rv.k_ctx.reshape(c, 1, -1), None, k_pool, None, ps, P, kind="mla",
+                             interleave=wl.interleave)
             else:
-                api.kv_write(s, rv.k_ctx, rv.v_ctx, k_pool, v_pool, ps, P)
+                api.kv_write(s, rv.k_ctx, rv.v_ctx, k_pool, v_pool, ps, P, interleave=wl.interleave)
         del rv
     ctx = torch.from_numpy(wl.ctx_len.astype(np.int32)).to(dev)
     qrs_t = torch.from_numpy(qrs.astype(np.int32)).to(dev)
@@ -132,7 +133,7 @@ def run_step(batch: Batch, *, out=None, lse=None, merged=None, merged_lse=None, 
                                       batch.block_table, page_size=wl.page_size, partners=wl.partners,
                                       scale=wl.scale, kind=wl.kind, max_ctx_len=batch.max_ctx_len,
                                       max_row_tokens=batch.max_row_tokens, out=out, lse=lse, workspace=workspace,
-                                      stream=stream, fixed_splits=fixed_splits)
+                                      stream=stream, fixed_splits=fixed_splits, interleave=wl.interleave)
     outs = [out[s] for s in range(out.shape[0])]
     lses = [lse[s] for s in range(lse.shape[0])]
     own = None
@@ -172,7 +173,7 @@ class StepPlan:
                                      batch.block_table, page_size=wl.page_size, partners=P, scale=wl.scale,
                                      kind=wl.kind, stripe_begin=0, stripe_count=P, max_ctx_len=batch.max_ctx_len,
                                      max_row_tokens=batch.max_row_tokens, out=self.out, lse=self.lse, num_tokens=T,
-                                     fixed_splits=fixed_splits)
+                                     fixed_splits=fixed_splits, interleave=wl.interleave)
         n = C.c_int64(0)
         _lib.check(self.lib.cp_paged_attn_workspace_size(C.byref(self.paged), C.byref(n)))
         self.workspace_bytes = int(n.value)

@@ -70,13 +70,21 @@ int64_t cpattn_struct_size(int32_t which);
  * Source: the slot rule of mstar PR #1124 (PR description); the review thread on resident planning notes that a
  * partner pool holds page_size / P slots a page, which is why every write path must go through this map.
  *
+ * Interleave: the vLLM compare view "[Core] Add explicit layer parallel plans" reads a KV-cache interleave size I
+ * from the parallel config (FlashAttentionMetadataBuilder); the pages give no placement for it, and the one taken
+ * here is that runs of I consecutive slots go to one partner, partners in turn, each partner packing its runs:
+ * partner floor(s / I) mod P at physical slot floor(s / (I P)) * I + s mod I. I = 1 is the PR's rule.
+ *
  *   logical_slot  device int64 [n]: page_id * page_size + offset of each token to write; < 0 marks a padding token.
- *   partner_out   device int32 [n]: s mod P, or -1 for s < 0.
- *   phys_out      device int64 [n]: floor(s / P) (= page_id * (page_size / P) + offset / P), or -1 for s < 0.
- * EINVAL: n < 0, P < 1, page_size < 1, page_size % P != 0, or a null pointer with n > 0. n = 0 enqueues nothing.
+ *   interleave    I >= 1; I * P must divide page_size.
+ *   partner_out   device int32 [n]: floor(s / I) mod P (s mod P for I = 1), or -1 for s < 0.
+ *   phys_out      device int64 [n]: floor(s / (I P)) * I + s mod I (floor(s / P) for I = 1; always
+ *                 page_id * (page_size / P) + a slot below page_size / P), or -1 for s < 0.
+ * EINVAL: n < 0, P < 1, I < 1, page_size < 1, page_size % (I * P) != 0, or a null pointer with n > 0. n = 0 enqueues
+ * nothing.
  */
 int32_t cp_slot_map(const int64_t* logical_slot, int64_t n, int32_t page_size, int32_t num_partners,
-                    int32_t* partner_out, int64_t* phys_out, hipStream_t stream);
+                    int32_t interleave, int32_t* partner_out, int64_t* phys_out, hipStream_t stream);
 
 /*
  * cp_slot_map_rank: the per-rank write view. Rank `rank` writes a token it owns at its physical slot and every other
@@ -85,7 +93,8 @@ int32_t cp_slot_map(const int64_t* logical_slot, int64_t n, int32_t page_size, i
  * EINVAL: as cp_slot_map, plus rank outside [0, P) or sink_slot < 0.
  */
 int32_t cp_slot_map_rank(const int64_t* logical_slot, int64_t n, int32_t page_size, int32_t num_partners,
-                         int32_t rank, int64_t sink_slot, int64_t* write_slot_out, hipStream_t stream);
+                         int32_t interleave, int32_t rank, int64_t sink_slot, int64_t* write_slot_out,
+                         hipStream_t stream);
 
 /*
  * cp_kv_write: fused slot map + write of K (and V) rows into the stripe pools, for stripes
@@ -99,17 +108,19 @@ int32_t cp_slot_map_rank(const int64_t* logical_slot, int64_t n, int32_t page_si
  *   k_src         device [n, num_kv_heads, head_dim] (token stride src_stride_token, head stride src_stride_head).
  *   v_src         device [n, num_kv_heads, head_dim_v] with the same strides, or NULL (MLA: the latent row is K).
  *   pools         layout of cp_paged_args (element (r, page, slot, g, d) at pool + r*kv_stride_stripe + ...).
+ *   interleave    I >= 1: the placement of cp_slot_map (I = 1: partner s mod P at floor(s / P)).
  *   sink_slot     >= 0: stripes in range that do not own a token write it to this physical slot (per-rank view);
  *                 < 0: only the owner writes (all stripes resident on one device).
  * A token whose page id falls outside [0, num_pages) is not written. Tokens sharing a destination race (last wins).
- * EINVAL: bad geometry, stripe range, null pointers, negative sizes or strides, sink_slot >= num_pages * page_size / P.
+ * EINVAL: bad geometry (as cp_slot_map), stripe range, null pointers, negative sizes or strides,
+ * sink_slot >= num_pages * page_size / P.
  */
 int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const void* k_src, const void* v_src,
                     int64_t src_stride_token, int64_t src_stride_head, int32_t dtype, int32_t num_kv_heads,
                     int32_t head_dim, int32_t head_dim_v, void* k_pool, void* v_pool, int64_t kv_stride_stripe,
                     int64_t kv_stride_page, int64_t kv_stride_slot, int64_t kv_stride_head, int32_t page_size,
-                    int32_t num_partners, int32_t num_pages, int32_t stripe_begin, int32_t stripe_count,
-                    int64_t sink_slot, hipStream_t stream);
+                    int32_t num_partners, int32_t interleave, int32_t num_pages, int32_t stripe_begin,
+                    int32_t stripe_count, int64_t sink_slot, hipStream_t stream);
 
 /*
  * Arguments of cp_paged_attn_partial.
@@ -146,6 +157,8 @@ typedef struct cp_paged_args {
     int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
     int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
     int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */
+    int32_t interleave;       /* KV-cache interleave size I (0 or 1: none); the placement of cp_slot_map; I * P must
+                                 divide page_size */
     const int32_t* q_row_start;  /* device int32 [num_rows + 1], non-decreasing, q_row_start[num_rows] <= num_tokens */
     const int32_t* ctx_len;      /* device int32 [num_rows]: context tokens of row b in the pool (all stripes) */
     const int32_t* block_table;  /* device int32 [num_rows, bt_stride]: logical page ids */
@@ -175,8 +188,9 @@ typedef struct cp_paged_args {
  * compare view, FlashAttentionImpl._forward_with_dcp.
  *
  * For every real query token t of row b, head h and stripe r: the keys are the context positions p < ctx_len[b] with
- * p mod P == r (the slots partner r holds); local token i of stripe r is position i*P + r, found at page
- * block_table[b][i / (page_size/P)], slot i % (page_size/P) of r's pool. Every query token of a row sees the whole
+ * floor(p / I) mod P == r (p mod P == r without interleave: the slots partner r holds); local token i of stripe r is
+ * position floor(i / I) * I * P + r * I + i mod I (i*P + r for I = 1), found at page block_table[b][i / (page_size/P)],
+ * slot i % (page_size/P) of r's pool, for every I. Every query token of a row sees the whole
  * context (no mask). Rows with ctx_len[b] <= r give (0, -inf). Padding tokens get out = 0 and lse = -inf and their
  * queries are not read.
  *
@@ -188,7 +202,7 @@ typedef struct cp_paged_args {
  * the bit whatever else the call holds (e.g. one stripe alone equals that stripe of an all-stripes call), at some cost
  * in speed when context lengths vary widely.
  *
- * EINVAL: a null args/pointer, unknown flag bits, Hq % Hkv != 0, page_size % P != 0, a stripe range outside [0, P), negative sizes or
+ * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
  * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
  * (128, 128); MLA bf16 with (576, 512).
@@ -283,15 +297,16 @@ int32_t cp_lse_merge(const cp_merge_args* args, hipStream_t stream);
 /*
  * cp_debug_gather_stripe (test support): copy stripe r's keys of one row, in local order, into a dense buffer, through
  * the same device addressing function the attention kernels use, so page addressing can be checked bit for bit.
- *   dst (i, g, d) at dst + (i*num_kv_heads + g)*head_dim + d for i < ceil((ctx_len - r) / P), same dtype as the pool.
+ *   dst (i, g, d) at dst + (i*num_kv_heads + g)*head_dim + d for i below stripe r's length (ceil((ctx_len - r) / P)
+ *   for I = 1), same dtype as the pool.
  *   block_table_row: device int32 [>= ceil(ctx_len / page_size)].
  * EINVAL: bad geometry, r outside [0, P), null pointers, negative sizes.
  */
 int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe, int64_t kv_stride_page,
                                int64_t kv_stride_slot, int64_t kv_stride_head, int32_t num_pages,
                                const int32_t* block_table_row, int32_t ctx_len, int32_t page_size,
-                               int32_t num_partners, int32_t r, int32_t num_kv_heads, int32_t head_dim, void* dst,
-                               hipStream_t stream);
+                               int32_t num_partners, int32_t interleave, int32_t r, int32_t num_kv_heads,
+                               int32_t head_dim, void* dst, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -50,7 +50,7 @@ def row_oracle(wl, b, device):
     k, v = rv.k_ctx.cpu(), rv.v_ctx.cpu()
     kn = rv.k_new.cpu() if rv.k_new is not None else None
     vn = rv.v_new.cpu() if rv.v_new is not None else None
-    parts, merged = oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn)
+    parts, merged = oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn, interleave=wl.interleave)
     full = oracle.row_attention(q, k, v, wl.scale, kn, vn)
     return parts, merged, full
 

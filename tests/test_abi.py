@@ -51,14 +51,19 @@ def _err(lib):
 
 
 def test_slot_map_refusals(lib):
-    assert lib.cp_slot_map(None, 4, 16, 3, None, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, 4, 16, 3, 1, None, None, None) == _lib.CPATTN_EINVAL
     assert "divide" in _err(lib)
-    assert lib.cp_slot_map(None, 4, 16, 0, None, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_slot_map(None, -1, 16, 4, None, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_slot_map(None, 4, 16, 4, None, None, None) == _lib.CPATTN_EINVAL   # null pointers
-    assert lib.cp_slot_map(None, 0, 16, 4, None, None, None) == _lib.CPATTN_OK      # nothing to do
-    assert lib.cp_slot_map_rank(None, 4, 16, 4, 4, 0, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_slot_map_rank(None, 4, 16, 4, 1, -2, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, 4, 16, 0, 1, None, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, -1, 16, 4, 1, None, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map(None, 4, 16, 4, 1, None, None, None) == _lib.CPATTN_EINVAL   # null pointers
+    assert lib.cp_slot_map(None, 0, 16, 4, 1, None, None, None) == _lib.CPATTN_OK      # nothing to do
+    assert lib.cp_slot_map(None, 0, 16, 4, 0, None, None, None) == _lib.CPATTN_EINVAL  # interleave < 1
+    assert lib.cp_slot_map(None, 0, 16, 4, 8, None, None, None) == _lib.CPATTN_EINVAL  # I * P does not divide 16
+    assert "interleave" in _err(lib)
+    assert lib.cp_slot_map(None, 0, 16, 4, 4, None, None, None) == _lib.CPATTN_OK      # I * P = 16
+    assert lib.cp_slot_map_rank(None, 4, 16, 4, 1, 4, 0, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map_rank(None, 4, 16, 4, 1, 1, -2, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_slot_map_rank(None, 0, 16, 2, 3, 1, 0, None, None) == _lib.CPATTN_EINVAL   # I * P = 6
 
 
 def _paged(**kw):
@@ -91,6 +96,8 @@ def _paged(**kw):
     (dict(kv_stride_page=-8), _lib.CPATTN_EINVAL),
     (dict(flags=2), _lib.CPATTN_EINVAL),
     (dict(flags=-1), _lib.CPATTN_EINVAL),
+    (dict(interleave=-1), _lib.CPATTN_EINVAL),
+    (dict(interleave=8), _lib.CPATTN_EINVAL),          # I * P = 32 does not divide page_size 16
 ])
 def test_paged_refusals(lib, bad, code):
     a = _paged(**bad)
@@ -159,15 +166,21 @@ def test_merge_refusals(lib):
 
 
 def test_kv_write_refusals(lib):
-    args = [None, 4, None, None, 0, 0, 1, 8, 128, 128, None, None, 0, 0, 0, 0, 16, 4, 10, 0, 4, -1, None]
+    args = [None, 4, None, None, 0, 0, 1, 8, 128, 128, None, None, 0, 0, 0, 0, 16, 4, 1, 10, 0, 4, -1, None]
     bad = list(args)
     bad[17] = 3                                                               # P does not divide page_size
     assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
     bad = list(args)
-    bad[20] = 5                                                               # stripe range past P
+    bad[18] = 8                                                               # I * P does not divide page_size
     assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
     bad = list(args)
-    bad[21] = 10 * 4                                                          # sink outside the pool
+    bad[18] = 0                                                               # interleave < 1
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
+    bad = list(args)
+    bad[21] = 5                                                               # stripe range past P
+    assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
+    bad = list(args)
+    bad[22] = 10 * 4                                                          # sink outside the pool
     assert lib.cp_kv_write(*bad) == _lib.CPATTN_EINVAL
     assert lib.cp_kv_write(*args) == _lib.CPATTN_EINVAL                      # null pointers
     bad = list(args)
@@ -176,6 +189,7 @@ def test_kv_write_refusals(lib):
 
 
 def test_debug_gather_refusals(lib):
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 4, 1, 8, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 8, None, None) == _lib.CPATTN_OK
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 1, 4, 1, 8, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 1, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 8, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 1, 8, None, None) == _lib.CPATTN_OK

@@ -27,6 +27,82 @@ def test_slot_map_bit_exact(page_size, P):
         assert np.array_equal(w.cpu().numpy(), oracle.slot_map_rank(s, page_size, P, rank, 3))
 
 
+@pytest.mark.parametrize("page_size,P,I", [(16, 4, 2), (16, 4, 4), (16, 2, 8), (64, 4, 16), (12, 3, 2), (16, 1, 16)])
+def test_interleaved_slot_map_bit_exact(page_size, P, I):
+    say(f"slot_map page_size={page_size} P={P} interleave={I}")
+    rng = np.random.default_rng(page_size * 37 + P * 5 + I)
+    s = np.concatenate([rng.integers(-5, 1 << 40, size=5000), np.arange(-3, 300), [0, (1 << 62) + 7]])
+    partner, phys = api.slot_map(torch.from_numpy(s).to(DEV), page_size, P, interleave=I)
+    rp, rq = oracle.slot_map(s, page_size, P, I)
+    assert np.array_equal(partner.cpu().numpy().astype(np.int64), rp)
+    assert np.array_equal(phys.cpu().numpy(), rq)
+    for rank in range(P):
+        w = api.slot_map_rank(torch.from_numpy(s).to(DEV), page_size, P, rank, 3, interleave=I)
+        assert np.array_equal(w.cpu().numpy(), oracle.slot_map_rank(s, page_size, P, rank, 3, I))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(interleave=4)),
+    ("llama8b", dict(batch=3, ctx_lengths=[1, 37, 301], interleave=2)),
+    ("llama8b", dict(batch=3, ctx_lengths=[5, 64, 333], interleave=4)),
+    ("mla", dict(batch=2, ctx_lengths=[5, 200], interleave=8)),
+], ids=["tiny-i4", "llama8b-i2", "llama8b-i4", "mla-i8"])
+def test_interleaved_write_path_and_page_addressing_bit_exact(name, kw):
+    """With interleave I, kv_write places every token by the interleaved rule and the kernels' addressing reads
+    stripe r back as the positions t with floor(t / I) mod P == r, in order."""
+    wl = workloads.make(name, **kw)
+    I = wl.interleave
+    say(f"interleaved write path {name} I={I}")
+    batch = pool.build_batch(wl, DEV)
+    P, ps = wl.partners, wl.page_size
+    for b in range(wl.batch):
+        rv = workloads.row_values(wl, b, DEV)
+        c = int(wl.ctx_len[b])
+        for r in range(P):
+            got = api.debug_gather_stripe(batch.k_pool, batch.block_table[b], c, ps, P, r, kind=wl.kind,
+                                          interleave=I)
+            idx = torch.from_numpy(oracle.stripe_positions(c, P, r, I)).to(DEV)
+            want = rv.k_ctx[idx]
+            assert got.shape == want.shape
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32))
+    rows = [workloads.row_values(wl, b, DEV).k_ctx.cpu().double().numpy().reshape(int(wl.ctx_len[b]), -1)
+            for b in range(wl.batch)]
+    ref = oracle.place_logical_rows(rows, wl.block_table, wl.ctx_len, ps, P, wl.num_pages, interleave=I)
+    pp = ps // P
+    kp = batch.k_pool.double().cpu().numpy()
+    for r in range(P):
+        got = kp[r].reshape(wl.num_pages * pp, -1)
+        assert np.array_equal(np.isnan(got), np.isnan(ref[r]))
+        fin = ~np.isnan(ref[r])
+        assert np.array_equal(got[fin], ref[r][fin])
+
+
+INTERLEAVED = [
+    ("tiny", dict(interleave=8)),
+    ("llama8b", dict(batch=5, ctx_lengths=[1, 9, 255, 1031, 4100], interleave=2)),
+    ("llama8b", dict(batch=4, ctx_lengths=[3, 17, 517, 2049], interleave=4)),
+    ("longctx", dict(batch=3, ctx_lengths=[5, 100, 3001], interleave=2)),
+    ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000], interleave=16)),
+    ("mixed", dict(batch=6, new_lengths=[1, 1, 5, 33, 1, 70], ctx_lengths=[0, 19, 0, 300, 1000, 2100], pad_rows=2,
+                   interleave=4)),
+]
+
+
+@pytest.mark.parametrize("fixed_splits", [False, True], ids=["balanced", "fixed"])
+@pytest.mark.parametrize("name,kw", INTERLEAVED, ids=[f"{n}-i{k['interleave']}" for n, k in INTERLEAVED])
+def test_interleaved_step_parity(name, kw, fixed_splits):
+    """Partials, own-token partial and merge of pools written with a KV-cache interleave size, against the oracle."""
+    wl = workloads.make(name, **kw)
+    say(f"interleaved step {name} I={wl.interleave} fixed_splits={fixed_splits} ctx={list(wl.ctx_len)}")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch, fixed_splits=fixed_splits)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
 def test_slot_map_empty_and_errors():
     p, q = api.slot_map(torch.empty(0, dtype=torch.int64, device=DEV), 16, 4)
     assert p.numel() == 0 and q.numel() == 0
@@ -280,6 +356,21 @@ def test_empty_batch_and_empty_context():
 
 # ------------------------------------------------------------------------- full sizes, sampled rows
 FULL = [("tiny", None), ("llama8b", 6), ("longctx", 4), ("mla", 3), ("mixed", 5)]
+
+
+def test_full_size_interleaved_llama8b_sampled_rows():
+    """The llama8b workload written with interleave 4 (runs of 4 slots, one physical page per run at page 16, P 4):
+    sampled rows against the oracle at full size."""
+    wl = workloads.make("llama8b", interleave=4)
+    batch = pool.build_batch(wl, DEV, fill=0.0)
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    order = np.argsort(wl.ctx_len)
+    rows = sorted({int(order[0]), int(order[-1]), 7, 30})
+    w = compare_rows(wl, batch, res, rows, DEV, check_partials=True)
+    say(f"  rows {rows} worst {w}")
+    del batch, res
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name,nsample", FULL, ids=[f[0] for f in FULL])

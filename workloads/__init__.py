@@ -55,6 +55,7 @@ class Workload:
     block_table: np.ndarray   # int32 [B, max_pages]: logical page ids, 0 = sink
     num_pages: int            # pages in each stripe's pool (page ids are logical: same range for every stripe)
     pad_rows: int = 0         # extra padding rows (zero tokens, zero context) appended after the real rows
+    interleave: int = 1       # KV-cache interleave size I of the pool (runs of I slots per partner)
     notes: list = field(default_factory=list)
 
     @property
@@ -126,12 +127,13 @@ def _block_tables(rng, tokens_per_row, page_size, spare_frac=0.02, min_spare=2, 
 
 def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_range=None,
          ctx_lengths=None, new_lengths=None, partners: int | None = None, page_size: int | None = None,
-         bucket: int | None = None, pad_rows: int = 0, bt_width: int | None = None) -> Workload:
+         bucket: int | None = None, pad_rows: int = 0, bt_width: int | None = None, interleave: int = 1) -> Workload:
     """Build workload ``name`` (one of :data:`CONFIG_NAMES`), optionally shrunk for parity tests.
 
     ``seed`` defaults to ``1000 + k`` for the k-th config (1-based). ``batch``/``ctx_range``/``ctx_lengths``/
     ``new_lengths`` override the row count and the length distribution while keeping head shapes, dtype, page size
-    and P; ``partners``/``page_size`` override P and the logical page size.
+    and P; ``partners``/``page_size`` override P and the logical page size; ``interleave`` sets the pool's KV-cache
+    interleave size (1 = the plain slot rule).
     """
     if name not in CONFIG_NAMES:
         raise ValueError(f"unknown workload {name!r}; expected one of {CONFIG_NAMES}")
@@ -207,7 +209,7 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
         notes.append(f"{pad_rows} padding rows (no tokens, no context, block table on the sink)")
     return Workload(name=name, seed=seed, ctx_len=ctx.astype(np.int32), new_len=new.astype(np.int32),
                     bucket=int(bucket), block_table=bt, num_pages=int(num_pages), pad_rows=int(pad_rows),
-                    notes=notes, **base)
+                    interleave=int(interleave), notes=notes, **base)
 
 
 def row_values(wl: Workload, row: int, device="cpu") -> RowValues:
