@@ -379,3 +379,26 @@ def check_interleave_stripe_partial(stripe_partial, gather_stripe, place_logical
             if np.max(np.abs(o - ref_o)) > 1e-13 or np.max(np.abs(l - ref_l)) > 1e-13:
                 fails.append(f"stripe {r} (page_size {page_size}, P {P}, I {I}) does not attend its pool's keys")
     return fails
+
+
+# ------------------------------------------------------------------------------------------------------ fp8
+def check_e4m3(e4m3_value, dequantize):
+    """Code values against the hand-decoded table and torch's float8_e4m3fn (a library routine) for all 256 codes;
+    dequantization is code value times descale."""
+    import torch
+    fails = []
+    for row in read_golden("fp8_e4m3.txt"):
+        code, val = row.split()
+        got, want = e4m3_value(int(code, 16)), float(val)
+        if not ((math.isnan(got) and math.isnan(want)) or (got == want and math.copysign(1, got) == math.copysign(1, want))):
+            fails.append(f"code {code}: {got} != {want}")
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([e4m3_value(c) for c in range(256)])
+    if not np.array_equal(np.isnan(mine), np.isnan(lib)) or not np.array_equal(mine[~np.isnan(mine)], lib[~np.isnan(lib)]):
+        fails.append("code values differ from torch.float8_e4m3fn")
+    codes = np.array([[0x38, 0x40], [0xb8, 0x01]])
+    dq = dequantize(codes, 0.37)
+    want = np.array([[0.37, 0.74], [-0.37, 0.37 * 2.0 ** -9]])
+    if not np.allclose(dq, want, rtol=0, atol=1e-15):
+        fails.append(f"dequantize is not code value times descale: {dq}")
+    return fails

@@ -192,3 +192,29 @@ def test_interleave_mistakes_are_caught():
     assert pins.check_interleave_stripes(S.stripe_positions, _stripe_len_interleave_ignored)
     assert pins.check_interleave_stripe_partial(_stripe_partial_interleave_ignored, oracle.gather_stripe,
                                                 oracle.place_logical_rows, oracle.gqa_attention)
+
+
+def _e4m3_bias_8(code):
+    v = oracle.e4m3_value(code)
+    return v / 2.0 if np.isfinite(v) else v
+
+
+def _e4m3_no_subnormals(code):
+    return 0.0 if (code & 0x78) == 0 else oracle.e4m3_value(code)
+
+
+def _e4m3_fnuz_nan(code):
+    return float("nan") if code == 0x80 else oracle.e4m3_value(code) if code not in (0x7f, 0xff) else 480.0
+
+
+def _dequant_inverse(codes, descale):
+    from oracle import quant
+    return quant.dequantize_e4m3(codes, 1.0) / descale
+
+
+def test_fp8_mistakes_are_caught():
+    from oracle import quant
+    assert pins.check_e4m3(_e4m3_bias_8, quant.dequantize_e4m3)
+    assert pins.check_e4m3(_e4m3_no_subnormals, quant.dequantize_e4m3)
+    assert pins.check_e4m3(_e4m3_fnuz_nan, quant.dequantize_e4m3)
+    assert pins.check_e4m3(oracle.e4m3_value, _dequant_inverse)

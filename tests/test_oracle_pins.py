@@ -214,3 +214,7 @@ def test_interleaved_placement_is_pinned():
     assert pins.check_interleave_stripes(oracle.stripe_positions, oracle.stripe_len) == []
     assert pins.check_interleave_stripe_partial(oracle.stripe_partial, oracle.gather_stripe, oracle.place_logical_rows,
                                                 oracle.gqa_attention) == []
+
+
+def test_fp8_codes_are_pinned():
+    assert pins.check_e4m3(oracle.e4m3_value, oracle.dequantize_e4m3) == []
