@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpattn.so")
 
 CPATTN_OK, CPATTN_EINVAL, CPATTN_EUNSUPPORTED, CPATTN_ELAUNCH = 0, 1, 2, 3
-CPATTN_F32, CPATTN_BF16 = 0, 1
+CPATTN_F32, CPATTN_BF16, CPATTN_FP8_E4M3 = 0, 1, 2
+CPATTN_KV_SAME, CPATTN_KV_FP8_E4M3 = 0, 1
 CPATTN_GQA, CPATTN_MLA = 0, 1
 MAX_PARTIALS = 17
 CPATTN_FLAG_FIXED_SPLITS = 1
@@ -27,7 +28,8 @@ class PagedArgs(C.Structure):
         ("stripe_begin", _i32), ("stripe_count", _i32), ("page_size", _i32), ("num_pages", _i32),
         ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32), ("head_dim_v", _i32),
         ("scale", C.c_float), ("max_ctx_len", _i32), ("max_row_tokens", _i32), ("max_pages", _i32),
-        ("flags", _i32), ("interleave", _i32),
+        ("flags", _i32), ("interleave", _i32), ("kv_format", _i32), ("k_descale", C.c_float),
+        ("v_descale", C.c_float),
         ("q_row_start", _p), ("ctx_len", _p), ("block_table", _p), ("bt_stride", _i64),
         ("q", _p), ("q_stride_token", _i64), ("q_stride_head", _i64),
         ("k_pool", _p), ("v_pool", _p),

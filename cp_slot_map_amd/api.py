@@ -39,7 +39,9 @@ def _dtype_code(dt):
         return CPATTN_F32
     if dt == torch.bfloat16:
         return CPATTN_BF16
-    raise TypeError(f"unsupported dtype {dt}; expected float32 or bfloat16")
+    if dt == torch.float8_e4m3fn:
+        return _lib.CPATTN_FP8_E4M3
+    raise TypeError(f"unsupported dtype {dt}; expected float32, bfloat16 or float8_e4m3fn (pools and rows only)")
 
 
 def _need_cuda(*ts):
@@ -115,14 +117,18 @@ def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partner
 
 def _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale, kind,
                 stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens, fixed_splits=False,
-                interleave=1):
+                interleave=1, k_descale=1.0, v_descale=1.0):
     a = PagedArgs()
     a.flags = _lib.CPATTN_FLAG_FIXED_SPLITS if fixed_splits else 0
     a.interleave = int(interleave)
     a.kind = CPATTN_MLA if kind == "mla" else CPATTN_GQA
     a.dtype = _dtype_code(q.dtype)
-    if k_pool.dtype != q.dtype:
-        raise TypeError("q and the pools must share a dtype")
+    if k_pool.dtype == torch.float8_e4m3fn:
+        # fp8 pools: codes dequantized with the per-tensor descales
+        a.kv_format = _lib.CPATTN_KV_FP8_E4M3
+        a.k_descale, a.v_descale = float(k_descale), float(v_descale)
+    elif k_pool.dtype != q.dtype:
+        raise TypeError("q and the pools must share a dtype (or the pools hold float8_e4m3fn codes)")
     a.num_rows = ctx_len.numel()
     a.num_tokens = num_tokens
     a.num_partners = int(partners)
@@ -187,13 +193,13 @@ def _check_int32_dev(*ts):
 
 def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                               kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens,
-                              fixed_splits=False, interleave=1):
+                              fixed_splits=False, interleave=1, k_descale=1.0, v_descale=1.0):
     lib = _lib_handle()
     sc = int(partners) - stripe_begin if stripe_count is None else stripe_count
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
                     max_row_tokens=max_row_tokens, out=None, lse=None, num_tokens=q.shape[0],
-                    fixed_splits=fixed_splits, interleave=interleave)
+                    fixed_splits=fixed_splits, interleave=interleave, k_descale=k_descale, v_descale=v_descale)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     return int(n.value)
@@ -201,13 +207,15 @@ def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_tab
 
 def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                        kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len=None, max_row_tokens=None,
-                       out=None, lse=None, workspace=None, stream=None, fixed_splits=False, interleave=1):
+                       out=None, lse=None, workspace=None, stream=None, fixed_splits=False, interleave=1,
+                       k_descale=1.0, v_descale=1.0):
     """Per-stripe partials (out [S, T, Hq, Dv] fp32, lse [S, T, Hq] fp32) of attention over the striped pool.
 
     q [T, Hq, D]; q_row_start int32 [B + 1]; ctx_len int32 [B]; block_table int32 [B, max_pages]. ``max_ctx_len``
     and ``max_row_tokens`` are host upper bounds (read from the device with a sync when omitted). ``fixed_splits``
     makes each row's result independent, to the bit, of the rest of the call (CPATTN_FLAG_FIXED_SPLITS).
     ``interleave`` is the KV-cache interleave size the pool was written with (runs of that many slots per partner).
+    float8_e4m3fn pools hold fp8 codes; ``k_descale``/``v_descale`` are their per-tensor descales.
     """
     lib = _lib_handle()
     _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
@@ -232,7 +240,7 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
                     max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits,
-                    interleave=interleave)
+                    interleave=interleave, k_descale=k_descale, v_descale=v_descale)
     n = C.c_int64(0)
     _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
     if n.value > 0:

@@ -43,6 +43,15 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
         return fail(CPATTN_EINVAL, "negative size");
     if (a.num_partners < 1 || a.num_partners > 16)
         return fail(CPATTN_EINVAL, "num_partners = %d outside [1, 16]", a.num_partners);
+    if (a.kv_format != CPATTN_KV_SAME && a.kv_format != CPATTN_KV_FP8_E4M3)
+        return fail(CPATTN_EINVAL, "kv_format = %d unknown", a.kv_format);
+    if (a.kv_format == CPATTN_KV_FP8_E4M3) {
+        if (a.dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "fp8 pools are read with bf16 queries (dtype = %d)", a.dtype);
+        if (!(a.k_descale > 0.f && a.k_descale < INFINITY) || !(a.v_descale > 0.f && a.v_descale < INFINITY))
+            return fail(CPATTN_EINVAL, "fp8 descales must be finite and positive (k %g, v %g)", double(a.k_descale),
+                        double(a.v_descale));
+        if (a.kind == CPATTN_MLA) return fail(CPATTN_EUNSUPPORTED, "MLA over fp8 pools is not built");
+    }
     if (a.interleave < 0 || a.interleave > 65536) return fail(CPATTN_EINVAL, "interleave = %d outside [0, 65536]", a.interleave);
     const int32_t ilv = interleave_of(a);
     if (a.page_size < 1 || a.page_size % (a.num_partners * ilv))

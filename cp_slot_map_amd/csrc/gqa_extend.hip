@@ -533,6 +533,7 @@ int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
 
 bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kD) return false;
+    if (a.kv_format != CPATTN_KV_SAME) return false;
     if (!(a.scale > 0.f && a.scale < INFINITY)) return false;   // the softmax tracks the max of unscaled scores
     const int32_t G = a.num_q_heads / a.num_kv_heads;
     if (kBlockRows % G != 0) return false;

@@ -29,9 +29,11 @@ __device__ __forceinline__ void copy_row(uint8_t* dst, const uint8_t* src, int32
     if ((bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15) == 0) {
         for (int32_t o = lane * 16; o < bytes; o += 64 * 16)
             *reinterpret_cast<u32x4_t*>(dst + o) = *reinterpret_cast<const u32x4_t*>(src + o);
-    } else {
+    } else if ((bytes & 1) == 0 && ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 1) == 0) {
         for (int32_t o = lane * 2; o < bytes; o += 64 * 2)
             *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
+    } else {
+        for (int32_t o = lane; o < bytes; o += 64) dst[o] = src[o];
     }
 }
 
@@ -79,7 +81,8 @@ extern "C" int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const voi
     if (stripe_count < 1 || stripe_begin < 0 || stripe_begin + stripe_count > num_partners)
         return fail(CPATTN_EINVAL, "stripes [%d, %d) outside [0, %d)", stripe_begin, stripe_begin + stripe_count,
                     num_partners);
-    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype = %d unknown", dtype);
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16 && dtype != CPATTN_FP8_E4M3)
+        return fail(CPATTN_EINVAL, "dtype = %d unknown", dtype);
     if (num_kv_heads < 1 || head_dim < 1 || head_dim_v < 0 || num_pages < 1)
         return fail(CPATTN_EINVAL, "bad size (Hkv=%d, D=%d, Dv=%d, pages=%d)", num_kv_heads, head_dim, head_dim_v,
                     num_pages);
@@ -91,7 +94,7 @@ extern "C" int32_t cp_kv_write(const int64_t* logical_slot, int64_t n, const voi
         return fail(CPATTN_EINVAL, "sink_slot = %lld outside the pool", (long long)sink_slot);
     if (n == 0) return CPATTN_OK;
     if (!logical_slot || !k_src || !k_pool || (v_src && !v_pool)) return fail(CPATTN_EINVAL, "null pointer");
-    const int64_t el = dtype == CPATTN_F32 ? 4 : 2;
+    const int64_t el = dtype == CPATTN_F32 ? 4 : dtype == CPATTN_BF16 ? 2 : 1;   // fp8 codes are copied as bytes
     KvWriteParams p{};
     p.slot = logical_slot;
     p.k_src = static_cast<const uint8_t*>(k_src);

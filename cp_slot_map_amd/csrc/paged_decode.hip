@@ -912,6 +912,7 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
 
 bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != 128 || a.head_dim_v != 128) return false;
+    if (a.kv_format != CPATTN_KV_SAME) return false;
     if (geo.pp_shift < 0 || geo.pp > 256) return false;
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool) || !al16(a.out)) return false;

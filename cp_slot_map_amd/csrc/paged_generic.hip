@@ -27,10 +27,12 @@ struct GenericParams {
     float* lse;
     int64_t l_ss, l_st;
     int32_t B, T, P, stripe_begin, Hq, Hkv, G, max_pages, page_size, max_row_tokens;
-    float scale_log2;
+    float scale_log2;   // softmax scale (times the key descale for fp8 pools) in log2 units
+    float v_scale;      // value descale of fp8 pools, else 1
 };
 
-template <typename T, int NQ, int NV, int R>
+// T: element type of q; TKV: element type of the pools (T itself, or uint8_t for fp8 codes).
+template <typename T, typename TKV, int NQ, int NV, int R>
 __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p) {
     const int lane = threadIdx.x;
     const int rb = blockIdx.x;
@@ -49,8 +51,8 @@ __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p
     const int32_t Lr = stripe_length(L, r, p.P, p.geo.interleave);
     const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
     const T* Q = static_cast<const T*>(p.q);
-    const T* K = static_cast<const T*>(p.kp);
-    const T* V = static_cast<const T*>(p.vp);
+    const TKV* K = static_cast<const TKV*>(p.kp);
+    const TKV* V = static_cast<const TKV*>(p.vp);
 
     float q[R][NQ];
     int32_t tok[R], head[R];
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p
         float* o = p.out + s * p.o_ss + int64_t(tok[rr]) * p.o_st + int64_t(head[rr]) * p.o_sh;
         const float inv = l[rr] > 0.f ? 1.0f / l[rr] : 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) o[lane + 64 * i] = acc[rr][i] * inv;
+        for (int i = 0; i < NV; ++i) o[lane + 64 * i] = acc[rr][i] * inv * p.v_scale;
         if (lane == 0)
             p.lse[s * p.l_ss + int64_t(tok[rr]) * p.l_st + head[rr]] =
                 l[rr] > 0.f ? (m[rr] + log2f(l[rr])) * kLn2 : neg_inf();
@@ -144,9 +146,9 @@ int32_t launch_pad_partials(const cp_paged_args& a, hipStream_t stream) {
                       a.head_dim_v, stream);
 }
 
-template <typename T, int NQ, int NV, int R>
+template <typename T, typename TKV, int NQ, int NV, int R>
 static void launch_generic_t(const GenericParams& p, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((paged_generic_kernel<T, NQ, NV, R>), grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((paged_generic_kernel<T, TKV, NQ, NV, R>), grid, dim3(64), 0, stream, p);
 }
 
 int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
@@ -178,7 +180,9 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
     p.max_pages = a.max_pages;
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
-    p.scale_log2 = a.scale * kLog2e;
+    const bool fp8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    p.scale_log2 = a.scale * (fp8 ? a.k_descale : 1.0f) * kLog2e;
+    p.v_scale = fp8 ? a.v_descale : 1.0f;
 
     if (int32_t st = launch_pad_partials(a, stream)) return st;
     if (a.num_rows == 0 || a.max_row_tokens == 0) return CPATTN_OK;
@@ -187,21 +191,25 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
     if (a.kind == CPATTN_MLA) {
         constexpr int R = 8;
         dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows), uint32_t(a.stripe_count));
-        launch_generic_t<uint16_t, 9, 8, R>(p, grid, stream);
+        launch_generic_t<uint16_t, uint16_t, 9, 8, R>(p, grid, stream);
     } else if (a.head_dim == 64) {
         constexpr int R = 8;
         dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows * a.num_kv_heads), uint32_t(a.stripe_count));
         if (f32)
-            launch_generic_t<float, 1, 1, R>(p, grid, stream);
+            launch_generic_t<float, float, 1, 1, R>(p, grid, stream);
+        else if (fp8)
+            launch_generic_t<uint16_t, uint8_t, 1, 1, R>(p, grid, stream);
         else
-            launch_generic_t<uint16_t, 1, 1, R>(p, grid, stream);
+            launch_generic_t<uint16_t, uint16_t, 1, 1, R>(p, grid, stream);
     } else {
         constexpr int R = 8;
         dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows * a.num_kv_heads), uint32_t(a.stripe_count));
         if (f32)
-            launch_generic_t<float, 2, 2, R>(p, grid, stream);
+            launch_generic_t<float, float, 2, 2, R>(p, grid, stream);
+        else if (fp8)
+            launch_generic_t<uint16_t, uint8_t, 2, 2, R>(p, grid, stream);
         else
-            launch_generic_t<uint16_t, 2, 2, R>(p, grid, stream);
+            launch_generic_t<uint16_t, uint16_t, 2, 2, R>(p, grid, stream);
     }
     return check_launch("cp_paged_attn_partial (generic)");
 }
@@ -239,7 +247,8 @@ extern "C" int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int
         return fail(CPATTN_EINVAL, "negative or zero size");
     if (kv_stride_stripe < 0 || kv_stride_page < 0 || kv_stride_slot < 0 || kv_stride_head < 0)
         return fail(CPATTN_EINVAL, "negative stride");
-    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d unknown", dtype);
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16 && dtype != CPATTN_FP8_E4M3)
+        return fail(CPATTN_EINVAL, "dtype %d unknown", dtype);
     const int32_t Lr = stripe_length(ctx_len, r, num_partners, interleave);
     if (Lr == 0) return CPATTN_OK;
     if (!k_pool || !block_table_row || !dst) return fail(CPATTN_EINVAL, "cp_debug_gather_stripe: null pointer");
@@ -251,6 +260,10 @@ extern "C" int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int
         hipLaunchKernelGGL(gather_stripe_kernel<float>, grid, dim3(256), 0, stream,
                            static_cast<const float*>(k_pool), geo, block_table_row, Lr, r, num_kv_heads, head_dim,
                            static_cast<float*>(dst));
+    else if (dtype == CPATTN_FP8_E4M3)
+        hipLaunchKernelGGL(gather_stripe_kernel<uint8_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint8_t*>(k_pool), geo, block_table_row, Lr, r, num_kv_heads, head_dim,
+                           static_cast<uint8_t*>(dst));
     else
         hipLaunchKernelGGL(gather_stripe_kernel<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<const uint16_t*>(k_pool), geo, block_table_row, Lr, r, num_kv_heads, head_dim,

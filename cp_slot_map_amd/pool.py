@@ -64,24 +64,25 @@ def build_batch(wl, device="cuda", *, fill=float("nan"), layout="hnd", rows=None
     dt = wl.torch_dtype
     dev = torch.device(device)
     q_fill = fill if q_fill is None else q_fill
+    pdt = torch.float8_e4m3fn if getattr(wl, "kv_dtype", "same") == "fp8" else dt   # pool element type
     if wl.kind == "mla":
-        k_store = torch.full((P, wl.num_pages, pp, wl.head_dim), fill, dtype=dt, device=dev)
+        k_store = torch.full((P, wl.num_pages, pp, wl.head_dim), fill, dtype=pdt, device=dev)
         v_store = None
         k_pool = v_pool = k_store
     elif layout == "hnd":
-        k_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim), fill, dtype=dt, device=dev)
-        v_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim_v), fill, dtype=dt, device=dev)
+        k_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim), fill, dtype=pdt, device=dev)
+        v_store = torch.full((P, wl.num_pages, wl.num_kv_heads, pp, wl.head_dim_v), fill, dtype=pdt, device=dev)
         k_pool, v_pool = k_store.transpose(2, 3), v_store.transpose(2, 3)
     elif layout == "hnd_kv":
         # K and V blocks of one (page, kv head) side by side: [P, num_pages, Hkv, 2, pp, D]
         if wl.head_dim != wl.head_dim_v:
             raise ValueError("the paired layout needs head_dim == head_dim_v")
-        kv = torch.full((P, wl.num_pages, wl.num_kv_heads, 2, pp, wl.head_dim), fill, dtype=dt, device=dev)
+        kv = torch.full((P, wl.num_pages, wl.num_kv_heads, 2, pp, wl.head_dim), fill, dtype=pdt, device=dev)
         k_store, v_store = kv, None
         k_pool, v_pool = kv[:, :, :, 0].transpose(2, 3), kv[:, :, :, 1].transpose(2, 3)
     elif layout == "nhd":
-        k_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim), fill, dtype=dt, device=dev)
-        v_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim_v), fill, dtype=dt, device=dev)
+        k_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim), fill, dtype=pdt, device=dev)
+        v_store = torch.full((P, wl.num_pages, pp, wl.num_kv_heads, wl.head_dim_v), fill, dtype=pdt, device=dev)
         k_pool, v_pool = k_store, v_store
     else:
         raise ValueError(f"unknown layout {layout!r}")
@@ -133,7 +134,8 @@ def run_step(batch: Batch, *, out=None, lse=None, merged=None, merged_lse=None, 
                                       batch.block_table, page_size=wl.page_size, partners=wl.partners,
                                       scale=wl.scale, kind=wl.kind, max_ctx_len=batch.max_ctx_len,
                                       max_row_tokens=batch.max_row_tokens, out=out, lse=lse, workspace=workspace,
-                                      stream=stream, fixed_splits=fixed_splits, interleave=wl.interleave)
+                                      stream=stream, fixed_splits=fixed_splits, interleave=wl.interleave,
+                                      k_descale=wl.k_descale, v_descale=wl.v_descale)
     outs = [out[s] for s in range(out.shape[0])]
     lses = [lse[s] for s in range(lse.shape[0])]
     own = None
@@ -173,7 +175,8 @@ class StepPlan:
                                      batch.block_table, page_size=wl.page_size, partners=P, scale=wl.scale,
                                      kind=wl.kind, stripe_begin=0, stripe_count=P, max_ctx_len=batch.max_ctx_len,
                                      max_row_tokens=batch.max_row_tokens, out=self.out, lse=self.lse, num_tokens=T,
-                                     fixed_splits=fixed_splits, interleave=wl.interleave)
+                                     fixed_splits=fixed_splits, interleave=wl.interleave, k_descale=wl.k_descale,
+                                     v_descale=wl.v_descale)
         n = C.c_int64(0)
         _lib.check(self.lib.cp_paged_attn_workspace_size(C.byref(self.paged), C.byref(n)))
         self.workspace_bytes = int(n.value)

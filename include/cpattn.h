@@ -44,6 +44,14 @@ extern "C" {
 
 #define CPATTN_F32 0
 #define CPATTN_BF16 1
+#define CPATTN_FP8_E4M3 2   /* element type of fp8 pools and rows (cp_kv_write, cp_debug_gather_stripe): OCP 8-bit
+                               E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities) */
+
+/* cp_paged_args.kv_format: what the pools hold. The vLLM compare view "[Core] Add explicit layer parallel plans" passes
+ * per-tensor k_descale / v_descale to its attention calls; a key or value element stands for its code's value times
+ * the tensor's descale. */
+#define CPATTN_KV_SAME 0       /* pools have the element type of q (dtype) */
+#define CPATTN_KV_FP8_E4M3 1   /* pools hold CPATTN_FP8_E4M3 codes, dequantized with k_descale / v_descale */
 
 #define CPATTN_GQA 0
 #define CPATTN_MLA 1
@@ -105,6 +113,7 @@ int32_t cp_slot_map_rank(const int64_t* logical_slot, int64_t n, int32_t page_si
  * planning shows what goes wrong when a write path skips it).
  *
  *   logical_slot  device int64 [n]; < 0 = padding (written nowhere).
+ *   dtype         CPATTN_F32, CPATTN_BF16 or CPATTN_FP8_E4M3 (codes copied as bytes): element type of rows and pools.
  *   k_src         device [n, num_kv_heads, head_dim] (token stride src_stride_token, head stride src_stride_head).
  *   v_src         device [n, num_kv_heads, head_dim_v] with the same strides, or NULL (MLA: the latent row is K).
  *   pools         layout of cp_paged_args (element (r, page, slot, g, d) at pool + r*kv_stride_stripe + ...).
@@ -159,6 +168,9 @@ typedef struct cp_paged_args {
     int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */
     int32_t interleave;       /* KV-cache interleave size I (0 or 1: none); the placement of cp_slot_map; I * P must
                                  divide page_size */
+    int32_t kv_format;        /* CPATTN_KV_SAME or CPATTN_KV_FP8_E4M3 (GQA with dtype bf16 only) */
+    float k_descale;          /* fp8 pools: a key element is its code's value times k_descale (finite, > 0) */
+    float v_descale;          /* fp8 pools: a value element is its code's value times v_descale (finite, > 0) */
     const int32_t* q_row_start;  /* device int32 [num_rows + 1], non-decreasing, q_row_start[num_rows] <= num_tokens */
     const int32_t* ctx_len;      /* device int32 [num_rows]: context tokens of row b in the pool (all stripes) */
     const int32_t* block_table;  /* device int32 [num_rows, bt_stride]: logical page ids */
@@ -202,10 +214,15 @@ typedef struct cp_paged_args {
  * the bit whatever else the call holds (e.g. one stripe alone equals that stripe of an all-stripes call), at some cost
  * in speed when context lengths vary widely.
  *
- * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
+ * fp8 pools (kv_format CPATTN_KV_FP8_E4M3): every element read from the pools is decoded exactly and multiplied by
+ * its descale in fp32 (the key descale folded into the score scale, the value descale applied to the normalised
+ * output).
+ *
+ * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, an unknown kv_format, fp8 pools with dtype other
+ * than bf16 or a descale that is not finite and positive, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
  * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
- * (128, 128); MLA bf16 with (576, 512).
+ * (128, 128), bf16 queries over fp8 pools for both; MLA bf16 with (576, 512) (not over fp8 pools).
  */
 int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
 

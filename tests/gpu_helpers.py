@@ -48,6 +48,9 @@ def row_oracle(wl, b, device):
     rv = workloads.row_values(wl, b, device)
     q = rv.q.cpu()
     k, v = rv.k_ctx.cpu(), rv.v_ctx.cpu()
+    if wl.kv_dtype == "fp8":        # the pools hold E4M3 codes: what they stand for, by the oracle's own decoding
+        k = oracle.dequantize_e4m3(k.view(torch.uint8), wl.k_descale)
+        v = oracle.dequantize_e4m3(v.view(torch.uint8), wl.v_descale)
     kn = rv.k_new.cpu() if rv.k_new is not None else None
     vn = rv.v_new.cpu() if rv.v_new is not None else None
     parts, merged = oracle.row_partials(q, k, v, wl.partners, wl.scale, kn, vn, interleave=wl.interleave)

@@ -98,6 +98,12 @@ def _paged(**kw):
     (dict(flags=-1), _lib.CPATTN_EINVAL),
     (dict(interleave=-1), _lib.CPATTN_EINVAL),
     (dict(interleave=8), _lib.CPATTN_EINVAL),          # I * P = 32 does not divide page_size 16
+    (dict(kv_format=2), _lib.CPATTN_EINVAL),
+    (dict(kv_format=1, k_descale=0.5, v_descale=0.0), _lib.CPATTN_EINVAL),
+    (dict(kv_format=1, k_descale=float("inf"), v_descale=0.5), _lib.CPATTN_EINVAL),
+    (dict(kv_format=1, dtype=0, k_descale=0.5, v_descale=0.5), _lib.CPATTN_EINVAL),   # fp8 pools need bf16 queries
+    (dict(kv_format=1, kind=1, num_kv_heads=1, head_dim=576, head_dim_v=512, k_descale=0.5, v_descale=0.5),
+     _lib.CPATTN_EUNSUPPORTED),
 ])
 def test_paged_refusals(lib, bad, code):
     a = _paged(**bad)

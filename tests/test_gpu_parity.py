@@ -103,6 +103,52 @@ def test_interleaved_step_parity(name, kw, fixed_splits):
     say(f"  worst errors {w}")
 
 
+def _bits(t):
+    return t.view({torch.bfloat16: torch.int16, torch.float8_e4m3fn: torch.uint8, torch.float32: torch.int32}[t.dtype])
+
+
+FP8 = [
+    ("llama8b", dict(batch=5, ctx_lengths=[1, 9, 255, 1031, 4100], kv_dtype="fp8")),
+    ("longctx", dict(batch=3, ctx_lengths=[5, 100, 3001], kv_dtype="fp8")),
+    ("llama8b", dict(batch=3, ctx_lengths=[17, 300, 2222], kv_dtype="fp8", interleave=4)),
+    ("mixed", dict(batch=6, new_lengths=[1, 1, 5, 33, 1, 70], ctx_lengths=[0, 19, 0, 300, 1000, 2100], pad_rows=2,
+                   kv_dtype="fp8")),
+]
+
+
+def test_fp8_write_path_bit_exact():
+    """fp8 pools: kv_write copies the E4M3 codes by the slot rule and the kernels' addressing reads them back."""
+    wl = workloads.make("llama8b", batch=3, ctx_lengths=[1, 37, 301], kv_dtype="fp8", interleave=2)
+    batch = pool.build_batch(wl, DEV)
+    assert batch.k_pool.dtype == torch.float8_e4m3fn
+    P, ps = wl.partners, wl.page_size
+    for b in range(wl.batch):
+        rv = workloads.row_values(wl, b, DEV)
+        c = int(wl.ctx_len[b])
+        for r in range(P):
+            got = api.debug_gather_stripe(batch.k_pool, batch.block_table[b], c, ps, P, r, interleave=2)
+            idx = torch.from_numpy(oracle.stripe_positions(c, P, r, 2)).to(DEV)
+            assert torch.equal(_bits(got), _bits(rv.k_ctx[idx]))
+            got = api.debug_gather_stripe(batch.v_pool, batch.block_table[b], c, ps, P, r, interleave=2)
+            assert torch.equal(_bits(got), _bits(rv.v_ctx[idx]))
+
+
+@pytest.mark.parametrize("fixed_splits", [False, True], ids=["balanced", "fixed"])
+@pytest.mark.parametrize("name,kw", FP8, ids=[f"{n}-fp8{'-i' + str(k['interleave']) if 'interleave' in k else ''}"
+                                             for n, k in FP8])
+def test_fp8_step_parity(name, kw, fixed_splits):
+    """bf16 queries over fp8 pools (E4M3 codes, per-tensor descales): partials and merge against the oracle, which
+    decodes the codes itself."""
+    wl = workloads.make(name, **kw)
+    say(f"fp8 step {name} fixed_splits={fixed_splits} ctx={list(wl.ctx_len)}")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch, fixed_splits=fixed_splits)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
 def test_slot_map_empty_and_errors():
     p, q = api.slot_map(torch.empty(0, dtype=torch.int64, device=DEV), 16, 4)
     assert p.numel() == 0 and q.numel() == 0

@@ -56,6 +56,9 @@ class Workload:
     num_pages: int            # pages in each stripe's pool (page ids are logical: same range for every stripe)
     pad_rows: int = 0         # extra padding rows (zero tokens, zero context) appended after the real rows
     interleave: int = 1       # KV-cache interleave size I of the pool (runs of I slots per partner)
+    kv_dtype: str = "same"    # "same" (pools in dtype) or "fp8" (pools hold E4M3 codes with per-tensor descales)
+    k_descale: float = 1.0    # fp8 pools: a key element is its code's value times k_descale
+    v_descale: float = 1.0
     notes: list = field(default_factory=list)
 
     @property
@@ -82,7 +85,7 @@ class Workload:
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes of the context attention: every context token's K and V once."""
-        el = 4 if self.dtype == "f32" else 2
+        el = 1 if self.kv_dtype == "fp8" else 4 if self.dtype == "f32" else 2
         total = int(self.ctx_len.astype(np.int64).sum())
         if self.kind == "mla":
             return total * self.head_dim * el
@@ -127,13 +130,16 @@ def _block_tables(rng, tokens_per_row, page_size, spare_frac=0.02, min_spare=2, 
 
 def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_range=None,
          ctx_lengths=None, new_lengths=None, partners: int | None = None, page_size: int | None = None,
-         bucket: int | None = None, pad_rows: int = 0, bt_width: int | None = None, interleave: int = 1) -> Workload:
+         bucket: int | None = None, pad_rows: int = 0, bt_width: int | None = None, interleave: int = 1,
+         kv_dtype: str = "same") -> Workload:
     """Build workload ``name`` (one of :data:`CONFIG_NAMES`), optionally shrunk for parity tests.
 
     ``seed`` defaults to ``1000 + k`` for the k-th config (1-based). ``batch``/``ctx_range``/``ctx_lengths``/
     ``new_lengths`` override the row count and the length distribution while keeping head shapes, dtype, page size
     and P; ``partners``/``page_size`` override P and the logical page size; ``interleave`` sets the pool's KV-cache
-    interleave size (1 = the plain slot rule).
+    interleave size (1 = the plain slot rule); ``kv_dtype="fp8"`` (bf16 GQA workloads) stores the context K/V as E4M3
+    codes: each value is divided by its tensor's descale (0.0173 for K, 0.0291 for V: fixed, unequal, not powers of two),
+    clipped to +-448 and rounded by torch's float8_e4m3fn conversion.
     """
     if name not in CONFIG_NAMES:
         raise ValueError(f"unknown workload {name!r}; expected one of {CONFIG_NAMES}")
@@ -207,9 +213,12 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
         new = np.concatenate([new, np.zeros(pad_rows, dtype=np.int64)])
         bt = np.concatenate([bt, np.zeros((pad_rows, bt.shape[1]), dtype=np.int32)])
         notes.append(f"{pad_rows} padding rows (no tokens, no context, block table on the sink)")
+    fp8 = dict(kv_dtype="fp8", k_descale=0.0173, v_descale=0.0291) if kv_dtype == "fp8" else {}
+    if fp8 and (base["kind"] != "gqa" or base["dtype"] != "bf16"):
+        raise ValueError("fp8 pools are built for bf16 GQA workloads")
     return Workload(name=name, seed=seed, ctx_len=ctx.astype(np.int32), new_len=new.astype(np.int32),
                     bucket=int(bucket), block_table=bt, num_pages=int(num_pages), pad_rows=int(pad_rows),
-                    interleave=int(interleave), notes=notes, **base)
+                    interleave=int(interleave), notes=notes, **fp8, **base)
 
 
 def row_values(wl: Workload, row: int, device="cpu") -> RowValues:
@@ -220,10 +229,12 @@ def row_values(wl: Workload, row: int, device="cpu") -> RowValues:
     c = int(wl.ctx_len[row])
     dt = wl.torch_dtype
 
-    def draw(*shape):
+    def draw(*shape, descale=None):
         x = torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
         if wl.std != 1.0:
             x = x * wl.std
+        if descale is not None:     # fp8 pool contents: E4M3 codes of x / descale
+            return (x / descale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
         return x.to(dt)
 
     q = draw(n, wl.num_q_heads, wl.head_dim)
@@ -232,8 +243,9 @@ def row_values(wl: Workload, row: int, device="cpu") -> RowValues:
         lat_new = draw(n, 1, wl.head_dim) if wl.own_token else None
         return RowValues(q=q, k_ctx=lat, v_ctx=lat[..., :wl.head_dim_v],
                          k_new=lat_new, v_new=None if lat_new is None else lat_new[..., :wl.head_dim_v])
-    k_ctx = draw(c, wl.num_kv_heads, wl.head_dim)
-    v_ctx = draw(c, wl.num_kv_heads, wl.head_dim_v)
+    fp8 = wl.kv_dtype == "fp8"
+    k_ctx = draw(c, wl.num_kv_heads, wl.head_dim, descale=wl.k_descale if fp8 else None)
+    v_ctx = draw(c, wl.num_kv_heads, wl.head_dim_v, descale=wl.v_descale if fp8 else None)
     if wl.own_token:
         k_new = draw(n, wl.num_kv_heads, wl.head_dim)
         v_new = draw(n, wl.num_kv_heads, wl.head_dim_v)
