@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "longctx", "mla", "mixed"])
     ap.add_argument("--interleave", type=int, default=1,
                     help="KV-cache interleave size of the pool (runs of that many slots per partner; 1 = plain rule)")
+    ap.add_argument("--kv-dtype", default="same", choices=["same", "fp8"],
+                    help="pool element type: the workload's dtype, or fp8 E4M3 codes with per-tensor descales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -97,6 +99,9 @@ def cpu_baseline(wl, budget_s):
     for b in rows:
         rv = workloads.row_values(wl, int(b), "cuda")
         q, k, v = rv.q.cpu(), rv.k_ctx.cpu(), rv.v_ctx.cpu()
+        if wl.kv_dtype == "fp8":
+            k = oracle.dequantize_e4m3(k.view(torch.uint8), wl.k_descale)
+            v = oracle.dequantize_e4m3(v.view(torch.uint8), wl.v_descale)
         kn = rv.k_new.cpu() if rv.k_new is not None else None
         vn = rv.v_new.cpu() if rv.v_new is not None else None
         del rv
@@ -133,7 +138,7 @@ def main():
         copy_calibration()
         return
     torch.cuda.set_device(0)
-    wl = workloads.make(args.workload, interleave=args.interleave)
+    wl = workloads.make(args.workload, interleave=args.interleave, kv_dtype=args.kv_dtype)
     batch = pool.build_batch(wl, "cuda", fill=0.0)
     plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
@@ -206,7 +211,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "page_size": wl.page_size, "partners": wl.partners,
                    "ctx_tokens": int(wl.ctx_len.astype(np.int64).sum()), "query_tokens": qtok, "seed": wl.seed,
-                   "kv_bytes": kv_bytes, "interleave": wl.interleave},
+                   "kv_bytes": kv_bytes, "interleave": wl.interleave, "kv_dtype": wl.kv_dtype},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "query_tokens_per_s": round(qtok / (ms_per_step * 1e-3), 1),
         "kernel_ms": {"partial_avg": round(part_avg, 5), "partial_min": round(float(np.min(part_ms)), 5),

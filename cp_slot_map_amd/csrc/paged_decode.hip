@@ -30,6 +30,7 @@
 
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 namespace cpattn {
 
@@ -57,7 +58,8 @@ struct DecodeParams {
     int32_t total_items, pad_blocks, pad_tokens_per_block;
     int32_t rec_rows;
     int32_t num_tiles, nwaves;    // persistent schedule
-    float scale_log2;
+    float scale_log2;             // softmax scale (times the key descale for fp8 pools) in log2 units
+    float v_scale;                // value descale of fp8 pools, else 1 (applied where output rows are written)
 };
 
 // s_waitcnt with vmcnt = 0 and the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14],
@@ -145,6 +147,48 @@ __device__ __forceinline__ void step_load(StepData& d, const uint16_t* __restric
 #pragma unroll
     for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + sb.base[e] + lane_off);
 }
+
+// fp8 pools: the same lanes and dims, 8 one-byte E4M3 codes per lane and instruction. The codes stay packed while the
+// step is in flight (half the registers of a bf16 step) and are widened to bf16 only when the step is computed.
+struct StepData8 {
+    u32x2_t k[4];
+    u32x2_t v[4];
+};
+
+__device__ __forceinline__ void step_load(StepData8& d, const uint16_t* __restrict__ kp,
+                                          const uint16_t* __restrict__ vp, const StepBase& sb, uint32_t lane_off) {
+    const uint8_t* k8 = reinterpret_cast<const uint8_t*>(kp);
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d.k[e] = *reinterpret_cast<const u32x2_t*>(k8 + sb.base[e] + lane_off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d.v[e] = *reinterpret_cast<const u32x2_t*>(v8 + sb.base[e] + lane_off);
+}
+
+// Eight E4M3 codes (bytes 0..7) to eight bf16 in the same order. E4M3 values are exact in bf16, and the gfx950
+// conversion decodes every code exactly (measured over all 256 codes); the descales are applied in fp32 elsewhere.
+__device__ __forceinline__ u32x4_t widen_fp8(u32x2_t c) {
+    const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false);
+    const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true);
+    const auto w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false);
+    const auto w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true);
+    return (u32x4_t){__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1),
+                     __builtin_bit_cast(uint32_t, w2), __builtin_bit_cast(uint32_t, w3)};
+}
+
+__device__ __forceinline__ const StepData& widen(const StepData& d) { return d; }
+__device__ __forceinline__ StepData widen(const StepData8& d) {
+    StepData w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        w.k[e] = widen_fp8(d.k[e]);
+        w.v[e] = widen_fp8(d.v[e]);
+    }
+    return w;
+}
+
+template <bool KV8>
+using StepBuf = typename std::conditional<KV8, StepData8, StepData>::type;
 
 struct SoftmaxState {
     f32x4_t o[8];      // o[n][ii]: query row 4*(l/16)+ii, head dim 8*(l%16)+n (unnormalised)
@@ -238,8 +282,9 @@ __device__ __forceinline__ void write_row(const DecodeParams& p, int32_t s, int3
     const int32_t t = tok0 + rho / p.G;
     const int32_t h = g * p.G + rho % p.G;
     float* o = p.out + s * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * n16;
-    *reinterpret_cast<f32x4_t*>(o) = (f32x4_t){vals[0], vals[1], vals[2], vals[3]};
-    *reinterpret_cast<f32x4_t*>(o + 4) = (f32x4_t){vals[4], vals[5], vals[6], vals[7]};
+    const float c = p.v_scale;
+    *reinterpret_cast<f32x4_t*>(o) = (f32x4_t){vals[0] * c, vals[1] * c, vals[2] * c, vals[3] * c};
+    *reinterpret_cast<f32x4_t*>(o + 4) = (f32x4_t){vals[4] * c, vals[5] * c, vals[6] * c, vals[7] * c};
 }
 
 __device__ __forceinline__ void write_lse(const DecodeParams& p, int32_t s, int32_t tok0, int32_t row0, int32_t g,
@@ -250,7 +295,7 @@ __device__ __forceinline__ void write_lse(const DecodeParams& p, int32_t s, int3
     p.lse[s * p.l_ss + int64_t(t) * p.l_st + h] = l > 0.f ? (m_log2 + log2f(l)) * kLn2 : neg_inf();
 }
 
-template <int DEPTH, int PPMODE>
+template <int DEPTH, int PPMODE, bool KV8>
 __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams p) {
     __shared__ u32x4_t s_kx[256];
     const int lane = threadIdx.x;
@@ -335,7 +380,7 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
     const int64_t base_rg = int64_t(r) * p.geo.s_stripe + int64_t(g) * p.geo.s_head;
     const int32_t nsteps = (j1 - j0 + 15) >> 4;
     const int32_t last = max(nsteps - 1, 0);
-    StepData buf[DEPTH];
+    StepBuf<KV8> buf[DEPTH];
 #pragma unroll
     for (int u = 0; u < DEPTH - 1; ++u) {
         StepBase sb;
@@ -351,7 +396,7 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
                 step_bases<PPMODE>(sb, bt_row, j0 + 16 * min(k + DEPTH - 1, last), last_pidx, c4, base_rg, p.geo);
                 step_load(buf[(u + DEPTH - 1) % DEPTH], p.kp, p.vp, sb, lane_off);
             }
-            if (k < nsteps) step_compute(st, buf[u], qop, s_kx, j0 + 16 * k, j1, n16, c4, p.scale_log2);
+            if (k < nsteps) step_compute(st, widen(buf[u]), qop, s_kx, j0 + 16 * k, j1, n16, c4, p.scale_log2);
         }
     }
 
@@ -540,8 +585,8 @@ __device__ __forceinline__ ItemAddr item_addr(const DecodeParams& p, const Tile&
     return ia;
 }
 
-template <int PPMODE>
-__device__ __forceinline__ void issue_step(StepData& d, const DecodeParams& p, const ItemAddr& ia, int32_t k,
+template <int PPMODE, typename SD>
+__device__ __forceinline__ void issue_step(SD& d, const DecodeParams& p, const ItemAddr& ia, int32_t k,
                                            int32_t c4, uint32_t lane_off) {
     // Step index, last page index and block-table row are wave-uniform; the compiler cannot always prove it inside the
     // persistent loop, and then reads the page ids with vector loads, whose wait also drains the previous step's
@@ -640,7 +685,7 @@ __device__ __forceinline__ int32_t wave_exclusive_scan(int32_t v, int lane, int3
 // A value every lane holds identically, moved to a scalar register so everything derived from it stays scalar.
 __device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <int PPMODE>
+template <int PPMODE, bool KV8>
 __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeParams p) {
     __shared__ u32x4_t s_kx[256];
     __shared__ u32x4_t s_q[2][256];
@@ -691,7 +736,7 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     int32_t seg_end = int32_t(min<int64_t>(tl.n_steps, seg_begin + remaining));
     bool first_seg = true;
     int qbuf = 0;                                    // LDS query buffer of the current item
-    StepData da, db;
+    StepBuf<KV8> da, db;
     {
         bf16x8_t q0[4];
         load_query(q0, p, tl, g, n16, c4);
@@ -713,7 +758,7 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
             bf16x8_t qop[4];
             issue_step<PPMODE>(db, p, ia, k + 1, c4, lane_off);
             read_query(qop, sq, lane);
-            step_compute(st, da, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            step_compute(st, widen(da), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
             ++k;
             if (k + 1 >= seg_end) {
                 da = db;
@@ -721,7 +766,7 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
             }
             issue_step<PPMODE>(da, p, ia, k + 1, c4, lane_off);
             read_query(qop, sq, lane);
-            step_compute(st, db, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            step_compute(st, widen(db), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
             ++k;
         }
         // Last step of the segment: the next item's query and first step are issued before it is computed.
@@ -752,7 +797,7 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
         {
             bf16x8_t qop[4];
             read_query(qop, sq, lane);
-            step_compute(st, da, qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            step_compute(st, widen(da), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
         }
         if (more) {
             wait_vmem_8();
@@ -912,7 +957,6 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
 
 bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != 128 || a.head_dim_v != 128) return false;
-    if (a.kv_format != CPATTN_KV_SAME) return false;
     if (geo.pp_shift < 0 || geo.pp > 256) return false;
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool) || !al16(a.out)) return false;
@@ -933,7 +977,7 @@ int64_t decode_bf16_workspace_bytes(const cp_paged_args& a) {
 }
 
 // Resident one-wave blocks of the persistent kernel on this device (cached per device and kernel variant).
-template <int PPMODE>
+template <int PPMODE, bool KV8>
 static int32_t persistent_waves() {
     static int32_t cache[64][1] = {};
     int dev = 0;
@@ -941,7 +985,7 @@ static int32_t persistent_waves() {
     if (cache[dev][0] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_decode_persist_kernel<PPMODE>, 64, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_decode_persist_kernel<PPMODE, KV8>, 64, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 8;
@@ -989,22 +1033,30 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.pad_blocks = (a.num_tokens + 3) / 4;
     p.rec_rows = int32_t(d.rec_rows);
     p.num_tiles = int32_t(d.num_tiles);
-    p.scale_log2 = a.scale * kLog2e;
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    p.scale_log2 = a.scale * (kv8 ? a.k_descale : 1.0f) * kLog2e;
+    p.v_scale = kv8 ? a.v_descale : 1.0f;
     const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
 
     if (d.persistent) {
         p.ws_blockpref = static_cast<int32_t*>(a.workspace);
         p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + kBlockPrefBytes);
         if (d.num_tiles > 0) {
-            int32_t nw = ppmode == 2 ? persistent_waves<2>() : ppmode == 1 ? persistent_waves<1>() : persistent_waves<0>();
-            p.nwaves = nw;
-            const dim3 grid{uint32_t(nw), 1, 1};
+            auto launch = [&](auto pp, auto k8) {
+                constexpr int PP = decltype(pp)::value;
+                constexpr bool K8 = decltype(k8)::value;
+                const int32_t nw = persistent_waves<PP, K8>();
+                p.nwaves = nw;
+                hipLaunchKernelGGL((gqa_decode_persist_kernel<PP, K8>), dim3(uint32_t(nw)), dim3(64), 0, stream, p);
+            };
+            using T8 = std::true_type;
+            using F8 = std::false_type;
             if (ppmode == 2)
-                hipLaunchKernelGGL((gqa_decode_persist_kernel<2>), grid, dim3(64), 0, stream, p);
+                kv8 ? launch(std::integral_constant<int, 2>{}, T8{}) : launch(std::integral_constant<int, 2>{}, F8{});
             else if (ppmode == 1)
-                hipLaunchKernelGGL((gqa_decode_persist_kernel<1>), grid, dim3(64), 0, stream, p);
+                kv8 ? launch(std::integral_constant<int, 1>{}, T8{}) : launch(std::integral_constant<int, 1>{}, F8{});
             else
-                hipLaunchKernelGGL((gqa_decode_persist_kernel<0>), grid, dim3(64), 0, stream, p);
+                kv8 ? launch(std::integral_constant<int, 0>{}, T8{}) : launch(std::integral_constant<int, 0>{}, F8{});
             if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode, persistent)")) return st;
         }
         const int64_t fix_blocks = d.num_tiles * a.num_kv_heads + p.pad_blocks;
@@ -1019,13 +1071,21 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     const int64_t blocks = ((d.total_items + p.pad_blocks) + 7) / 8 * 8;
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
-    switch (decode_depth() * 4 + ppmode) {
-        case 8: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0>), grid, dim3(64), 0, stream, p); break;
-        case 9: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1>), grid, dim3(64), 0, stream, p); break;
-        case 10: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2>), grid, dim3(64), 0, stream, p); break;
-        case 12: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 0>), grid, dim3(64), 0, stream, p); break;
-        case 13: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 1>), grid, dim3(64), 0, stream, p); break;
-        default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 2>), grid, dim3(64), 0, stream, p); break;
+    if (kv8) {   // fp8 pools: the two-buffer ring (a step of codes is half the registers of a bf16 step)
+        switch (ppmode) {
+            case 0: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0, true>), grid, dim3(64), 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1, true>), grid, dim3(64), 0, stream, p); break;
+            default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2, true>), grid, dim3(64), 0, stream, p); break;
+        }
+    } else {
+        switch (decode_depth() * 4 + ppmode) {
+            case 8: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0, false>), grid, dim3(64), 0, stream, p); break;
+            case 9: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1, false>), grid, dim3(64), 0, stream, p); break;
+            case 10: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2, false>), grid, dim3(64), 0, stream, p); break;
+            case 12: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 0, false>), grid, dim3(64), 0, stream, p); break;
+            case 13: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 1, false>), grid, dim3(64), 0, stream, p); break;
+            default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 2, false>), grid, dim3(64), 0, stream, p); break;
+        }
     }
     if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode)")) return st;
     if (d.n_chunks > 1 && d.triples > 0) {
