@@ -572,32 +572,64 @@ __device__ __forceinline__ Tile load_tile(const DecodeParams& p, int32_t T) {
 }
 
 struct ItemAddr {
-    const_i32_ptr bt_row;
+    const int32_t* bt_row;
     int64_t base_rg;
     int32_t last_pidx;
 };
 
 __device__ __forceinline__ ItemAddr item_addr(const DecodeParams& p, const Tile& tl, int32_t g) {
     ItemAddr ia;
-    ia.bt_row = (const_i32_ptr)(p.bt + int64_t(tl.b) * p.bt_stride);
+    ia.bt_row = p.bt + int64_t(tl.b) * p.bt_stride;
     ia.base_rg = int64_t(p.stripe_begin + tl.s) * p.geo.s_stripe + int64_t(g) * p.geo.s_head;
     ia.last_pidx = tl.Lr > 0 ? (tl.Lr - 1) >> p.geo.pp_shift : 0;
     return ia;
 }
 
+// Block-table entries of one step, fetched a step ahead: lane i < 16 holds entry min(pbase + i, last_pidx) of the
+// item's row, pbase = (16 k) >> pp_shift, which covers every page the step's 16 tokens touch (pp >= 1). The fetch is a
+// vector load issued before the K/V loads of the step before it; vector loads complete in order, so by the time those
+// K/V loads have been waited for, the entries are in registers and the next issue does not wait on memory.
+__device__ __forceinline__ int32_t fetch_step_pages(const ItemAddr& ia, int32_t k, int lane, const PoolGeom& geo) {
+    const int32_t pbase = (16 * k) >> geo.pp_shift;
+    return ia.bt_row[min(pbase + (lane & 15), ia.last_pidx)];
+}
+
+// Page of block-table slot q (0 <= q < 16, wave-uniform) of a fetched step; invalid ids read page 0.
+__device__ __forceinline__ int32_t step_page(int32_t pv, int32_t q, const PoolGeom& geo) {
+    const int32_t page = __builtin_amdgcn_readlane(pv, q);
+    return (page >= 0 && page < geo.num_pages) ? page : 0;
+}
+
+// Issue step k's K/V loads with its block-table entries `pv` (fetched earlier), and fetch step k + 1's entries into
+// `pv`. Step index, last page index and the block-table row are wave-uniform; they go through readfirstlane so that
+// everything derived from them stays scalar.
 template <int PPMODE, typename SD>
-__device__ __forceinline__ void issue_step(SD& d, const DecodeParams& p, const ItemAddr& ia, int32_t k,
-                                           int32_t c4, uint32_t lane_off) {
-    // Step index, last page index and block-table row are wave-uniform; the compiler cannot always prove it inside the
-    // persistent loop, and then reads the page ids with vector loads, whose wait also drains the previous step's
-    // K/V loads. Moved to scalar registers, the page ids come through scalar loads and the K/V loads stay in flight.
+__device__ __forceinline__ void issue_step(SD& d, int32_t& pv, const DecodeParams& p, const ItemAddr& ia, int32_t k,
+                                           int32_t c4, uint32_t lane_off, int lane) {
     const int32_t ku = __builtin_amdgcn_readfirstlane(k);
-    const int32_t lp = __builtin_amdgcn_readfirstlane(ia.last_pidx);
-    const uint64_t bt = reinterpret_cast<uint64_t>(ia.bt_row);
-    const uint64_t btu = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int32_t(bt >> 32)))) << 32) |
-                         uint32_t(__builtin_amdgcn_readfirstlane(int32_t(bt)));
+    const int32_t cur = pv;
+    pv = fetch_step_pages(ia, ku + 1, lane, p.geo);          // first: the K/V loads below may stay in flight
+    const int32_t jb = 16 * ku;
+    const int32_t pbase = jb >> p.geo.pp_shift;
     StepBase sb;
-    step_bases<PPMODE>(sb, reinterpret_cast<const_i32_ptr>(btu), 16 * ku, lp, c4, ia.base_rg, p.geo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int32_t j = jb + 4 * e;                        // first token of instruction e
+        const int32_t q0 = (j >> p.geo.pp_shift) - pbase;
+        if (PPMODE == 2) {
+            sb.base[e] = ia.base_rg + int64_t(step_page(cur, q0, p.geo)) * p.geo.s_page +
+                         int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot;
+        } else if (PPMODE == 1) {
+            const int64_t c0 = ia.base_rg + int64_t(step_page(cur, q0, p.geo)) * p.geo.s_page;
+            const int64_t c1 = ia.base_rg + int64_t(step_page(cur, q0 + 1, p.geo)) * p.geo.s_page;
+            sb.base[e] = c4 >= 2 ? c1 : c0;
+        } else {
+            int64_t c[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = ia.base_rg + int64_t(step_page(cur, q0 + q, p.geo)) * p.geo.s_page;
+            sb.base[e] = c4 == 0 ? c[0] : c4 == 1 ? c[1] : c4 == 2 ? c[2] : c[3];
+        }
+    }
     step_load(d, p.kp, p.vp, sb, lane_off);
 }
 
@@ -737,10 +769,12 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     bool first_seg = true;
     int qbuf = 0;                                    // LDS query buffer of the current item
     StepBuf<KV8> da, db;
+    int32_t pv;                                      // block-table entries of the next step to issue
     {
         bf16x8_t q0[4];
         load_query(q0, p, tl, g, n16, c4);
-        issue_step<PPMODE>(da, p, ia, seg_begin, c4, lane_off);
+        pv = fetch_step_pages(ia, seg_begin, lane, p.geo);
+        issue_step<PPMODE>(da, pv, p, ia, seg_begin, c4, lane_off, lane);
         wait_vmem_8();                               // the query is in; the first step may still be in flight
         stage_query(s_q[0], q0, lane);
     }
@@ -752,24 +786,25 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
         st.m = neg_inf();
         st.l = 0.f;
         const u32x4_t* sq = s_q[qbuf];
+        // Steady state: steps go in pairs, step k in da and step k + 1 in db, so a buffer is never copied (copying a
+        // buffer whose loads are in flight makes the wave wait for every load). Loads are unconditional: a step past
+        // the segment (the second of an odd segment's last pair) is loaded and not computed; its addresses stay inside
+        // the row's pages.
+        const int32_t last = seg_end - 1;
         int32_t k = seg_begin;
-        // Steady state: one item, unconditional loads, the next step always in flight.
-        while (k + 1 < seg_end) {
+        for (;;) {
             bf16x8_t qop[4];
-            issue_step<PPMODE>(db, p, ia, k + 1, c4, lane_off);
+            issue_step<PPMODE>(db, pv, p, ia, k + 1, c4, lane_off, lane);
             read_query(qop, sq, lane);
             step_compute(st, widen(da), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
-            ++k;
-            if (k + 1 >= seg_end) {
-                da = db;
-                break;
-            }
-            issue_step<PPMODE>(da, p, ia, k + 1, c4, lane_off);
+            if (k + 2 > last) break;                 // db holds step k + 1: the segment's last, or past it
+            issue_step<PPMODE>(da, pv, p, ia, k + 2, c4, lane_off, lane);
             read_query(qop, sq, lane);
-            step_compute(st, widen(db), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
-            ++k;
+            step_compute(st, widen(db), qop, s_kx, 16 * (k + 1), tl.Lr, n16, c4, p.scale_log2);
+            k += 2;
         }
-        // Last step of the segment: the next item's query and first step are issued before it is computed.
+        // Last step of the segment (in db): the next item's query and first step (into da) are issued before it is
+        // computed.
         remaining -= seg_end - seg_begin;
         bool more = remaining > 0;
         Tile nt = tl;
@@ -789,15 +824,16 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
                 T = nT;
                 na = item_addr(p, nt, ng);
                 load_query(qn, p, nt, ng, n16, c4);
-                issue_step<PPMODE>(db, p, na, 0, c4, lane_off);
+                pv = fetch_step_pages(na, 0, lane, p.geo);   // the next item's first entries (once per item)
+                issue_step<PPMODE>(da, pv, p, na, 0, c4, lane_off, lane);
             } else {
                 more = false;                        // cannot happen while steps remain; never read past the heads
             }
         }
-        {
+        if (k + 1 <= last) {
             bf16x8_t qop[4];
             read_query(qop, sq, lane);
-            step_compute(st, widen(da), qop, s_kx, 16 * k, tl.Lr, n16, c4, p.scale_log2);
+            step_compute(st, widen(db), qop, s_kx, 16 * (k + 1), tl.Lr, n16, c4, p.scale_log2);
         }
         if (more) {
             wait_vmem_8();
@@ -809,8 +845,7 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
         tl = nt;
         ia = na;
         g = ng;
-        qbuf ^= 1;
-        da = db;
+        qbuf ^= 1;                                   // the new segment's first step is in da
         seg_begin = 0;
         seg_end = int32_t(min<int64_t>(tl.n_steps, remaining));
         first_seg = false;
