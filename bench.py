@@ -16,6 +16,10 @@ traffic per launch from rocprofv3 counters, scaled by the counter/bytes ratio of
 kernel build.
 
 `cpu_baseline` is the float64 CPU oracle timed on host cores over a bounded sample of the same workload.
+
+Warm-up is at least W steps and at least ``--min-warmup-s`` seconds of steps: the GPU's clocks settle only under
+sustained load. Measured on the MLA workload, the partial takes ~560 us right after a few steps or after an idle
+second and ~460 us after two seconds of back-to-back steps; the HBM-bound GQA decode changes by ~1%.
 """
 from __future__ import annotations
 
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--min-warmup-s", type=float, default=2.0,
+                    help="keep running untimed warm-up steps until this many seconds have passed (clock settling)")
     ap.add_argument("--workload", default="llama8b", choices=["tiny", "llama8b", "longctx", "mla", "mixed"])
     ap.add_argument("--interleave", type=int, default=1,
                     help="KV-cache interleave size of the pool (runs of that many slots per partner; 1 = plain rule)")
@@ -143,9 +149,14 @@ def main():
     plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        plan.run()
-    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
+        for _ in range(10 if warm_steps >= args.warmup else 1):
+            plan.run()
+            warm_steps += 1
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_warm
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -202,6 +213,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_s, 2)},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -6,11 +6,15 @@
 // the context-parallel decode covers MLA's single latent head as well as GQA).
 //
 // Work decomposition. A unit is (row b, stripe s, query token, chunk of the stripe's local tokens). One workgroup of
-// Hq / 16 waves (eight for 128 heads, two per SIMD) serves all query heads of a unit, so each latent tile is fetched
-// once; each wave owns 16 heads. The latent rows stream through LDS in tiles of 32 tokens (four buffers, three tiles
-// in flight), loaded straight from global memory into LDS, and every wave reads each tile twice: as the key operand of
-// the score product and as the value operand of the output product. 16 heads per wave keeps the query operand (72
-// VGPRs) and the output accumulators (128) in registers; 32 heads per wave would halve the LDS reads but does not fit.
+// NW = Hq / 16 waves (eight for 128 heads, two per SIMD) serves all query heads of a unit, so each latent tile is
+// fetched once. The latent rows stream through LDS in tiles of 32 tokens (four buffers, three tiles in flight), loaded
+// straight from global memory into LDS. The two products split the work differently:
+//   * scores: wave w owns query heads [16 w, 16 w + 16) (their query operand, 72 VGPRs, stays in registers) and reads
+//     the whole key tile;
+//   * output: wave w owns value dims [512 w / NW, 512 (w + 1) / NW) of every head (128 accumulator VGPRs) and reads
+//     only its slice of the value tile. The probabilities of all heads go through a 1 KB-per-wave LDS buffer.
+// Reading the whole value tile in every wave (the other split of the output product) cost 32 KB of transposing LDS
+// reads per wave and tile, more than the key reads; with the slice it is 4 KB of value plus 8 KB of probabilities.
 // The chunk's page ids are staged in LDS when a unit starts. A small plan kernel orders the units longest first, so
 // the hardware's in-order dispatch packs long and short units onto the same compute unit. A stripe longer than one
 // chunk leaves one unnormalised record per chunk and a merge kernel combines them exactly.
@@ -23,12 +27,14 @@
 //     exact maximum as reference). The accumulators are thus written only by MFMAs and stay in the accumulation
 //     registers. The running sum adds the fp32 probabilities, so the lse keeps fp32 accuracy; the value product takes
 //     them rounded to bf16 (a relative change of at most 2^-9 per weight, which averages out over a stripe's tokens).
-//   * out += P . V with v_mfma_f32_16x16x32_bf16: the score layout left by the first product is already the A-operand
-//     layout (k index 8c + e of lane group c is tile token 16 (e / 4) + 4c + e % 4), and the B operand of each 16-dim
-//     output tile comes from two transposed LDS reads (ds_read_b64_tr_b16), so no register staging or permutes are
-//     needed. 32 MFMAs into 128 accumulator registers.
+//   * the probabilities (bf16) go to the wave's slot of the LDS probability buffer in the A-operand layout the score
+//     product leaves (k index 8c + e of lane group c is tile token 16 (e / 4) + 4c + e % 4); one barrier.
+//   * out += P . V with v_mfma_f32_16x16x32_bf16 over the wave's 32 / NW dim blocks and the NW head groups: A = a head
+//     group's probabilities (one 16-byte LDS read per lane), B = a 16-dim value block from two transposed LDS reads
+//     (ds_read_b64_tr_b16) in the same k order, so no register staging or permutes are needed. 32 MFMAs into 128
+//     accumulator registers.
 //
-// LDS layout of a tile (37,888 bytes; three buffers): the value dims [0, 512) of token t in a row of 1056 bytes at
+// LDS layout of a tile (37,888 bytes; four buffers): the value dims [0, 512) of token t in a row of 1056 bytes at
 // 1056 t (1024 bytes of data, 32 of padding), the rope dims [512, 576) in a 128-byte row at 33,792 + 128 t whose eight
 // 16-byte pieces are stored XOR g(t) = (t ^ (t >> 2)) & 7. Measured on gfx950, the three read patterns (sixteen
 // tokens at one 16-byte piece for the score operand, in either region, and the transposed reads of four tokens for
@@ -51,7 +57,7 @@ constexpr int kRowR = 128;                     // LDS bytes per token for the ro
 constexpr int kTileBytes = kRegionV + kTile * kRowR;
 constexpr int kBufs = 4;                       // LDS tile buffers: three tiles in flight while one is computed
 constexpr int kAhead = kBufs - 1;
-constexpr int kMaxChunkPages = 1024;           // page ids of one chunk staged in LDS
+constexpr int kMaxChunkPages = 512;            // page ids of one chunk staged in LDS
 constexpr int kKSteps = kD / 32;               // k-steps of the score product
 constexpr int kMaxPlanUnits = 1024;            // units sorted by the plan kernel (block order above)
 constexpr int kTargetUnits = 512;              // about two units per compute unit before chunks are split
@@ -191,6 +197,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed (the other counters at their maximum).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Wait until at most the loads of kAhead - 1 tiles are outstanding (the counter saturates at 63: with one or two
 // waves a little more than the oldest tile is waited for).
 template <int NW>
@@ -211,6 +220,20 @@ __device__ __forceinline__ void sched_pipeline() {
         __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD / R, 0);
+}
+
+// Scheduling groups of the output product: AHEAD LDS reads, then G groups of M MFMAs, each but the last followed by R
+// reads.
+template <int M, int G, int AHEAD, int R>
+__device__ __forceinline__ void sched_pv() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < G - 1; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (those would drain the tiles in flight); the empty
@@ -249,8 +272,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     __shared__ __attribute__((aligned(16))) char s_tile1[kTileBytes];
     __shared__ __attribute__((aligned(16))) char s_tile2[kTileBytes];
     __shared__ __attribute__((aligned(16))) char s_tile3[kTileBytes];
+    __shared__ __attribute__((aligned(16))) char s_prob[NW * 1024];   // probabilities of head group w at 1024 w
     __shared__ int32_t s_pages[kMaxChunkPages];
+    __shared__ float s_rowsum[16 * NW];
     __shared__ int32_t s_over[NW];
+    constexpr int kDB = 32 / NW;                           // 16-dim output blocks of a wave
     const int lane = threadIdx.x & 63;
     const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t blk = blockIdx.x;
@@ -315,17 +341,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     //   value operand through transposed reads (ds_read_b64_tr_b16): in each 16-lane group, lane s supplies four
     //   consecutive values of one row and lane q receives element q % 4 of rows q / 4, 4 + q / 4, 8 + q / 4, 12 + q / 4.
     //   Lane s of group c4 points at token 16 r + 4 c4 + s / 4, dims 16 b + 4 (s % 4) (read r = 0, 1 of dim block b),
-    //   so lane q receives dim 16 b + q of tokens 8 c4 + e in k order: the B operand, with no permutes.
-    int32_t kofs_v[2], kofs_r[2][2], vofs[2];
+    //   so lane q receives dim 16 b + q of tokens 8 c4 + e in k order: the B operand, with no permutes. The wave's
+    //   dim blocks are b = kDB w + [0, kDB).
+    //   Only the token-block-0 offsets live in registers: token block 1 is 16 rows further (a constant), and its rope
+    //   swizzle g(t + 16) = g(t) ^ 4 swaps the two pieces k = 0, 1 of block 0.
+    const int32_t kofs_v = kRowV * n16 + 16 * c4;
+    int32_t kofs_r[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int32_t t = 16 * tb + n16;
-        kofs_v[tb] = kRowV * t + 16 * c4;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) kofs_r[tb][k] = kRegionV + kRowR * t + 16 * ((4 * k + c4) ^ swz(t));
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) vofs[r] = kRowV * (16 * r + 4 * c4 + (n16 >> 2)) + 8 * (n16 & 3);
+    for (int k = 0; k < 2; ++k) kofs_r[k] = kRegionV + kRowR * n16 + 16 * ((4 * k + c4) ^ swz(n16));
+    const int32_t vofs = kRowV * (4 * c4 + (n16 >> 2)) + 8 * (n16 & 3) + 32 * kDB * w;
+    const lds_char_ptr prob_r = (lds_char_ptr)s_prob + 16 * lane;   // + 1024 hg: head group hg's probabilities
     // Buffer b of the ring, b a compile-time constant.
     auto tile_buf = [&](auto bc) __attribute__((always_inline)) -> lds_char_ptr {
         constexpr int b = decltype(bc)::value % kBufs;
@@ -346,20 +371,28 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     float m = REDO ? p.ws_max[int64_t(u) * p.Hq + hw + n16] : neg_inf();
     float m_seen = neg_inf(), l = 0.f;
     bool over = false;
-    f32x4_t o[32];                                   // o[b][i]: head hw + 4 c4 + i, dim 16 b + n16 (unnormalised)
+    f32x4_t o[32];        // o[kDB hg + b][i]: head 16 hg + 4 c4 + i, dim 16 (kDB w + b) + n16 (unnormalised)
 #pragma unroll
     for (int b = 0; b < 32; ++b) o[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     {
         // kAhead tiles in flight before the loop; every iteration issues one more (tile indices past the end re-read
         // the last tile into a buffer nobody reads), so the wait at the top of an iteration leaves exactly the
         // kAhead - 1 newest tiles' loads outstanding.
+        // The prologue's loads take their LDS address through an opaque copy of the buffer pointer, so the
+        // compiler's wait-count pass does not track them against the buffer arrays; tracked, their state merged into
+        // the loop header's and made it wait for every load in flight there (a full drain every fourth tile). The
+        // explicit wait and barrier at the top of each step order them before the reads of their tiles all the same.
+        auto opaque = [](lds_char_ptr t) __attribute__((always_inline)) {
+            asm volatile("" : "+v"(t));
+            return t;
+        };
         const lds_i32_ptr pages = (lds_i32_ptr)s_pages;
-        issue_tile<NW>(token_rows(p, pages, pidx0, x.j0, j_last, kv_r, lane), tile_buf(std::integral_constant<int, 0>{}),
-                       w, lane);
+        issue_tile<NW>(token_rows(p, pages, pidx0, x.j0, j_last, kv_r, lane),
+                       opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
         issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + kTile, last_tile0), j_last, kv_r, lane),
-                       tile_buf(std::integral_constant<int, 1>{}), w, lane);
+                       opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
         issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + 2 * kTile, last_tile0), j_last, kv_r, lane),
-                       tile_buf(std::integral_constant<int, 2>{}), w, lane);
+                       opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
         static_assert(kAhead == 3 && kBufs == 4, "ring");
 
         // Compute tile kt from `tile`.
@@ -368,15 +401,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             const bool tail = tile0 + kTile > x.j1;
             // This tile's lane base addresses, formed once so that every read below carries its remaining offset as
             // an instruction immediate.
-            lds_char_ptr kb_v[2], kb_r[2][2], vb[2];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                kb_v[tb] = tile + kofs_v[tb];
-                kb_r[tb][0] = tile + kofs_r[tb][0];
-                kb_r[tb][1] = tile + kofs_r[tb][1];
-            }
-            vb[0] = tile + vofs[0];
-            vb[1] = tile + vofs[1];
+            const lds_char_ptr kb_v = tile + kofs_v, kb_r0 = tile + kofs_r[0], kb_r1 = tile + kofs_r[1];
+            const lds_char_ptr vb = tile + vofs;
 
             // Scores S^T[token 16 tb + 4 c4 + i][head n16].
             f32x4_t sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -384,7 +410,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
-                    const lds_char_ptr a = ks < 16 ? kb_v[tb] + 64 * ks : kb_r[tb][ks - 16];
+                    const lds_char_ptr a = ks < 16 ? kb_v + 16 * kRowV * tb + 64 * ks
+                                                   : ((ks - 16) ^ tb ? kb_r1 : kb_r0) + 16 * kRowR * tb;
                     const u32x4_t kv = *(const __attribute__((address_space(3))) u32x4_t*)a;
                     sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qreg[ks]), sacc[tb],
                                                                        0, 0, 0);
@@ -417,17 +444,45 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
                 l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
             }
 
-            // Values: 32 output tiles of 16 dims, each from two transposed reads.
-            {
+            // Share the probabilities: every wave needs all head groups' for its dim slice.
+            *(__attribute__((address_space(3))) u32x4_t*)(prob_r + 1024 * w) = pa;
+            wait_lgkm0();
+            lds_barrier();
+
+            // Values: kDB output blocks of 16 dims for each of the NW head groups; one block's operand from two
+            // transposed reads, one head group's from one 16-byte read.
+            auto vop = [&](int b) __attribute__((always_inline)) {
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 32 * b));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 16 * kRowV + 32 * b));
+                return __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            };
+            auto pop = [&](int hg) __attribute__((always_inline)) {
+                return as_bf16x8(*(const __attribute__((address_space(3))) u32x4_t*)(prob_r + 1024 * hg));
+            };
+            if constexpr (NW >= 8) {                // hold the kDB value operands, stream the head groups
+                bf16x8_t vv[kDB];
 #pragma unroll
-                for (int b = 0; b < 32; ++b) {
-                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb[0] + 32 * b));
-                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb[1] + 32 * b));
-                    const bf16x8_t bop =
-                        __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                    o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), bop, o[b], 0, 0, 0);
+                for (int b = 0; b < kDB; ++b) vv[b] = vop(b);
+#pragma unroll
+                for (int hg = 0; hg < NW; ++hg) {
+                    const bf16x8_t a = pop(hg);
+#pragma unroll
+                    for (int b = 0; b < kDB; ++b)
+                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vv[b], o[kDB * hg + b], 0, 0, 0);
                 }
-                sched_pipeline<32, 2, 8>();         // four output tiles' operands ahead
+                sched_pv<kDB, NW, 2 * kDB + 2, 1>();  // value operands and two head groups ahead, then one read per group
+            } else {                                // hold the NW probability operands, stream the value blocks
+                bf16x8_t pp[NW];
+#pragma unroll
+                for (int hg = 0; hg < NW; ++hg) pp[hg] = pop(hg);
+#pragma unroll
+                for (int b = 0; b < kDB; ++b) {
+                    const bf16x8_t v = vop(b);
+#pragma unroll
+                    for (int hg = 0; hg < NW; ++hg)
+                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[hg], v, o[kDB * hg + b], 0, 0, 0);
+                }
+                sched_pv<NW, kDB, NW + 4, 2>();       // probabilities and two value blocks ahead, then one block per group
             }
         };
 
@@ -437,7 +492,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             constexpr int b = decltype(bc)::value;
             // This wave's pieces of tile kt are in LDS: the loads of the kAhead - 1 newer tiles may stay in flight.
             wait_tile<NW>();
-            lds_barrier();                          // ... and every wave's; tile kt - 1's buffer is free
+            wait_lgkm0();                           // this wave's reads of tile kt - 1 and of the probabilities are done
+            lds_barrier();                          // ... and every wave's: tile kt - 1's buffer is free
             const int32_t tn0 = min(x.j0 + (kt + kAhead) * kTile, last_tile0);
             issue_tile<NW>(token_rows(p, pages, pidx0, tn0, j_last, kv_r, lane),
                            tile_buf(std::integral_constant<int, b + kAhead>{}), w, lane);
@@ -468,21 +524,29 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         }
     }
 
-    // Epilogue: row sums over the four lane groups, then the normalised partial or this chunk's record.
+    // Epilogue: row sums over the four lane groups (each head's sum lives in the wave that scored it, and goes to LDS
+    // for the waves holding that head's dims), then the normalised partial or this chunk's record.
     const bool split = p.n_chunks > 1 && x.Lr > p.chunk_tokens;
     float* rec = split ? p.ws_rec + int64_t(u) * p.rec_floats : nullptr;
     float ls = l;
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
+    if (c4 == 0) s_rowsum[hw + n16] = ls;
+    __syncthreads();
+    // Lane base: head 4 c4 (+ 16 hg + i), dim 16 kDB w + n16 (+ 16 b); head stride of the partial or of the record.
+    const int64_t hs = split ? int64_t(kDv) : p.o_sh;
+    float* const base = (split ? rec : p.out + int64_t(x.s) * p.o_ss + int64_t(x.t) * p.o_st) + 4 * c4 * hs +
+                        16 * kDB * w + n16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int32_t h = hw + 4 * c4 + i;
-        const float li = __shfl(ls, 4 * c4 + i);
-        const float inv = split ? 1.0f : (li > 0.f ? 1.0f / li : 0.f);
-        float* dst = split ? rec + int64_t(h) * kDv
-                           : p.out + int64_t(x.s) * p.o_ss + int64_t(x.t) * p.o_st + int64_t(h) * p.o_sh;
+    for (int hg = 0; hg < NW; ++hg) {
 #pragma unroll
-        for (int b = 0; b < 32; ++b) dst[16 * b + n16] = o[b][i] * inv;
+        for (int i = 0; i < 4; ++i) {
+            const float li = s_rowsum[16 * hg + 4 * c4 + i];
+            const float inv = split ? 1.0f : (li > 0.f ? 1.0f / li : 0.f);
+            float* dst = base + (16 * hg + i) * hs;
+#pragma unroll
+            for (int b = 0; b < kDB; ++b) dst[16 * b] = o[kDB * hg + b][i] * inv;
+        }
     }
     if (c4 == 0) {
         const int32_t h = hw + n16;

@@ -288,12 +288,27 @@ def test_stripe_subset_matches_all_stripes(fixed_splits):
         check_lse(pl[:, :t], fl[:, :t].double().cpu().numpy(), "balanced vs fixed lse")
 
 
-def test_mla_late_score_jump():
+@pytest.mark.parametrize("heads", [16, 32, 64])
+def test_mla_query_head_counts(heads):
+    """The MLA kernel runs Hq / 16 waves per workgroup and splits the value dims over them (512, 256, 128 dims a wave
+    for 16, 32, 64 heads); contexts of one token, a ragged tail and several chunks per stripe."""
+    wl = workloads.make("mla", batch=3, ctx_lengths=[7, 130, 2000], num_q_heads=heads)
+    say(f"mla heads={heads} ctx={list(wl.ctx_len)}")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_mla_late_score_jump(heads):
     """A late latent row aligned with one query head scores far above everything in the stripe's first tile. The MLA
     kernel takes its softmax reference from a unit's first tile, so this case makes it repeat the unit with the exact
     maximum; the partials must still match the oracle."""
-    wl = workloads.make("mla", batch=2, ctx_lengths=[300, 1000])
-    say("mla late score jump")
+    wl = workloads.make("mla", batch=2, ctx_lengths=[300, 1000], num_q_heads=heads)
+    say(f"mla late score jump heads={heads}")
     batch = pool.build_batch(wl, DEV)
     b, c = 1, 1000
     rv = workloads.row_values(wl, b, DEV)

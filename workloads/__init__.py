@@ -131,7 +131,7 @@ def _block_tables(rng, tokens_per_row, page_size, spare_frac=0.02, min_spare=2, 
 def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_range=None,
          ctx_lengths=None, new_lengths=None, partners: int | None = None, page_size: int | None = None,
          bucket: int | None = None, pad_rows: int = 0, bt_width: int | None = None, interleave: int = 1,
-         kv_dtype: str = "same") -> Workload:
+         kv_dtype: str = "same", num_q_heads: int | None = None) -> Workload:
     """Build workload ``name`` (one of :data:`CONFIG_NAMES`), optionally shrunk for parity tests.
 
     ``seed`` defaults to ``1000 + k`` for the k-th config (1-based). ``batch``/``ctx_range``/``ctx_lengths``/
@@ -139,7 +139,8 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
     and P; ``partners``/``page_size`` override P and the logical page size; ``interleave`` sets the pool's KV-cache
     interleave size (1 = the plain slot rule); ``kv_dtype="fp8"`` (bf16 GQA workloads) stores the context K/V as E4M3
     codes: each value is divided by its tensor's descale (0.0173 for K, 0.0291 for V: fixed, unequal, not powers of two),
-    clipped to +-448 and rounded by torch's float8_e4m3fn conversion.
+    clipped to +-448 and rounded by torch's float8_e4m3fn conversion. ``num_q_heads`` (MLA only) sets the query heads
+    sharing the latent head: 128 is the whole model, 64, 32 and 16 are its share on 2, 4 and 8 tensor-parallel ranks.
     """
     if name not in CONFIG_NAMES:
         raise ValueError(f"unknown workload {name!r}; expected one of {CONFIG_NAMES}")
@@ -196,6 +197,10 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
         if int(new.sum()) > bucket:
             raise ValueError(f"in-step tokens {int(new.sum())} exceed the bucket {bucket}")
 
+    if num_q_heads is not None:
+        if base["kind"] != "mla":
+            raise ValueError("num_q_heads is only set for the MLA workload")
+        base["num_q_heads"] = int(num_q_heads)
     if partners is not None:
         base["partners"] = int(partners)
     if page_size is not None:
