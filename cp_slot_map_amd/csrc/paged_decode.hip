@@ -536,17 +536,22 @@ __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const Decode
 // padding tokens.
 
 // Steps of tile T (0 when the tile holds no query row). Per-lane T: vector loads.
-__device__ __forceinline__ int32_t tile_steps(const DecodeParams& p, int32_t T) {
+// Steps of tile T from its row's q_row_start[b], q_row_start[b + 1] and ctx_len[b].
+__device__ __forceinline__ int32_t tile_steps_of(const DecodeParams& p, int32_t T, int32_t qrs0, int32_t qrs1,
+                                                 int32_t ctx) {
     const int32_t qt = T % p.n_qtiles;
-    const int32_t bs = T / p.n_qtiles;
-    const int32_t s = bs % p.S;
-    const int32_t b = bs / p.S;
-    const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
-    const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    const int32_t s = (T / p.n_qtiles) % p.S;
+    const int32_t tok0 = min(max(qrs0, 0), p.T);
+    const int32_t tok1 = min(max(qrs1, tok0), p.T);
     const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(ctx, 0), p.max_pages * p.page_size);
     const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     return qt * 16 < nrows ? (Lr + 15) >> 4 : 0;
+}
+
+__device__ __forceinline__ int32_t tile_steps(const DecodeParams& p, int32_t T) {
+    const int32_t b = (T / p.n_qtiles) / p.S;
+    return tile_steps_of(p, T, p.q_row_start[b], p.q_row_start[b + 1], p.ctx_len[b]);
 }
 
 struct Tile {
@@ -727,11 +732,24 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     const int32_t n16 = lane & 15, c4 = lane >> 4;
     const int32_t NT = p.num_tiles;
 
-    // Step counts of every tile: lane l sums a block of K consecutive tiles; a wave scan gives block offsets.
+    // Step counts of every tile: lane l sums a block of K consecutive tiles; a wave scan gives block offsets. Four
+    // tiles' loads are issued before any is used (indices clamped into the lane's block), so a block of K tiles costs
+    // ceil(K / 4) memory round trips rather than K: every wave runs this before its first K/V load.
     const int32_t K = (NT + 63) >> 6;
     const int32_t t_lo = min(lane * K, NT), t_hi = min(t_lo + K, NT);
     int32_t my_sum = 0;
-    for (int32_t t = t_lo; t < t_hi; ++t) my_sum += tile_steps(p, t);
+    for (int32_t t = t_lo; t < t_hi; t += 4) {
+        int32_t qa[4], qb[4], cl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int32_t b = (min(t + u, t_hi - 1) / p.n_qtiles) / p.S;
+            qa[u] = p.q_row_start[b];
+            qb[u] = p.q_row_start[b + 1];
+            cl[u] = p.ctx_len[b];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) my_sum += t + u < t_hi ? tile_steps_of(p, t + u, qa[u], qb[u], cl[u]) : 0;
+    }
     int32_t N = 0;
     const int32_t my_excl = wave_exclusive_scan(my_sum, lane, N);
     if (w == 0) {                                    // block offsets for the fix-up kernel
@@ -909,19 +927,39 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
         const int32_t row = 4 * rg + rsub;
         const bool active = row < tile_rows;
         const int32_t rrow = min(row, RR - 1);
-        float M = neg_inf();
-        for (int64_t wv = wA; wv <= wB; ++wv) {
-            const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
-            M = fmaxf(M, rc[RR * 128 + rrow]);
-        }
-        float Lsum = 0.f;
+        // One online pass over the covering waves' records, four loaded together (an item split over two waves, the
+        // usual case, costs one memory round trip): M is the running maximum, earlier sums are rescaled when it rises.
+        // Records hold finite maxima (every segment has at least one key); unused batch entries carry -inf and weigh 0.
+        float M = neg_inf(), Lsum = 0.f;
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t wv = wA; wv <= wB; ++wv) {
-            const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
-            const float wgt = exp2f(rc[RR * 128 + rrow] - M);
-            Lsum += wgt * rc[RR * 128 + RR + rrow];
-            a0 += wgt * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
-            a1 += wgt * *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
+        for (int64_t w0 = wA; w0 <= wB; w0 += 4) {
+            float mc[4], lc[4];
+            f32x4_t o0[4], o1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t wv = min(w0 + u, wB);
+                const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
+                mc[u] = rc[RR * 128 + rrow];
+                lc[u] = rc[RR * 128 + RR + rrow];
+                o0[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
+                o1[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
+                if (w0 + u > wB) mc[u] = neg_inf();
+            }
+            float Mn = M;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mc[u]);
+            const float f = M == neg_inf() ? 0.f : exp2f(M - Mn);
+            Lsum *= f;
+            a0 *= f;
+            a1 *= f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wgt = mc[u] == neg_inf() ? 0.f : exp2f(mc[u] - Mn);
+                Lsum += wgt * lc[u];
+                a0 += wgt * o0[u];
+                a1 += wgt * o1[u];
+            }
+            M = Mn;
         }
         if (active) {
             const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
