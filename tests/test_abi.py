@@ -199,3 +199,21 @@ def test_debug_gather_refusals(lib):
     assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 1, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
     assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 8, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
     assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 1, 8, None, None) == _lib.CPATTN_OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With no built library the binding raises at load time: there is no non-HIP fallback."""
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libcpattn.so"))
+    with pytest.raises(ImportError, match="not built"):
+        _lib.load()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message (before touching a device)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
