@@ -206,6 +206,8 @@ def main():
                     "mla": "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel)",
                     "mixed": "cp_paged_attn_partial + cp_own_token_attn (gqa_extend_kernel, context and own-token)",
                     "tiny": "cp_paged_attn_partial (paged_generic_kernel)"}
+    if wl.kind == "mla" and wl.kv_dtype == "fp8":
+        kernel_names["mla"] = "cp_paged_attn_partial (paged_generic_kernel over the fp8 latent pool)"
     # The roofline that bounds the partial: HBM below the ridge point (peak flops / peak bytes), MFMA above it.
     mfma_bound = flops / kv_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) if kv_bytes else False
     if mfma_bound:

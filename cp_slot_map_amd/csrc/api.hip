@@ -50,7 +50,10 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
         if (!(a.k_descale > 0.f && a.k_descale < INFINITY) || !(a.v_descale > 0.f && a.v_descale < INFINITY))
             return fail(CPATTN_EINVAL, "fp8 descales must be finite and positive (k %g, v %g)", double(a.k_descale),
                         double(a.v_descale));
-        if (a.kind == CPATTN_MLA) return fail(CPATTN_EUNSUPPORTED, "MLA over fp8 pools is not built");
+        // MLA keys and values are the same latent rows, so they carry one descale.
+        if (a.kind == CPATTN_MLA && a.k_descale != a.v_descale)
+            return fail(CPATTN_EINVAL, "MLA latent rows have one descale (k %g != v %g)", double(a.k_descale),
+                        double(a.v_descale));
     }
     if (a.interleave < 0 || a.interleave > 65536) return fail(CPATTN_EINVAL, "interleave = %d outside [0, 65536]", a.interleave);
     const int32_t ilv = interleave_of(a);

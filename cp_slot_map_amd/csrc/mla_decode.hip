@@ -628,6 +628,7 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 bool mla_decode_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_MLA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kDv) return false;
+    if (a.kv_format != CPATTN_KV_SAME) return false;   // fp8 latent pools: the generic kernel
     if (a.num_q_heads != 16 && a.num_q_heads != 32 && a.num_q_heads != 64 && a.num_q_heads != 128) return false;
     if (geo.pp_shift < 0) return false;
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };

@@ -191,7 +191,10 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
     if (a.kind == CPATTN_MLA) {
         constexpr int R = 8;
         dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows), uint32_t(a.stripe_count));
-        launch_generic_t<uint16_t, uint16_t, 9, 8, R>(p, grid, stream);
+        if (fp8)
+            launch_generic_t<uint16_t, uint8_t, 9, 8, R>(p, grid, stream);
+        else
+            launch_generic_t<uint16_t, uint16_t, 9, 8, R>(p, grid, stream);
     } else if (a.head_dim == 64) {
         constexpr int R = 8;
         dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows * a.num_kv_heads), uint32_t(a.stripe_count));

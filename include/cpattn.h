@@ -168,9 +168,10 @@ typedef struct cp_paged_args {
     int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */
     int32_t interleave;       /* KV-cache interleave size I (0 or 1: none); the placement of cp_slot_map; I * P must
                                  divide page_size */
-    int32_t kv_format;        /* CPATTN_KV_SAME or CPATTN_KV_FP8_E4M3 (GQA with dtype bf16 only) */
+    int32_t kv_format;        /* CPATTN_KV_SAME or CPATTN_KV_FP8_E4M3 (dtype bf16 only) */
     float k_descale;          /* fp8 pools: a key element is its code's value times k_descale (finite, > 0) */
-    float v_descale;          /* fp8 pools: a value element is its code's value times v_descale (finite, > 0) */
+    float v_descale;          /* fp8 pools: a value element is its code's value times v_descale (finite, > 0);
+                                 MLA: equal to k_descale (one latent tensor) */
     const int32_t* q_row_start;  /* device int32 [num_rows + 1], non-decreasing, q_row_start[num_rows] <= num_tokens */
     const int32_t* ctx_len;      /* device int32 [num_rows]: context tokens of row b in the pool (all stripes) */
     const int32_t* block_table;  /* device int32 [num_rows, bt_stride]: logical page ids */
@@ -219,10 +220,11 @@ typedef struct cp_paged_args {
  * output).
  *
  * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, an unknown kv_format, fp8 pools with dtype other
- * than bf16 or a descale that is not finite and positive, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
+ * than bf16, a descale that is not finite and positive or MLA with k_descale != v_descale, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
  * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
- * (128, 128), bf16 queries over fp8 pools for both; MLA bf16 with (576, 512) (not over fp8 pools).
+ * (128, 128), bf16 queries over fp8 pools for both; MLA bf16 with (576, 512), also over fp8 latent pools (read by
+ * the generic kernel, which decodes each code as it is read).
  */
 int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
 

@@ -102,8 +102,8 @@ def _paged(**kw):
     (dict(kv_format=1, k_descale=0.5, v_descale=0.0), _lib.CPATTN_EINVAL),
     (dict(kv_format=1, k_descale=float("inf"), v_descale=0.5), _lib.CPATTN_EINVAL),
     (dict(kv_format=1, dtype=0, k_descale=0.5, v_descale=0.5), _lib.CPATTN_EINVAL),   # fp8 pools need bf16 queries
-    (dict(kv_format=1, kind=1, num_kv_heads=1, head_dim=576, head_dim_v=512, k_descale=0.5, v_descale=0.5),
-     _lib.CPATTN_EUNSUPPORTED),
+    (dict(kv_format=1, kind=1, num_kv_heads=1, head_dim=576, head_dim_v=512, k_descale=0.5, v_descale=0.25),
+     _lib.CPATTN_EINVAL),                              # MLA latent rows carry one descale
 ])
 def test_paged_refusals(lib, bad, code):
     a = _paged(**bad)
@@ -111,6 +111,15 @@ def test_paged_refusals(lib, bad, code):
     assert _err(lib)
     n = C.c_int64(-1)
     assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == code
+
+
+def test_mla_over_fp8_passes_host_checks(lib):
+    """MLA over an fp8 latent pool with one descale is accepted (the generic kernel reads it)."""
+    a = _paged(kv_format=1, kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, head_dim_v=512, k_descale=0.5,
+               v_descale=0.5)
+    n = C.c_int64(-1)
+    assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == _lib.CPATTN_OK
+    assert n.value == 0
 
 
 def test_paged_null_args(lib):

@@ -113,12 +113,15 @@ FP8 = [
     ("llama8b", dict(batch=3, ctx_lengths=[17, 300, 2222], kv_dtype="fp8", interleave=4)),
     ("mixed", dict(batch=6, new_lengths=[1, 1, 5, 33, 1, 70], ctx_lengths=[0, 19, 0, 300, 1000, 2100], pad_rows=2,
                    kv_dtype="fp8")),
+    ("mla", dict(batch=4, ctx_lengths=[1, 3, 70, 700], kv_dtype="fp8")),
+    ("mla", dict(batch=2, ctx_lengths=[65, 1500], kv_dtype="fp8", num_q_heads=16, interleave=2)),
 ]
 
 
-def test_fp8_write_path_bit_exact():
+@pytest.mark.parametrize("name", ["llama8b", "mla"])
+def test_fp8_write_path_bit_exact(name):
     """fp8 pools: kv_write copies the E4M3 codes by the slot rule and the kernels' addressing reads them back."""
-    wl = workloads.make("llama8b", batch=3, ctx_lengths=[1, 37, 301], kv_dtype="fp8", interleave=2)
+    wl = workloads.make(name, batch=3, ctx_lengths=[1, 37, 301], kv_dtype="fp8", interleave=2)
     batch = pool.build_batch(wl, DEV)
     assert batch.k_pool.dtype == torch.float8_e4m3fn
     P, ps = wl.partners, wl.page_size
@@ -126,9 +129,12 @@ def test_fp8_write_path_bit_exact():
         rv = workloads.row_values(wl, b, DEV)
         c = int(wl.ctx_len[b])
         for r in range(P):
-            got = api.debug_gather_stripe(batch.k_pool, batch.block_table[b], c, ps, P, r, interleave=2)
+            got = api.debug_gather_stripe(batch.k_pool, batch.block_table[b], c, ps, P, r, kind=wl.kind, interleave=2)
             idx = torch.from_numpy(oracle.stripe_positions(c, P, r, 2)).to(DEV)
             assert torch.equal(_bits(got), _bits(rv.k_ctx[idx]))
+            if wl.kind == "mla":        # values are the latent rows' first head_dim_v columns, in the same pool
+                assert torch.equal(_bits(got[..., :wl.head_dim_v].contiguous()), _bits(rv.v_ctx[idx].contiguous()))
+                continue
             got = api.debug_gather_stripe(batch.v_pool, batch.block_table[b], c, ps, P, r, interleave=2)
             assert torch.equal(_bits(got), _bits(rv.v_ctx[idx]))
 

@@ -137,9 +137,10 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
     ``seed`` defaults to ``1000 + k`` for the k-th config (1-based). ``batch``/``ctx_range``/``ctx_lengths``/
     ``new_lengths`` override the row count and the length distribution while keeping head shapes, dtype, page size
     and P; ``partners``/``page_size`` override P and the logical page size; ``interleave`` sets the pool's KV-cache
-    interleave size (1 = the plain slot rule); ``kv_dtype="fp8"`` (bf16 GQA workloads) stores the context K/V as E4M3
-    codes: each value is divided by its tensor's descale (0.0173 for K, 0.0291 for V: fixed, unequal, not powers of two),
-    clipped to +-448 and rounded by torch's float8_e4m3fn conversion. ``num_q_heads`` (MLA only) sets the query heads
+    interleave size (1 = the plain slot rule); ``kv_dtype="fp8"`` (bf16 workloads) stores the context K/V as E4M3
+    codes: each value is divided by its tensor's descale (GQA: 0.0173 for K, 0.0291 for V, fixed, unequal, not powers
+    of two; MLA: 0.0091 for the latent rows, which serve as keys and, by their first 512 columns, as values), clipped to
+    +-448 and rounded by torch's float8_e4m3fn conversion. ``num_q_heads`` (MLA only) sets the query heads
     sharing the latent head: 128 is the whole model, 64, 32 and 16 are its share on 2, 4 and 8 tensor-parallel ranks.
     """
     if name not in CONFIG_NAMES:
@@ -218,9 +219,13 @@ def make(name: str, seed: int | None = None, *, batch: int | None = None, ctx_ra
         new = np.concatenate([new, np.zeros(pad_rows, dtype=np.int64)])
         bt = np.concatenate([bt, np.zeros((pad_rows, bt.shape[1]), dtype=np.int32)])
         notes.append(f"{pad_rows} padding rows (no tokens, no context, block table on the sink)")
-    fp8 = dict(kv_dtype="fp8", k_descale=0.0173, v_descale=0.0291) if kv_dtype == "fp8" else {}
-    if fp8 and (base["kind"] != "gqa" or base["dtype"] != "bf16"):
-        raise ValueError("fp8 pools are built for bf16 GQA workloads")
+    fp8 = {}
+    if kv_dtype == "fp8":
+        if base["dtype"] != "bf16":
+            raise ValueError("fp8 pools are built for bf16 workloads")
+        # GQA: separate K and V descales; MLA: the latent rows (keys, and values as their first columns) share one.
+        fp8 = dict(kv_dtype="fp8", k_descale=0.0173, v_descale=0.0291) if base["kind"] == "gqa" else \
+            dict(kv_dtype="fp8", k_descale=0.0091, v_descale=0.0091)
     return Workload(name=name, seed=seed, ctx_len=ctx.astype(np.int32), new_len=new.astype(np.int32),
                     bucket=int(bucket), block_table=bt, num_pages=int(num_pages), pad_rows=int(pad_rows),
                     interleave=int(interleave), notes=notes, **fp8, **base)
@@ -244,7 +249,7 @@ def row_values(wl: Workload, row: int, device="cpu") -> RowValues:
 
     q = draw(n, wl.num_q_heads, wl.head_dim)
     if wl.kind == "mla":
-        lat = draw(c, 1, wl.head_dim)
+        lat = draw(c, 1, wl.head_dim, descale=wl.k_descale if wl.kv_dtype == "fp8" else None)
         lat_new = draw(n, 1, wl.head_dim) if wl.own_token else None
         return RowValues(q=q, k_ctx=lat, v_ctx=lat[..., :wl.head_dim_v],
                          k_new=lat_new, v_new=None if lat_new is None else lat_new[..., :wl.head_dim_v])
