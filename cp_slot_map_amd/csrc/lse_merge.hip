@@ -10,6 +10,8 @@
 // Dv/4 threads of a (token, head)) and writes one float4 (or 4 bf16).
 #include "common.h"
 
+#include <cstdlib>
+
 namespace cpattn {
 
 struct MergeParams {
@@ -25,13 +27,15 @@ struct MergeParams {
     int32_t N, T, H, Dv4;
 };
 
-template <bool kBf16Out>
+// kV = 1: a thread handles 4 dims of a (token, head); kV = 2: 8 dims (two float4 per partial in flight per thread).
+template <bool kBf16Out, int kV>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = int64_t(p.T) * p.H * p.Dv4;
+    const int32_t Dq = p.Dv4 / kV;                        // threads per (token, head)
+    const int64_t total = int64_t(p.T) * p.H * Dq;
     if (gid >= total) return;
-    const int32_t d4 = int32_t(gid % p.Dv4);
-    const int64_t th = gid / p.Dv4;
+    const int32_t d4 = int32_t(gid % Dq) * kV;            // first float4 of this thread
+    const int64_t th = gid / Dq;
     const int32_t h = int32_t(th % p.H);
     const int32_t t = int32_t(th / p.H);
 
@@ -39,21 +43,26 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     // never multiplied, so whatever its out row holds cannot reach the result.
     const bool padding = p.token_count != nullptr && t >= *p.token_count;
     float l[CPATTN_MAX_PARTIALS];
-    f32x4_t o[CPATTN_MAX_PARTIALS];
+    f32x4_t o[CPATTN_MAX_PARTIALS][kV];
 #pragma unroll
     for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
         if (i < p.N && !padding) {
             l[i] = p.lse_i[i][int64_t(t) * p.l_st[i] + int64_t(h) * p.l_sh[i]];
-            o[i] = *reinterpret_cast<const f32x4_t*>(p.out_i[i] + int64_t(t) * p.o_st[i] + int64_t(h) * p.o_sh[i] + 4 * d4);
+            const float* src = p.out_i[i] + int64_t(t) * p.o_st[i] + int64_t(h) * p.o_sh[i] + 4 * d4;
+#pragma unroll
+            for (int v = 0; v < kV; ++v) o[i][v] = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
         } else {
             l[i] = neg_inf();
-            o[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < kV; ++v) o[i][v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         }
     }
     float M = neg_inf();
 #pragma unroll
     for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) M = fmaxf(M, l[i]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[kV];
+#pragma unroll
+    for (int v = 0; v < kV; ++v) acc[v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     float lse = neg_inf();
     if (M != neg_inf()) {
         float w[CPATTN_MAX_PARTIALS];
@@ -66,17 +75,23 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         const float inv = 1.0f / tot;
 #pragma unroll
         for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
-            const f32x4_t c = (w[i] * inv) * o[i];
-            if (w[i] != 0.f) acc += c;
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                const f32x4_t c = (w[i] * inv) * o[i][v];
+                if (w[i] != 0.f) acc[v] += c;
+            }
         }
         lse = M + logf(tot);
     }
     const int64_t off = int64_t(t) * p.out_st + int64_t(h) * p.out_sh + 4 * d4;
-    if (kBf16Out) {
-        u32x2_t v = {pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3])};
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + off) = v;
-    } else {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + off) = acc;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+        if (kBf16Out) {
+            u32x2_t b = {pack2_bf16(acc[v][0], acc[v][1]), pack2_bf16(acc[v][2], acc[v][3])};
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + off + 4 * v) = b;
+        } else {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + off + 4 * v) = acc[v];
+        }
     }
     if (d4 == 0 && p.lse_out) p.lse_out[int64_t(t) * p.lse_out_st + h] = lse;
 }
@@ -125,10 +140,19 @@ extern "C" int32_t cp_lse_merge(const cp_merge_args* a, hipStream_t stream) {
     p.T = a->num_tokens;
     p.H = a->num_heads;
     p.Dv4 = a->head_dim_v / 4;
-    const dim3 grid(uint32_t((total + 255) / 256));
-    if (a->out_dtype == CPATTN_BF16)
-        hipLaunchKernelGGL(lse_merge_kernel<true>, grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(lse_merge_kernel<false>, grid, dim3(256), 0, stream, p);
+    // Eight dims a thread when Dv allows it (unless CPATTN_MERGE_DIMS=4): twice the bytes in flight per thread.
+    static const bool wide_ok = [] {
+        const char* e = std::getenv("CPATTN_MERGE_DIMS");
+        return !(e && std::atoi(e) == 4);
+    }();
+    const bool wide = wide_ok && (a->head_dim_v % 8) == 0;
+    const dim3 grid(uint32_t((total / (wide ? 2 : 1) + 255) / 256));
+    if (a->out_dtype == CPATTN_BF16) {
+        if (wide) hipLaunchKernelGGL((lse_merge_kernel<true, 2>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((lse_merge_kernel<true, 1>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (wide) hipLaunchKernelGGL((lse_merge_kernel<false, 2>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((lse_merge_kernel<false, 1>), grid, dim3(256), 0, stream, p);
+    }
     return check_launch("cp_lse_merge");
 }

@@ -246,21 +246,39 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
-// Plan: rank every unit by its token count, longest first (ties in unit order), into p.order.
-__global__ __launch_bounds__(1024) void mla_plan_kernel(const MlaParams p) {
-    __shared__ int32_t s_len[kMaxPlanUnits];
+// Plan: rank every unit by its token count, longest first (ties in unit order), into p.order. Workgroup b ranks units
+// [64 b, 64 b + 64): each workgroup loads all n lengths into LDS (entries past n hold -1, below every real length, so
+// they never count), four threads share a unit and each compares it with a quarter of the others, reading four
+// lengths at a time; the quarter counts are summed through LDS. Spread over n / 64 workgroups, the n^2 comparisons take
+// a few microseconds instead of the ~16 us one workgroup needed.
+__global__ __launch_bounds__(256) void mla_plan_kernel(const MlaParams p) {
+    __shared__ __attribute__((aligned(16))) int32_t s_len[kMaxPlanUnits];
+    __shared__ int32_t s_part[256];
+    const int32_t tid = threadIdx.x;
     const int32_t n = p.n_units;
-    for (int32_t u = threadIdx.x; u < n; u += blockDim.x) s_len[u] = unit_tokens(p, u);
+    const int32_t n16 = (n + 15) & ~15;                  // a multiple of 16: four quarters of whole int4 reads
+    for (int32_t v = tid; v < n16; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, v) : -1;
     __syncthreads();
-    for (int32_t u = threadIdx.x; u < n; u += blockDim.x) {
+    const int32_t u = int32_t(blockIdx.x) * 64 + (tid & 63);
+    const int32_t quarter = tid >> 6;
+    int32_t rank = 0;
+    if (u < n) {
         const int32_t mine = s_len[u];
-        int32_t rank = 0;
-        for (int32_t v = 0; v < n; ++v) {
-            const int32_t o = s_len[v];
-            rank += (o > mine) || (o == mine && v < u);
+        const int4* s_len4 = reinterpret_cast<const int4*>(s_len);
+        const int32_t q4 = n16 / 16;                     // int4 entries per quarter
+#pragma unroll 4
+        for (int32_t v4 = quarter * q4; v4 < (quarter + 1) * q4; ++v4) {
+            const int4 o = s_len4[v4];
+            const int32_t v = 4 * v4;
+            rank += (o.x > mine) || (o.x == mine && v < u);
+            rank += (o.y > mine) || (o.y == mine && v + 1 < u);
+            rank += (o.z > mine) || (o.z == mine && v + 2 < u);
+            rank += (o.w > mine) || (o.w == mine && v + 3 < u);
         }
-        p.order[rank] = u;
     }
+    s_part[tid] = rank;
+    __syncthreads();
+    if (tid < 64 && u < n) p.order[s_part[tid] + s_part[tid + 64] + s_part[tid + 128] + s_part[tid + 192]] = u;
 }
 
 // One workgroup per (unit, group of 16 NW heads); wave w of group hg owns heads hg 16 NW + 16 w + [0, 16).
@@ -705,7 +723,7 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.scale_log2 = a.scale * kLog2e;
 
     if (p.order) {
-        hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+        hipLaunchKernelGGL(mla_plan_kernel, dim3(uint32_t((d.n_units + 63) / 64)), dim3(256), 0, stream, p);
         if (int32_t st = check_launch("cp_paged_attn_partial (MLA plan)")) return st;
     }
     const int64_t blocks = d.work_blocks + p.pad_blocks;
