@@ -83,7 +83,7 @@ struct MlaParams {
     int64_t l_ss, l_st;
     float* ws_rec;          // n_units records of rec_floats when n_chunks > 1
     int32_t* order;         // unit of each block, longest first; null: block order
-    int32_t* ws_redo;       // per (unit, head group): 1 when the workgroup's scores outgrew its reference
+    int32_t* ws_redo;       // per workgroup of the first launch: 1 when its scores outgrew their reference
     float* ws_max;          // per (unit, query head): exact score maximum (log2 units) of a unit to redo
     int64_t rec_floats;
     int32_t B, T, P, stripe_begin, S, Hq, max_pages, page_size, max_row_tokens;
@@ -312,6 +312,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     }
     const int32_t rank = blk, hg = 0;                       // one workgroup serves all query heads of a unit
     if (rank >= p.n_units) return;
+    // Redo flags are indexed by workgroup: every workgroup of the first launch clears its own here (early-exit units
+    // included) and sets it below when its scores outgrew the reference, so a workgroup of the redo launch needs one
+    // load to know whether it has anything to do.
+    if (!REDO && threadIdx.x == 0) p.ws_redo[rank] = 0;
+    if (REDO && !p.ws_redo[rank]) return;
     const int32_t u = p.order ? __builtin_amdgcn_readfirstlane(((const_i32_ptr)p.order)[rank]) : rank;
     const Unit x = decode_unit(p, u);
     if (!x.live) return;
@@ -385,7 +390,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     // its outputs unwritten, records the exact maxima and a redo flag, and the REDO launch of this kernel computes the
     // unit again with the exact maxima as references.
     constexpr float kRefSlack = 64.0f;
-    if (REDO && !p.ws_redo[int64_t(u) * p.head_groups + hg]) return;
     float m = REDO ? p.ws_max[int64_t(u) * p.Hq + hw + n16] : neg_inf();
     float m_seen = neg_inf(), l = 0.f;
     bool over = false;
@@ -535,7 +539,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         int32_t any_over = 0;
 #pragma unroll
         for (int v = 0; v < NW; ++v) any_over |= s_over[v];
-        if (threadIdx.x == 0) p.ws_redo[int64_t(u) * p.head_groups + hg] = any_over;
+        if (threadIdx.x == 0) p.ws_redo[rank] = any_over;
         if (any_over) {
             if (c4 == 0) p.ws_max[int64_t(u) * p.Hq + hw + n16] = m_seen;
             return;
