@@ -402,14 +402,18 @@ def test_step_plan_matches_run_step(name, kw):
     batch = pool.build_batch(wl, DEV)
     mo, ml, po, pl, own = pool.run_step(batch)
     plan = pool.StepPlan(batch)
-    plan.out.fill_(7.0)
-    plan.merged.fill_(7.0)
-    pm, pml = plan.run()
-    torch.cuda.synchronize()
-    assert torch.equal(plan.out, po) and torch.equal(plan.lse, pl)
-    assert torch.equal(pm, mo) and torch.equal(pml, ml)
-    if own is not None:
-        assert torch.equal(plan.own_out, own[0]) and torch.equal(plan.own_lse, own[1])
+    for rep in range(3):        # repeated steps into poisoned buffers: every output is rewritten every time
+        plan.out.fill_(7.0)
+        plan.merged.fill_(7.0)
+        if own is not None:
+            plan.own_out.fill_(float("nan"))
+            plan.own_lse.fill_(7.0)
+        pm, pml = plan.run()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, po) and torch.equal(plan.lse, pl)
+        assert torch.equal(pm, mo) and torch.equal(pml, ml)
+        if own is not None:
+            assert torch.equal(plan.own_out, own[0]) and torch.equal(plan.own_lse, own[1])
 
 
 def test_empty_batch_and_empty_context():
