@@ -27,8 +27,9 @@ struct MergeParams {
     int32_t N, T, H, Dv4;
 };
 
-// kV = 1: a thread handles 4 dims of a (token, head); kV = 2: 8 dims (two float4 per partial in flight per thread).
-template <bool kBf16Out, int kV>
+// A thread handles 4 kV dims of a (token, head): kV float4 loads per partial in flight. NMAX >= N bounds the partial
+// arrays (registers), so that wide threads stay within the register file when there are few partials.
+template <bool kBf16Out, int kV, int NMAX>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int32_t Dq = p.Dv4 / kV;                        // threads per (token, head)
@@ -42,10 +43,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     // All loads are issued before any is used (one memory round trip). A partial whose lse is -inf is selected out,
     // never multiplied, so whatever its out row holds cannot reach the result.
     const bool padding = p.token_count != nullptr && t >= *p.token_count;
-    float l[CPATTN_MAX_PARTIALS];
-    f32x4_t o[CPATTN_MAX_PARTIALS][kV];
+    float l[NMAX];
+    f32x4_t o[NMAX][kV];
 #pragma unroll
-    for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
+    for (int i = 0; i < NMAX; ++i) {
         if (i < p.N && !padding) {
             l[i] = p.lse_i[i][int64_t(t) * p.l_st[i] + int64_t(h) * p.l_sh[i]];
             const float* src = p.out_i[i] + int64_t(t) * p.o_st[i] + int64_t(h) * p.o_sh[i] + 4 * d4;
@@ -59,22 +60,22 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     }
     float M = neg_inf();
 #pragma unroll
-    for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) M = fmaxf(M, l[i]);
+    for (int i = 0; i < NMAX; ++i) M = fmaxf(M, l[i]);
     f32x4_t acc[kV];
 #pragma unroll
     for (int v = 0; v < kV; ++v) acc[v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     float lse = neg_inf();
     if (M != neg_inf()) {
-        float w[CPATTN_MAX_PARTIALS];
+        float w[NMAX];
         float tot = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
+        for (int i = 0; i < NMAX; ++i) {
             w[i] = l[i] == neg_inf() ? 0.f : expf(l[i] - M);
             tot += w[i];
         }
         const float inv = 1.0f / tot;
 #pragma unroll
-        for (int i = 0; i < CPATTN_MAX_PARTIALS; ++i) {
+        for (int i = 0; i < NMAX; ++i) {
 #pragma unroll
             for (int v = 0; v < kV; ++v) {
                 const f32x4_t c = (w[i] * inv) * o[i][v];
@@ -140,19 +141,30 @@ extern "C" int32_t cp_lse_merge(const cp_merge_args* a, hipStream_t stream) {
     p.T = a->num_tokens;
     p.H = a->num_heads;
     p.Dv4 = a->head_dim_v / 4;
-    // Eight dims a thread when Dv allows it (unless CPATTN_MERGE_DIMS=4): twice the bytes in flight per thread.
-    static const bool wide_ok = [] {
+    // Dims a thread: 4 * kV with kV as large as Dv and the partial count allow (CPATTN_MERGE_DIMS=4, 8 or 16 caps
+    // it): more bytes in flight per thread. The partial arrays are sized for 5, 9 or 17 partials.
+    static const int dims_cap = [] {
         const char* e = std::getenv("CPATTN_MERGE_DIMS");
-        return !(e && std::atoi(e) == 4);
+        const int v = e ? std::atoi(e) : 16;
+        return v >= 16 ? 16 : v >= 8 ? 8 : 4;
     }();
-    const bool wide = wide_ok && (a->head_dim_v % 8) == 0;
-    const dim3 grid(uint32_t((total / (wide ? 2 : 1) + 255) / 256));
-    if (a->out_dtype == CPATTN_BF16) {
-        if (wide) hipLaunchKernelGGL((lse_merge_kernel<true, 2>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((lse_merge_kernel<true, 1>), grid, dim3(256), 0, stream, p);
+    const int nmax = a->num_partials <= 5 ? 5 : a->num_partials <= 9 ? 9 : 17;
+    int kv = 1;
+    if (dims_cap >= 16 && nmax == 5 && a->head_dim_v % 16 == 0) kv = 4;
+    else if (dims_cap >= 8 && nmax <= 9 && a->head_dim_v % 8 == 0) kv = 2;
+    const dim3 grid(uint32_t((total / kv + 255) / 256));
+    const bool bf = a->out_dtype == CPATTN_BF16;
+#define CPATTN_MERGE_LAUNCH(BF, KV, NM) hipLaunchKernelGGL((lse_merge_kernel<BF, KV, NM>), grid, dim3(256), 0, stream, p)
+    if (nmax == 5) {
+        if (kv == 4) { if (bf) CPATTN_MERGE_LAUNCH(true, 4, 5); else CPATTN_MERGE_LAUNCH(false, 4, 5); }
+        else if (kv == 2) { if (bf) CPATTN_MERGE_LAUNCH(true, 2, 5); else CPATTN_MERGE_LAUNCH(false, 2, 5); }
+        else { if (bf) CPATTN_MERGE_LAUNCH(true, 1, 5); else CPATTN_MERGE_LAUNCH(false, 1, 5); }
+    } else if (nmax == 9) {
+        if (kv == 2) { if (bf) CPATTN_MERGE_LAUNCH(true, 2, 9); else CPATTN_MERGE_LAUNCH(false, 2, 9); }
+        else { if (bf) CPATTN_MERGE_LAUNCH(true, 1, 9); else CPATTN_MERGE_LAUNCH(false, 1, 9); }
     } else {
-        if (wide) hipLaunchKernelGGL((lse_merge_kernel<false, 2>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((lse_merge_kernel<false, 1>), grid, dim3(256), 0, stream, p);
+        if (bf) CPATTN_MERGE_LAUNCH(true, 1, 17); else CPATTN_MERGE_LAUNCH(false, 1, 17);
     }
+#undef CPATTN_MERGE_LAUNCH
     return check_launch("cp_lse_merge");
 }

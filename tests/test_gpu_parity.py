@@ -200,10 +200,12 @@ def test_write_path_and_page_addressing_bit_exact(name, kw, layout):
 
 
 # ----------------------------------------------------------------------------------------------- merge
-def test_merge_edge_cases():
-    say("merge edge cases")
-    g = torch.Generator(device=DEV).manual_seed(5)
-    T, H, Dv, N = 37, 6, 128, 5
+@pytest.mark.parametrize("N,Dv", [(5, 128), (9, 128), (17, 128), (3, 68), (7, 8), (4, 512)])
+def test_merge_edge_cases(N, Dv):
+    """Every width path of the merge (16, 8 or 4 dims a thread; arrays for 5, 9 or 17 partials)."""
+    say(f"merge edge cases N={N} Dv={Dv}")
+    g = torch.Generator(device=DEV).manual_seed(5 + N + Dv)
+    T, H = 37, 6
     outs = [torch.randn(T, H, Dv, generator=g, device=DEV) for _ in range(N)]
     lses = [torch.randn(T, H, generator=g, device=DEV) * 3 for _ in range(N)]
     lses[1][:5] = -float("inf")
