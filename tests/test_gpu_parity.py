@@ -468,3 +468,27 @@ def test_full_size_sampled_rows(name, nsample):
     assert torch.isfinite(res[0][:t]).all() and torch.isfinite(res[1][:t]).all()
     del batch, res
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,nsample", [("llama8b", 6), ("mixed", 5)])
+def test_full_size_bench_configuration_sampled_rows(name, nsample):
+    """The step exactly as the benchmark times it (zero-filled pools, prepared StepPlan, bf16 merged output, the merge
+    told the real token count), repeated, against the oracle on sampled rows at full size."""
+    wl = workloads.make(name)
+    say(f"bench configuration {name}: B={wl.batch}")
+    batch = pool.build_batch(wl, DEV, fill=0.0)
+    plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
+    for _ in range(3):
+        plan.run()
+    torch.cuda.synchronize()
+    own = (plan.own_out, plan.own_lse) if plan.own is not None else None
+    res = (plan.merged, plan.merged_lse, plan.out, plan.lse, own)
+    order = np.argsort(wl.ctx_len + wl.new_len)
+    rng = np.random.default_rng(11)
+    rows = sorted(set([int(order[0]), int(order[-1])] +
+                      [int(x) for x in rng.choice(wl.batch, size=nsample - 2, replace=False)]))
+    w = compare_rows(wl, batch, res, rows, DEV, check_partials=True)
+    check_padding(wl, res)
+    say(f"  rows {rows} worst {w}")
+    del plan, batch, res
+    torch.cuda.empty_cache()
