@@ -77,6 +77,7 @@ struct ExtParams {
     float* lse;
     int64_t l_ss, l_st;
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G, max_pages, page_size, max_row_tokens;
+    int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_qblocks, n_units, pad_tokens_per_block;
     float scale_log2;
 };
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     const int32_t r = p.stripe_begin + s;
     int32_t nkeys;
     if (MODE == kFromPool) {
-        const int32_t L = min(max(((const_i32_ptr)p.ctx_len)[b], 0), p.max_pages * p.page_size);
+        const int32_t L = min(max(((const_i32_ptr)p.ctx_len)[b], 0), p.ctx_cap);
         nkeys = stripe_length(L, r, p.P, p.geo.interleave);
     } else {
         nkeys = min(ntok, (min(row0 + kBlockRows, nrows) - 1) / p.G + 1);   // keys up to the block's last token
@@ -580,6 +581,7 @@ int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.Hkv = a.num_kv_heads;
     p.G = a.num_q_heads / a.num_kv_heads;
     p.max_pages = a.max_pages;
+    p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;

@@ -8,6 +8,14 @@ namespace cpattn {
 // Interleave size of a call (0 in the struct means 1) and the longest stripe of a row with max_ctx_len tokens (stripe
 // 0 holds the most); host-side bounds size launches and workspaces from it.
 inline int32_t interleave_of(const cp_paged_args& a) { return a.interleave > 1 ? a.interleave : 1; }
+// The context length every kernel uses for row b: ctx_len[b] clamped to [0, ctx_cap], ctx_cap the smaller of what the
+// block table can address and the host's bound max_ctx_len (launch sizes and workspaces follow max_ctx_len, so a
+// larger device value must not reach them).
+inline int32_t ctx_cap_of(const cp_paged_args& a) {
+    const int64_t cap = std::min<int64_t>(int64_t(a.max_pages) * a.page_size, a.max_ctx_len > 0 ? a.max_ctx_len : 0);
+    return int32_t(cap);
+}
+
 inline int64_t max_stripe_length(const cp_paged_args& a) {
     return stripe_length(a.max_ctx_len > 0 ? a.max_ctx_len : 0, 0, a.num_partners, interleave_of(a));
 }

@@ -87,6 +87,7 @@ struct MlaParams {
     float* ws_max;          // per (unit, query head): exact score maximum (log2 units) of a unit to redo
     int64_t rec_floats;
     int32_t B, T, P, stripe_begin, S, Hq, max_pages, page_size, max_row_tokens;
+    int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_chunks, chunk_tokens, n_units, pad_blocks, pad_tokens_per_block;
     int32_t head_groups, work_blocks;   // workgroups per unit (1 or 2) and blocks before the padding role
     float scale_log2;
@@ -119,7 +120,7 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
     x.live = x.qtok < ntok;
     x.t = tok0 + x.qtok;
-    const int32_t L = min(max(cl[x.b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(cl[x.b], 0), p.ctx_cap);
     x.Lr = stripe_length(L, p.stripe_begin + x.s, p.P, p.geo.interleave);
     x.j0 = x.c * p.chunk_tokens;
     x.j1 = min(x.j0 + p.chunk_tokens, x.Lr);
@@ -137,7 +138,7 @@ __device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
     const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
     const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
     if (qtok >= min(tok1 - tok0, p.max_row_tokens)) return 0;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
     const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     return max(0, min(Lr - c * p.chunk_tokens, p.chunk_tokens));
 }
@@ -715,6 +716,7 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.S = a.stripe_count;
     p.Hq = a.num_q_heads;
     p.max_pages = a.max_pages;
+    p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
     p.max_row_tokens = std::max(1, a.max_row_tokens);
     p.n_chunks = int32_t(d.n_chunks);

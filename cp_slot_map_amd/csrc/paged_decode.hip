@@ -54,6 +54,7 @@ struct DecodeParams {
     int32_t* ws_blockpref;        // persistent schedule: 64 block offsets + the total step count
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G;
     int32_t max_pages, page_size, max_row_tokens;
+    int32_t ctx_cap;              // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_qtiles, n_chunks, chunk_steps;
     int32_t total_items, pad_blocks, pad_tokens_per_block;
     int32_t rec_rows;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
     const int32_t tile_rows = min(16, nrows - row0);
 
     const int32_t r = p.stripe_begin + s;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
     const int32_t Lr = stripe_length(L, r, p.P, p.geo.interleave);
     const int32_t CH = p.chunk_steps * 16;
     const int32_t nch = (Lr + CH - 1) / CH;
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(64) void gqa_decode_chunk_merge_kernel(const Decode
     const int32_t row0 = qt * 16;
     if (row0 >= nrows) return;
     const int32_t tile_rows = min(16, nrows - row0);
-    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
     const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     const int32_t CH = p.chunk_steps * 16;
     const int32_t nch = (Lr + CH - 1) / CH;
@@ -544,7 +545,7 @@ __device__ __forceinline__ int32_t tile_steps_of(const DecodeParams& p, int32_t 
     const int32_t tok0 = min(max(qrs0, 0), p.T);
     const int32_t tok1 = min(max(qrs1, tok0), p.T);
     const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
-    const int32_t L = min(max(ctx, 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(ctx, 0), p.ctx_cap);
     const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
     return qt * 16 < nrows ? (Lr + 15) >> 4 : 0;
 }
@@ -570,7 +571,7 @@ __device__ __forceinline__ Tile load_tile(const DecodeParams& p, int32_t T) {
     tl.tok0 = min(max(qrs[tl.b], 0), p.T);
     const int32_t tok1 = min(max(qrs[tl.b + 1], tl.tok0), p.T);
     tl.nrows = min(tok1 - tl.tok0, p.max_row_tokens) * p.G;
-    const int32_t L = min(max(cl[tl.b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(cl[tl.b], 0), p.ctx_cap);
     tl.Lr = stripe_length(L, p.stripe_begin + tl.s, p.P, p.geo.interleave);
     tl.n_steps = tl.qt * 16 < tl.nrows ? (tl.Lr + 15) >> 4 : 0;
     return tl;
@@ -1096,6 +1097,7 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.Hkv = a.num_kv_heads;
     p.G = a.num_q_heads / a.num_kv_heads;
     p.max_pages = a.max_pages;
+    p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
     p.n_qtiles = int32_t(d.n_qtiles);

@@ -27,6 +27,7 @@ struct GenericParams {
     float* lse;
     int64_t l_ss, l_st;
     int32_t B, T, P, stripe_begin, Hq, Hkv, G, max_pages, page_size, max_row_tokens;
+    int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     float scale_log2;   // softmax scale (times the key descale for fp8 pools) in log2 units
     float v_scale;      // value descale of fp8 pools, else 1
 };
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p
     if (rb * R >= nrows) return;
 
     const int32_t r = p.stripe_begin + s;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.max_pages * p.page_size);
+    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
     const int32_t Lr = stripe_length(L, r, p.P, p.geo.interleave);
     const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
     const T* Q = static_cast<const T*>(p.q);
@@ -178,6 +179,7 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
     p.Hkv = a.num_kv_heads;
     p.G = a.num_q_heads / a.num_kv_heads;
     p.max_pages = a.max_pages;
+    p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
     const bool fp8 = a.kv_format == CPATTN_KV_FP8_E4M3;

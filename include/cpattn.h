@@ -162,7 +162,8 @@ typedef struct cp_paged_args {
     int32_t head_dim;         /* qk dim: 64 or 128 (GQA), 576 (MLA) */
     int32_t head_dim_v;       /* value dim: equal to head_dim (GQA), 512 (MLA) */
     float scale;              /* softmax scale applied to q.k */
-    int32_t max_ctx_len;      /* host upper bound of ctx_len[b], sizes the launch; larger device values are clamped */
+    int32_t max_ctx_len;      /* host upper bound of ctx_len[b]; sizes the launch and the workspace. A row whose device
+                                 ctx_len exceeds it is taken as its first max_ctx_len tokens (every kernel clamps) */
     int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
     int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
     int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */

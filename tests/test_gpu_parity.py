@@ -492,3 +492,39 @@ def test_full_size_bench_configuration_sampled_rows(name, nsample):
     say(f"  rows {rows} worst {w}")
     del plan, batch, res
     torch.cuda.empty_cache()
+
+
+CLAMP_CASES = [
+    ("decode_balanced", "llama8b", dict(batch=5, ctx_lengths=[9, 400, 1100, 3000, 64]), 1000, False),
+    ("decode_fixed", "llama8b", dict(batch=5, ctx_lengths=[9, 400, 1100, 3000, 64]), 1000, True),
+    ("extend", "mixed", dict(batch=3, new_lengths=[1, 40, 7], ctx_lengths=[500, 3000, 40]), 1000, False),
+    ("mla", "mla", dict(batch=3, ctx_lengths=[7, 130, 2000], num_q_heads=16), 500, False),
+    ("generic", "tiny", dict(ctx_lengths=[1, 17, 100, 200]), 60, False),
+]
+
+
+@pytest.mark.parametrize("case,name,kw,cap,fixed_splits", CLAMP_CASES, ids=[c[0] for c in CLAMP_CASES])
+def test_understated_max_ctx_len_clamps_rows(case, name, kw, cap, fixed_splits):
+    """max_ctx_len sizes the launch and the workspace; a row whose device ctx_len exceeds it is taken as its first
+    max_ctx_len tokens, in every kernel (fixed-split decode, balanced decode, extend, MLA, generic)."""
+    wl = workloads.make(name, **kw)
+    say(f"clamp {case}: ctx={list(wl.ctx_len)} max_ctx_len={cap}")
+    batch = pool.build_batch(wl, DEV)
+    o, l = api.paged_attn_partial(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
+                                  batch.block_table, page_size=wl.page_size, partners=wl.partners, scale=wl.scale,
+                                  kind=wl.kind, max_ctx_len=cap, max_row_tokens=batch.max_row_tokens,
+                                  fixed_splits=fixed_splits, interleave=wl.interleave)
+    torch.cuda.synchronize()
+    qrs = wl.q_row_start
+    for b in range(wl.batch):
+        n = int(wl.new_len[b])
+        if n == 0:
+            continue
+        c = min(int(wl.ctx_len[b]), cap)
+        rv = workloads.row_values(wl, b, DEV)
+        q, k, v = rv.q.cpu(), rv.k_ctx.cpu()[:c], rv.v_ctx.cpu()[:c]
+        t0 = int(qrs[b])
+        for r in range(wl.partners):
+            ro, rl = oracle.stripe_partial(q, k, v, wl.partners, r, wl.scale, wl.interleave)
+            check_out(o[r, t0:t0 + n], ro, f"row {b} stripe {r} out")
+            check_lse(l[r, t0:t0 + n], rl, f"row {b} stripe {r} lse")
