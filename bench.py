@@ -17,6 +17,10 @@ traffic per launch from rocprofv3 counters, scaled by the counter/bytes ratio of
 ``--copy-calibration`` and the profiles directory); it is only filled in when the counters were taken on the current
 kernel build.
 
+`cold_cache` times K further steps with HIP events, each after an untimed 512 MiB write that evicts the 256 MB
+last-level cache (median, 10th and 90th percentiles). `achievable` is the read rate of a plain sequential 2 GiB stream
+(the library's streaming-read kernel, nontemporal loads) on the same device, and the step's and the partial's KV rates as fractions of it.
+
 `cpu_baseline` is the float64 CPU oracle timed on host cores over a bounded sample of the same workload.
 
 Warm-up is at least W steps and at least ``--min-warmup-s`` seconds of steps: the GPU's clocks settle only under
@@ -45,15 +49,18 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_llama8b.json")
 
 
+# Sources the GQA decode kernels are built from: the traffic record stays valid while none of them changes.
+DECODE_SOURCES = ("cp_slot_map_amd/csrc/paged_decode.hip", "cp_slot_map_amd/csrc/common.h",
+                  "cp_slot_map_amd/csrc/launch.h", "include/cpattn.h")
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "cp_slot_map_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode())
-                h.update(fh.read())
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(os.path.basename(rel).encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -87,6 +94,28 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
+def stream_read_rate(nbytes=2 << 30, launches=20):
+    """Read bandwidth (GB/s, median over launches) of the library's plain streaming-read kernel on this device: the
+    achievable denominator next to the nominal HBM peak."""
+    import numpy as np
+    import torch
+
+    from cp_slot_map_amd import api
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16384, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        api.debug_stream_read(buf, sink=sink)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(launches)]
+    for e0, e1 in ev:
+        e0.record()
+        api.debug_stream_read(buf, sink=sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(wl, budget_s):
     """Time the float64 oracle (stripe partials + exact merge per row) on a bounded sample of the workload's rows."""
     import numpy as np
@@ -96,15 +125,20 @@ def cpu_baseline(wl, budget_s):
     import workloads
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        blas_threads = max([p.get("num_threads", 1) for p in info] or [1])
+        blas_lib = ",".join(sorted({str(p.get("internal_api", p.get("prefix", "?"))) for p in info})) or "?"
     except Exception:
-        blas_threads = 1
+        blas_threads, blas_lib = 1, "?"
     order = list(np.argsort(wl.ctx_len))
     rows = [order[0], order[-1]] + [b for b in np.random.default_rng(0).permutation(wl.batch).tolist()
                                     if b not in (order[0], order[-1])]
     spent, kv_bytes, tokens, done = 0.0, 0, 0, []
     per_token = wl.kv_bytes() / max(1, int(wl.ctx_len.astype(np.int64).sum()))
-    for b in rows:
+    # Rows in that order, over again from the start when the whole batch takes less than the budget (a steadier
+    # figure); the budget is checked after each row.
+    passes = max(1, min(50, int(budget_s / 0.5)))
+    for b in rows * passes:
         rv = workloads.row_values(wl, int(b), "cuda")
         q, k, v = rv.q.cpu(), rv.k_ctx.cpu(), rv.v_ctx.cpu()
         if wl.kv_dtype == "fp8":
@@ -124,8 +158,10 @@ def cpu_baseline(wl, budget_s):
     torch.cuda.synchronize()
     return {
         "value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-        "sample": f"{len(done)} of {wl.batch} rows (shortest and longest included), {int(kv_bytes / per_token)} "
-                  f"context tokens, float64 numpy, {spent:.1f} s; query tokens/s {tokens / spent:.2f}",
+        "sample": f"{len(done)} row evaluations over {len(set(done))} of {wl.batch} rows (shortest and longest "
+                  f"included; {len(done) / wl.batch:.1f} passes over the batch), {int(kv_bytes / per_token)} context "
+                  f"tokens, float64 numpy on {blas_lib} with {blas_threads} threads, {spent:.1f} s; query tokens/s "
+                  f"{tokens / spent:.2f}",
         "query_tokens_per_s": round(tokens / spent, 3),
     }
 
@@ -184,6 +220,19 @@ def main():
     wall_ev = time.perf_counter() - t1
     part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    # Cold caches: K more steps, each after an untimed 512 MiB write that evicts the 256 MB last-level cache, timed
+    # with HIP events around the step; median and 10th / 90th percentiles.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        scratch.fill_(i & 0xFF)
+        cold[i][0].record()
+        plan.run()
+        cold[i][1].record()
+    torch.cuda.synchronize()
+    cold_ms = np.array([cold[i][0].elapsed_time(cold[i][1]) for i in range(K)])
+    del scratch
+    read_gbs = stream_read_rate()
 
     ms_per_step = wall * 1e3 / K
     kv_bytes = wl.kv_bytes()
@@ -244,6 +293,13 @@ def main():
                       "merge_avg": round(float(np.mean(merge_ms)), 5),
                       "step_with_events": round(wall_ev * 1e3 / K, 5)},
         "roofline": roof,
+        "cold_cache": {"median_ms": round(float(np.median(cold_ms)), 5),
+                       "p10_ms": round(float(np.percentile(cold_ms, 10)), 5),
+                       "p90_ms": round(float(np.percentile(cold_ms, 90)), 5),
+                       "GBs_at_median": round(kv_bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2)},
+        "achievable": {"kernel": "stream_read_kernel (cp_debug_stream_read, 2 GiB sequential read)",
+                       "read_GBs": round(read_gbs, 2), "value_frac": round(value / read_gbs, 4),
+                       "partial_frac": round(achieved / read_gbs, 4)},
     }
     if flops:
         tflops = flops / (part_avg * 1e-3) / 1e12

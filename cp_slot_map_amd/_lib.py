@@ -77,6 +77,7 @@ EXPORTS = {
     "cp_lse_merge": (_i32, [C.POINTER(MergeArgs), _p]),
     "cp_debug_gather_stripe": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _p, _p]),
+    "cp_debug_stream_read": (_i32, [_p, _i64, _p, _i32, _p]),
 }
 
 _LIB = None

@@ -339,3 +339,18 @@ def debug_gather_stripe(k_pool, block_table_row, ctx_len: int, page_size: int, p
                                           _ptr(block_table_row), int(ctx_len), int(page_size), P, I, int(r), hkv,
                                           D, _ptr(dst), _stream(stream)))
     return dst
+
+
+def debug_stream_read(buf, *, sink=None, stream=None):
+    """Read the bytes of the contiguous device tensor ``buf`` once (the streaming-read reference kernel).
+
+    Returns the int32 sink: one XOR word per workgroup (2048 by default, or ``sink.numel()`` words)."""
+    lib = _lib_handle()
+    _need_cuda(buf)
+    if not buf.is_contiguous():
+        raise ValueError("debug_stream_read: buf must be contiguous")
+    if sink is None:
+        sink = torch.empty(2048, dtype=torch.int32, device=buf.device)
+    _lib.check(lib.cp_debug_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
+                                        _stream(stream)))
+    return sink

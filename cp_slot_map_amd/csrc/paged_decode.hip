@@ -69,6 +69,18 @@ __device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0
 
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// K/V loads. A call reads each context K/V byte once, so the loads carry the nontemporal hint (CPATTN_KV_NONTEMPORAL,
+// default on). On a plain sequential 2 GiB read the hinted loads streamed at ~7.0 TB/s against ~6.3 TB/s for
+// default-policy loads on the same device.
+#ifndef CPATTN_KV_NONTEMPORAL
+#define CPATTN_KV_NONTEMPORAL 1
+#endif
+template <typename V>
+__device__ __forceinline__ V load_kv(const void* p) {
+    if (CPATTN_KV_NONTEMPORAL) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+    return *reinterpret_cast<const V*>(p);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Load mapping. Instruction e of a step reads, for K and V alike, the step tokens 4e + l/16 at head dims
@@ -144,9 +156,9 @@ struct StepData {
 __device__ __forceinline__ void step_load(StepData& d, const uint16_t* __restrict__ kp,
                                           const uint16_t* __restrict__ vp, const StepBase& sb, uint32_t lane_off) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.k[e] = load16(kp + sb.base[e] + lane_off);
+    for (int e = 0; e < 4; ++e) d.k[e] = load_kv<u32x4_t>(kp + sb.base[e] + lane_off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.v[e] = load16(vp + sb.base[e] + lane_off);
+    for (int e = 0; e < 4; ++e) d.v[e] = load_kv<u32x4_t>(vp + sb.base[e] + lane_off);
 }
 
 // fp8 pools: the same lanes and dims, 8 one-byte E4M3 codes per lane and instruction. The codes stay packed while the
@@ -161,9 +173,9 @@ __device__ __forceinline__ void step_load(StepData8& d, const uint16_t* __restri
     const uint8_t* k8 = reinterpret_cast<const uint8_t*>(kp);
     const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vp);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.k[e] = *reinterpret_cast<const u32x2_t*>(k8 + sb.base[e] + lane_off);
+    for (int e = 0; e < 4; ++e) d.k[e] = load_kv<u32x2_t>(k8 + sb.base[e] + lane_off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.v[e] = *reinterpret_cast<const u32x2_t*>(v8 + sb.base[e] + lane_off);
+    for (int e = 0; e < 4; ++e) d.v[e] = load_kv<u32x2_t>(v8 + sb.base[e] + lane_off);
 }
 
 // Eight E4M3 codes (bytes 0..7) to eight bf16 in the same order. E4M3 values are exact in bf16, and the gfx950

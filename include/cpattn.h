@@ -328,6 +328,16 @@ int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_str
                                int32_t num_partners, int32_t interleave, int32_t r, int32_t num_kv_heads,
                                int32_t head_dim, void* dst, hipStream_t stream);
 
+/*
+ * cp_debug_stream_read (measurement support): read `bytes` bytes at `src` (device, 16-byte aligned, bytes a multiple
+ * of 16) once, sequentially, with coalesced 16-byte loads, and write one 32-bit XOR of what each workgroup read into
+ * sink[0 .. blocks) (device, caller-owned, sink_words >= 1 words; blocks = min(sink_words, what the size needs)). Its
+ * duration gives the read bandwidth a plain stream reaches on the device, the achievable denominator next to the
+ * nominal HBM peak when the attention kernels' KV rate is reported. Asynchronous on `stream`.
+ * EINVAL: negative size, bytes not a multiple of 16, src misaligned, sink_words < 1, null pointers (bytes > 0).
+ */
+int32_t cp_debug_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t sink_words, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

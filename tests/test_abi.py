@@ -210,6 +210,16 @@ def test_debug_gather_refusals(lib):
     assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 1, 8, None, None) == _lib.CPATTN_OK
 
 
+def test_stream_read_host_checks(lib):
+    """The streaming-read reference kernel refuses what it cannot read; an empty buffer is a no-op."""
+    assert lib.cp_debug_stream_read(None, 0, None, 1, None) == _lib.CPATTN_OK
+    assert lib.cp_debug_stream_read(None, -16, None, 1, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_stream_read(None, 24, None, 1, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_stream_read(None, 32, None, 0, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_stream_read(None, 32, None, 1, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_debug_stream_read(C.c_void_p(8), 32, C.c_void_p(64), 1, None) == _lib.CPATTN_EINVAL  # misaligned
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     """With no built library the binding raises at load time: there is no non-HIP fallback."""
     monkeypatch.setattr(_lib, "_LIB", None)

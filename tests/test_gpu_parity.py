@@ -528,3 +528,18 @@ def test_understated_max_ctx_len_clamps_rows(case, name, kw, cap, fixed_splits):
             ro, rl = oracle.stripe_partial(q, k, v, wl.partners, r, wl.scale, wl.interleave)
             check_out(o[r, t0:t0 + n], ro, f"row {b} stripe {r} out")
             check_lse(l[r, t0:t0 + n], rl, f"row {b} stripe {r} lse")
+
+
+@pytest.mark.parametrize("nbytes,words", [(16, 2048), (4096 * 8 * 3 + 16 * 37, 2048), (64 << 20, 2048), (1 << 20, 3)])
+def test_stream_read_reads_every_byte(nbytes, words):
+    """The streaming-read reference kernel reads the whole buffer: the XOR of its per-workgroup words is the XOR of
+    every 32-bit word of the buffer (ragged sizes and a sink smaller than the grid would be)."""
+    say(f"stream read {nbytes} bytes, {words} sink words")
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    sink = torch.zeros(words, dtype=torch.int32, device=DEV)
+    api.debug_stream_read(host.to(DEV), sink=sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
