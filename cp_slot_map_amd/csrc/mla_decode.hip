@@ -154,6 +154,13 @@ __device__ __forceinline__ uint64_t token_rows(const MlaParams& p, lds_i32_ptr s
     return reinterpret_cast<uint64_t>(kv_r) + uint64_t(row) * 2u;
 }
 
+// Cache policy of the latent loads: nontemporal (CPATTN_MLA_NONTEMPORAL, default on), as every latent row is read
+// once per call.
+#ifndef CPATTN_MLA_NONTEMPORAL
+#define CPATTN_MLA_NONTEMPORAL 1
+#endif
+constexpr int kLatentCpol = CPATTN_MLA_NONTEMPORAL ? 2 : 0;     // 2: the nt bit of the load's cache-policy field
+
 // Issue the direct-to-LDS loads of one tile.
 //   * value dims [0, 512): wave w takes tokens [T w, T w + T) with T = 32 / NW, one instruction per token: 64 lanes x
 //     16 bytes = the token's 1024 bytes, written to its padded LDS row. The row address is moved to scalar registers
@@ -171,7 +178,7 @@ __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int
         const uint64_t base = (uint64_t(uint32_t(__builtin_amdgcn_readlane(ahi, t))) << 32) |
                               uint32_t(__builtin_amdgcn_readlane(alo, t));
         const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * lane);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t), 16, 0, kLatentCpol);
     }
     constexpr int kRInstr = (kTile / 2) / NW;                                    // 256-byte instructions
 #pragma unroll
@@ -181,7 +188,7 @@ __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int
         const int32_t q = lane & 31;                                             // dword of the 128-byte rope row
         const uint64_t base = (uint64_t(uint32_t(__shfl(int32_t(ahi), t))) << 32) | uint32_t(__shfl(int32_t(alo), t));
         const char* src = reinterpret_cast<const char*>(base) + 1024 + 16 * ((q >> 2) ^ swz(t)) + 4 * (q & 3);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRegionV + kRowR * 2 * pair), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRegionV + kRowR * 2 * pair), 4, 0, kLatentCpol);
     }
 }
 
