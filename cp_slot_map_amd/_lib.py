@@ -75,8 +75,9 @@ EXPORTS = {
     "cp_paged_attn_workspace_size": (_i32, [C.POINTER(PagedArgs), C.POINTER(_i64)]),
     "cp_own_token_attn": (_i32, [C.POINTER(OwnArgs), _p]),
     "cp_lse_merge": (_i32, [C.POINTER(MergeArgs), _p]),
+    "cp_stripe_length": (_i32, [_i32, _i32, _i32, _i32, _i32, C.POINTER(_i32)]),
     "cp_debug_gather_stripe": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i32, _p, _i32, _i32, _i32, _i32, _i32,
-                                      _i32, _i32, _p, _p]),
+                                      _i32, _i32, _p, _i64, C.POINTER(_i32), _p]),
     "cp_debug_stream_read": (_i32, [_p, _i64, _p, _i32, _p]),
 }
 

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import CPATTN_BF16, CPATTN_F32, CPATTN_GQA, CPATTN_MLA, MAX_PARTIALS, PagedArgs, OwnArgs, MergeArgs
 
 __all__ = ["slot_map", "slot_map_rank", "kv_write", "paged_attn_partial", "paged_attn_workspace_size",
-           "own_token_attn", "lse_merge", "debug_gather_stripe", "version"]
+           "own_token_attn", "lse_merge", "stripe_length", "debug_gather_stripe", "version"]
 
 
 def _lib_handle():
@@ -88,14 +88,43 @@ def _pool_strides(pool, kind):
     return pool.stride(0), pool.stride(1), pool.stride(2), pool.stride(3)
 
 
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
 def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partners: int, *, kind="gqa",
              stripe_begin=0, stripe_count=None, sink_slot=-1, stream=None, interleave: int = 1):
-    """Write rows k_src [n, Hkv, D] (v_src [n, Hkv, Dv] or None) into the stripe pools through the slot map."""
+    """Write rows k_src [n, Hkv, D] (v_src [n, Hkv, Dv] or None) into the stripe pools through the slot map.
+
+    Pools hold all P stripes (leading axis P). Rows must have the pools' element type and head shape; MLA rows are
+    [n, 576] or [n, 1, 576]."""
     lib = _lib_handle()
-    _need_cuda(logical_slot, k_src, v_src, k_pool, v_pool)
-    s = logical_slot.to(torch.int64).contiguous()
     if kind == "mla":
         k_src = k_src.reshape(k_src.shape[0], 1, -1)
+    P = int(partners)
+    _need(logical_slot.dim() == 1 and not logical_slot.dtype.is_floating_point,
+          "logical_slot must be a 1-D integer tensor")
+    _need(k_src.dim() == 3, "k_src must be [n, Hkv, D]")
+    _need(k_src.shape[0] == logical_slot.numel(), f"k_src has {k_src.shape[0]} rows for {logical_slot.numel()} slots")
+    _need(k_src.dtype == k_pool.dtype, f"k_src dtype {k_src.dtype} differs from the pool's {k_pool.dtype}", TypeError)
+    _need(k_pool.shape[0] == P, f"pools must hold all {P} stripes on their leading axis (got {k_pool.shape[0]})")
+    if kind == "mla":
+        _need(k_pool.dim() == 4 and k_src.shape[1] == 1 and k_src.shape[2] == k_pool.shape[3],
+              f"MLA rows {tuple(k_src.shape)} do not fit latent pool rows of {k_pool.shape[-1]}")
+        _need(v_src is None, "MLA writes latent rows only (v_src must be None)")
+    else:
+        _need(k_pool.dim() == 5 and tuple(k_src.shape[1:]) == (k_pool.shape[3], k_pool.shape[4]),
+              f"k_src heads/dims {tuple(k_src.shape[1:])} differ from the pool's {tuple(k_pool.shape[3:])}")
+        if v_src is not None:
+            _need(v_pool is not None, "v_src given without v_pool")
+            _need(v_src.dtype == v_pool.dtype == k_pool.dtype, "v_src and the pools must share the dtype", TypeError)
+            _need(v_src.dim() == 3 and v_src.shape[0] == k_src.shape[0] and
+                  tuple(v_src.shape[1:]) == (v_pool.shape[3], v_pool.shape[4]),
+                  f"v_src {tuple(v_src.shape)} does not fit the value pool {tuple(v_pool.shape)}")
+            _need(tuple(v_pool.shape[:4]) == tuple(k_pool.shape[:4]), "K and V pools differ in shape")
+    _need_cuda(logical_slot, k_src, v_src, k_pool, v_pool)
+    s = logical_slot.to(torch.int64).contiguous()
     if k_src.stride(-1) != 1 or (v_src is not None and v_src.stride(-1) != 1):
         raise ValueError("source rows must have a contiguous last dim")
     if v_src is not None and (v_src.stride(0) != k_src.stride(0) or v_src.stride(1) != k_src.stride(1)):
@@ -104,7 +133,6 @@ def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partner
     ss, sp, sl, sh = _pool_strides(k_pool, kind)
     if v_pool is not None and _pool_strides(v_pool, kind) != (ss, sp, sl, sh):
         raise ValueError("K and V pools must share strides")
-    P = int(partners)
     sc = P - stripe_begin if stripe_count is None else int(stripe_count)
     hkv = k_src.shape[1]
     _lib.check(lib.cp_kv_write(_ptr(s), s.numel(), _ptr(k_src), _ptr(v_src), k_src.stride(0), k_src.stride(1),
@@ -191,6 +219,47 @@ def _check_int32_dev(*ts):
             raise TypeError("row offsets, lengths and block tables must be contiguous int32 tensors")
 
 
+def _validate_paged(q, k_pool, v_pool, q_row_start, ctx_len, block_table, kind, P, S, out, lse):
+    """Shape and dtype checks of a partial call, made before anything reaches the library."""
+    _need(q.dim() == 3 and q.stride(2) == 1, "q must be [T, Hq, D] with a contiguous last dim")
+    if kind == "mla":
+        _need(k_pool.dim() == 4, "MLA pool must be [stripe, page, slot, 576]")
+        _need(v_pool is k_pool or v_pool.data_ptr() == k_pool.data_ptr(), "MLA values are the latent rows: "
+              "v_pool must be k_pool")
+        _need(q.shape[2] == k_pool.shape[3], f"q head dim {q.shape[2]} differs from the latent rows' {k_pool.shape[3]}")
+        Dv = 512
+    else:
+        _need(k_pool.dim() == 5 and v_pool is not None and v_pool.dim() == 5,
+              "GQA pools must be [stripe, page, slot, kv_head, dim]")
+        _need(tuple(v_pool.shape[:4]) == tuple(k_pool.shape[:4]), "K and V pools differ in shape")
+        _need(q.shape[2] == k_pool.shape[4], f"q head dim {q.shape[2]} differs from the pool's {k_pool.shape[4]}")
+        _need(q.shape[1] % k_pool.shape[3] == 0, f"{q.shape[1]} query heads over {k_pool.shape[3]} kv heads")
+        _need(v_pool.dtype == k_pool.dtype, "K and V pools must share a dtype", TypeError)
+        Dv = v_pool.shape[4]
+    _need(k_pool.shape[0] == P, f"pools must hold all {P} stripes on their leading axis (got {k_pool.shape[0]})")
+    if k_pool.dtype == torch.float8_e4m3fn:
+        _need(q.dtype == torch.bfloat16, "fp8 pools are read with bf16 queries", TypeError)
+    else:
+        _need(k_pool.dtype == q.dtype, "q and the pools must share a dtype (or the pools hold float8_e4m3fn codes)",
+              TypeError)
+    _check_int32_dev(q_row_start, ctx_len, block_table)
+    B = ctx_len.numel()
+    _need(ctx_len.dim() == 1, "ctx_len must be 1-D [B]")
+    _need(q_row_start.dim() == 1 and q_row_start.numel() == B + 1,
+          f"q_row_start must have B + 1 = {B + 1} entries (got {q_row_start.numel()})")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= B,
+          f"block_table must be [>= {B}, max_pages] (got {tuple(block_table.shape)})")
+    T, Hq = q.shape[0], q.shape[1]
+    if out is not None:
+        _need(out.dtype == torch.float32 and tuple(out.shape) == (S, T, Hq, Dv) and out.stride(3) == 1,
+              f"out must be fp32 [{S}, {T}, {Hq}, {Dv}] with a contiguous last dim (got {out.dtype} "
+              f"{tuple(out.shape)})")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (S, T, Hq) and lse.stride(2) == 1,
+              f"lse must be fp32 [{S}, {T}, {Hq}] with a contiguous last dim (got {lse.dtype} {tuple(lse.shape)})")
+    _need((out is None) == (lse is None), "give both out and lse, or neither")
+
+
 def paged_attn_workspace_size(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
                               kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens,
                               fixed_splits=False, interleave=1, k_descale=1.0, v_descale=1.0):
@@ -218,13 +287,11 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
     float8_e4m3fn pools hold fp8 codes; ``k_descale``/``v_descale`` are their per-tensor descales.
     """
     lib = _lib_handle()
-    _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
-    _check_int32_dev(q_row_start, ctx_len, block_table)
-    if q.dim() != 3 or q.stride(2) != 1:
-        raise ValueError("q must be [T, Hq, D] with a contiguous last dim")
     if kind == "mla" and v_pool is None:
         v_pool = k_pool
     sc = int(partners) - stripe_begin if stripe_count is None else int(stripe_count)
+    _validate_paged(q, k_pool, v_pool, q_row_start, ctx_len, block_table, kind, int(partners), sc, out, lse)
+    _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
     T, Hq = q.shape[0], q.shape[1]
     Dv = 512 if kind == "mla" else v_pool.shape[4]
     if max_ctx_len is None:
@@ -235,8 +302,6 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
         out = torch.empty((sc, T, Hq, Dv), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((sc, T, Hq), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or lse.dtype != torch.float32 or out.stride(3) != 1 or lse.stride(2) != 1:
-        raise ValueError("out/lse must be fp32 with contiguous last dims")
     a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
                     scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
                     max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits,
@@ -257,12 +322,25 @@ def own_token_attn(q, k, v, cu_seqlens, *, scale, num_rows=None, max_row_tokens=
                    stream=None):
     """Causal attention of each row's in-step queries over its in-step K/V: out [T, Hq, D] fp32, lse [T, Hq]."""
     lib = _lib_handle()
-    _need_cuda(q, k, v, cu_seqlens, out, lse)
+    _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [T, H, D]")
+    T, Hq, D = q.shape
+    _need(q.dtype == k.dtype == v.dtype, "q, k and v must share a dtype", TypeError)
+    _need(k.shape[0] == T and tuple(v.shape) == tuple(k.shape) and k.shape[2] == D,
+          f"k {tuple(k.shape)} and v {tuple(v.shape)} must be [{T}, Hkv, {D}]")
+    _need(Hq % k.shape[1] == 0, f"{Hq} query heads over {k.shape[1]} kv heads")
     _check_int32_dev(cu_seqlens)
+    B = cu_seqlens.numel() - 1 if num_rows is None else int(num_rows)
+    _need(cu_seqlens.dim() == 1 and 0 <= B <= cu_seqlens.numel() - 1,
+          f"cu_seqlens must hold num_rows + 1 = {B + 1} entries (got {cu_seqlens.numel()})")
+    if out is not None:
+        _need(out.dtype == torch.float32 and tuple(out.shape) == (T, Hq, D) and out.stride(2) == 1,
+              f"out must be fp32 [{T}, {Hq}, {D}] with a contiguous last dim")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (T, Hq) and lse.stride(1) == 1,
+              f"lse must be fp32 [{T}, {Hq}] with a contiguous last dim")
+    _need_cuda(q, k, v, cu_seqlens, out, lse)
     if q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1 or k.stride() != v.stride():
         raise ValueError("q/k/v need contiguous last dims and k, v the same strides")
-    T, Hq, D = q.shape
-    B = cu_seqlens.numel() - 1 if num_rows is None else int(num_rows)
     if max_row_tokens is None:
         max_row_tokens = int((cu_seqlens[1:B + 1] - cu_seqlens[:B]).max().item()) if B > 0 else 0
     if out is None:
@@ -297,7 +375,22 @@ def lse_merge(outs, lses, *, out_dtype=torch.float32, out=None, lse_out=None, to
     n = len(outs)
     if n != len(lses) or not 1 <= n <= MAX_PARTIALS:
         raise ValueError(f"need 1..{MAX_PARTIALS} partials with matching lses")
+    _need(outs[0].dim() == 3, "partials must be [T, H, Dv]")
     T, H, Dv = outs[0].shape
+    for o, l in zip(outs, lses):
+        _need(o.dtype == torch.float32 and l.dtype == torch.float32, "partials and lses must be fp32", TypeError)
+        _need(tuple(o.shape) == (T, H, Dv) and o.stride(2) == 1,
+              "partials must be fp32 [T, H, Dv] with a contiguous last dim")
+        _need(tuple(l.shape) == (T, H), f"partial lses must be [{T}, {H}] (got {tuple(l.shape)})")
+    if out is not None:
+        _need(out.dtype in (torch.float32, torch.bfloat16) and tuple(out.shape) == (T, H, Dv) and out.stride(2) == 1,
+              f"out must be fp32 or bf16 [{T}, {H}, {Dv}] with a contiguous last dim")
+    if lse_out is not None:
+        _need(lse_out.dtype == torch.float32 and tuple(lse_out.shape) == (T, H) and lse_out.stride(1) == 1,
+              f"lse_out must be fp32 [{T}, {H}] with a contiguous last dim")
+    if token_count is not None:
+        _need(token_count.dtype == torch.int32 and token_count.numel() >= 1, "token_count must be int32 [1]",
+              TypeError)
     _need_cuda(*outs, *lses, out, lse_out, token_count)
     if out is None:
         out = torch.empty((T, H, Dv), dtype=out_dtype, device=outs[0].device)
@@ -308,8 +401,6 @@ def lse_merge(outs, lses, *, out_dtype=torch.float32, out=None, lse_out=None, to
     a.out_dtype = _dtype_code(out.dtype)
     a.token_count = token_count.data_ptr() if token_count is not None else None
     for i, (o, l) in enumerate(zip(outs, lses)):
-        if o.dtype != torch.float32 or l.dtype != torch.float32 or o.stride(2) != 1 or tuple(o.shape) != (T, H, Dv):
-            raise ValueError("partials must be fp32 [T, H, Dv] with a contiguous last dim")
         a.part_out[i] = o.data_ptr()
         a.part_lse[i] = l.data_ptr()
         a.part_out_stride_token[i], a.part_out_stride_head[i] = o.stride(0), o.stride(1)
@@ -322,22 +413,36 @@ def lse_merge(outs, lses, *, out_dtype=torch.float32, out=None, lse_out=None, to
     return out, lse_out
 
 
+def stripe_length(ctx_len: int, page_size: int, partners: int, r: int, *, interleave: int = 1) -> int:
+    """Context tokens of a row that stripe r holds, by the library's own rule (cp_stripe_length)."""
+    lib = _lib_handle()
+    n = C.c_int32(-1)
+    _lib.check(lib.cp_stripe_length(int(ctx_len), int(page_size), int(partners), int(interleave), int(r),
+                                    C.byref(n)))
+    return int(n.value)
+
+
 def debug_gather_stripe(k_pool, block_table_row, ctx_len: int, page_size: int, partners: int, r: int, *,
                         kind="gqa", stream=None, interleave: int = 1):
-    """Stripe r's keys of one row in local order, read with the kernels' own addressing: [Lr, Hkv, D]."""
+    """Stripe r's keys of one row in local order, read with the kernels' own addressing: [Lr, Hkv, D].
+
+    The row count comes from the library (cp_stripe_length) and the gather reports how many rows it wrote; the two
+    must agree."""
     lib = _lib_handle()
     _need_cuda(k_pool, block_table_row)
     _check_int32_dev(block_table_row)
     ss, sp, sl, sh = _pool_strides(k_pool, kind)
     hkv = 1 if kind == "mla" else k_pool.shape[3]
     D = k_pool.shape[-1]
-    P = int(partners)
-    I, L = int(interleave), int(ctx_len)
-    Lr = (L // (I * P)) * I + min(max(L % (I * P) - r * I, 0), I) if I >= 1 else 0   # output rows to allocate
+    P, I = int(partners), int(interleave)
+    Lr = stripe_length(ctx_len, page_size, P, r, interleave=I)
     dst = torch.empty((Lr, hkv, D), dtype=k_pool.dtype, device=k_pool.device)
+    rows = C.c_int32(-1)
     _lib.check(lib.cp_debug_gather_stripe(_ptr(k_pool), _dtype_code(k_pool.dtype), ss, sp, sl, sh, k_pool.shape[1],
                                           _ptr(block_table_row), int(ctx_len), int(page_size), P, I, int(r), hkv,
-                                          D, _ptr(dst), _stream(stream)))
+                                          D, _ptr(dst), Lr, C.byref(rows), _stream(stream)))
+    if rows.value != Lr:
+        raise RuntimeError(f"cp_debug_gather_stripe wrote {rows.value} rows, cp_stripe_length said {Lr}")
     return dst
 
 

@@ -141,17 +141,13 @@ extern "C" int32_t cp_lse_merge(const cp_merge_args* a, hipStream_t stream) {
     p.T = a->num_tokens;
     p.H = a->num_heads;
     p.Dv4 = a->head_dim_v / 4;
-    // Dims a thread: 4 * kV with kV as large as Dv and the partial count allow (CPATTN_MERGE_DIMS=4, 8 or 16 caps
-    // it): more bytes in flight per thread. The partial arrays are sized for 5, 9 or 17 partials.
-    static const int dims_cap = [] {
-        const char* e = std::getenv("CPATTN_MERGE_DIMS");
-        const int v = e ? std::atoi(e) : 16;
-        return v >= 16 ? 16 : v >= 8 ? 8 : 4;
-    }();
+    // Dims a thread: 4 * kV with kV as large as Dv and the partial count allow (more bytes in flight per thread); the
+    // partial arrays are sized for 5, 9 or 17 partials. Every output element is the same function of its inputs
+    // whichever width serves it.
     const int nmax = a->num_partials <= 5 ? 5 : a->num_partials <= 9 ? 9 : 17;
     int kv = 1;
-    if (dims_cap >= 16 && nmax == 5 && a->head_dim_v % 16 == 0) kv = 4;
-    else if (dims_cap >= 8 && nmax <= 9 && a->head_dim_v % 8 == 0) kv = 2;
+    if (nmax == 5 && a->head_dim_v % 16 == 0) kv = 4;
+    else if (nmax <= 9 && a->head_dim_v % 8 == 0) kv = 2;
     const dim3 grid(uint32_t((total / kv + 255) / 256));
     const bool bf = a->out_dtype == CPATTN_BF16;
 #define CPATTN_MERGE_LAUNCH(BF, KV, NM) hipLaunchKernelGGL((lse_merge_kernel<BF, KV, NM>), grid, dim3(256), 0, stream, p)

@@ -399,7 +399,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     // unit again with the exact maxima as references.
     constexpr float kRefSlack = 64.0f;
     float m = REDO ? p.ws_max[int64_t(u) * p.Hq + hw + n16] : neg_inf();
-    float m_seen = neg_inf(), l = 0.f;
+    // l: the fp32 sum of the probabilities (for the LSE); lr: the sum of the bf16-rounded probabilities that the value
+    // product actually weights by (for the normalisation, so that the applied weights sum to one).
+    float m_seen = neg_inf(), l = 0.f, lr = 0.f;
     bool over = false;
     f32x4_t o[32];        // o[kDB hg + b][i]: head 16 hg + 4 c4 + i, dim 16 (kDB w + b) + n16 (unnormalised)
 #pragma unroll
@@ -472,6 +474,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
 #pragma unroll
                 for (int d = 0; d < 4; ++d) pa[d] = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
                 l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                float pr[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    pr[2 * d] = __uint_as_float(pa[d] << 16);
+                    pr[2 * d + 1] = __uint_as_float(pa[d] & 0xffff0000u);
+                }
+                lr += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             }
 
             // Share the probabilities: every wave needs all head groups' for its dim slice.
@@ -558,10 +567,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     // for the waves holding that head's dims), then the normalised partial or this chunk's record.
     const bool split = p.n_chunks > 1 && x.Lr > p.chunk_tokens;
     float* rec = split ? p.ws_rec + int64_t(u) * p.rec_floats : nullptr;
-    float ls = l;
+    float ls = l, lrs = lr;
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
-    if (c4 == 0) s_rowsum[hw + n16] = ls;
+    lrs += __shfl_xor(lrs, 16);
+    lrs += __shfl_xor(lrs, 32);
+    if (c4 == 0) s_rowsum[hw + n16] = lrs;
     __syncthreads();
     // Lane base: head 4 c4 (+ 16 hg + i), dim 16 kDB w + n16 (+ 16 b); head stride of the partial or of the record.
     const int64_t hs = split ? int64_t(kDv) : p.o_sh;
@@ -583,6 +594,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         if (split) {
             rec[int64_t(p.Hq) * kDv + h] = m;
             rec[int64_t(p.Hq) * kDv + p.Hq + h] = ls;
+            rec[int64_t(p.Hq) * kDv + 2 * p.Hq + h] = lrs;
         } else {
             p.lse[int64_t(x.s) * p.l_ss + int64_t(x.t) * p.l_st + h] = ls > 0.f ? (m + log2f(ls)) * kLn2 : neg_inf();
         }
@@ -590,7 +602,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
 }
 
 // Exact merge of the chunk records of every (row, stripe, query token) whose stripe spans several chunks:
-// with M = max_c m_c, o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c and lse = (M + log2 sum_c 2^(m_c - M) l_c) ln 2.
+// with M = max_c m_c, o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) lr_c and lse = (M + log2 sum_c 2^(m_c - M) l_c) ln 2
+// (l_c the fp32 sum of a chunk's probabilities, lr_c the sum of their bf16 roundings that o_c was weighted by).
 // One block of 256 threads per (item, pair of heads); thread i handles head 2 blk + i / 128, dims [4 (i % 128), +4).
 __global__ __launch_bounds__(256) void mla_chunk_merge_kernel(const MlaParams p) {
     const int32_t hpairs = p.Hq / 2;
@@ -603,15 +616,16 @@ __global__ __launch_bounds__(256) void mla_chunk_merge_kernel(const MlaParams p)
     const float* rec0 = p.ws_rec + int64_t(item) * p.n_chunks * p.rec_floats;
     float M = neg_inf();
     for (int32_t c = 0; c < nch; ++c) M = fmaxf(M, rec0[c * p.rec_floats + int64_t(p.Hq) * kDv + h]);
-    float Lsum = 0.f;
+    float Lsum = 0.f, Lr = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int32_t c = 0; c < nch; ++c) {
         const float* rc = rec0 + c * p.rec_floats;
         const float wgt = exp2f(rc[int64_t(p.Hq) * kDv + h] - M);
         Lsum += wgt * rc[int64_t(p.Hq) * kDv + p.Hq + h];
+        Lr += wgt * rc[int64_t(p.Hq) * kDv + 2 * p.Hq + h];
         acc += wgt * *reinterpret_cast<const f32x4_t*>(rc + int64_t(h) * kDv + 4 * d4);
     }
-    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+    const float inv = Lr > 0.f ? 1.0f / Lr : 0.f;
     float* o = p.out + int64_t(x.s) * p.o_ss + int64_t(x.t) * p.o_st + int64_t(h) * p.o_sh + 4 * d4;
     *reinterpret_cast<f32x4_t*>(o) = acc * inv;
     if (d4 == 0) p.lse[int64_t(x.s) * p.l_ss + int64_t(x.t) * p.l_st + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf();
@@ -644,7 +658,7 @@ MlaShape mla_shape(const cp_paged_args& a) {
     d.chunk_tokens = ch;
     d.n_chunks = std::max<int64_t>(1, (max_lr + ch - 1) / ch);
     d.n_units = d.n_items * d.n_chunks;
-    d.rec_floats = int64_t(a.num_q_heads) * (kDv + 2);
+    d.rec_floats = int64_t(a.num_q_heads) * (kDv + 3);
     d.plan = d.n_units <= kMaxPlanUnits;
     d.nw = std::min<int64_t>(8, a.num_q_heads / 16);
     d.head_groups = 1;

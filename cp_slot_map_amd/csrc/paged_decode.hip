@@ -984,35 +984,8 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
     }
 }
 
-static int32_t decode_chunk_steps() {
-    static int32_t steps = [] {
-        const char* e = std::getenv("CPATTN_DECODE_CHUNK_STEPS");
-        int v = e ? std::atoi(e) : 64;
-        if (v < 1) v = 1;
-        if (v > 64) v = 64;
-        return v;
-    }();
-    return steps;
-}
-
-// Prefetch depth of the chunked kernel's step ring (2 or 3 buffers of 8 KB per wave).
-static int32_t decode_depth() {
-    static int32_t depth = [] {
-        const char* e = std::getenv("CPATTN_DECODE_DEPTH");
-        int v = e ? std::atoi(e) : 2;
-        return v == 2 ? 2 : 3;
-    }();
-    return depth;
-}
-
-// Persistent schedule unless CPATTN_DECODE_SCHEDULE=chunked (kept for comparison and for very large tile counts).
-static bool decode_persistent_enabled() {
-    static bool on = [] {
-        const char* e = std::getenv("CPATTN_DECODE_SCHEDULE");
-        return !(e && std::string(e) == "chunked");
-    }();
-    return on;
-}
+// Steps (16 keys each) of one chunk of the fixed-split schedule: splits fall every 1024 keys of a stripe.
+constexpr int32_t kChunkSteps = 64;
 
 constexpr int64_t kMaxPersistWaves = 8192;
 constexpr int64_t kMaxPersistTiles = 4096;
@@ -1029,10 +1002,9 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
     const int64_t rows = int64_t(a.max_row_tokens) * G;
     d.n_qtiles = std::max<int64_t>(1, (rows + 15) / 16);
     d.num_tiles = int64_t(a.num_rows) * a.stripe_count * d.n_qtiles;
-    d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && decode_persistent_enabled() &&
-                   d.num_tiles <= kMaxPersistTiles;
+    d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && d.num_tiles <= kMaxPersistTiles;
     const int64_t max_lr = max_stripe_length(a);
-    const int64_t CH = int64_t(decode_chunk_steps()) * 16;
+    const int64_t CH = int64_t(kChunkSteps) * 16;
     d.n_chunks = d.persistent ? 1 : std::max<int64_t>(1, (max_lr + CH - 1) / CH);
     d.triples = d.num_tiles * a.num_kv_heads;
     d.total_items = d.triples * d.n_chunks;
@@ -1114,7 +1086,7 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.max_row_tokens = a.max_row_tokens;
     p.n_qtiles = int32_t(d.n_qtiles);
     p.n_chunks = int32_t(d.n_chunks);
-    p.chunk_steps = decode_chunk_steps();
+    p.chunk_steps = kChunkSteps;
     p.total_items = int32_t(d.total_items);
     p.pad_tokens_per_block = 4;
     p.pad_blocks = (a.num_tokens + 3) / 4;
@@ -1164,14 +1136,11 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
             case 1: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1, true>), grid, dim3(64), 0, stream, p); break;
             default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2, true>), grid, dim3(64), 0, stream, p); break;
         }
-    } else {
-        switch (decode_depth() * 4 + ppmode) {
-            case 8: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0, false>), grid, dim3(64), 0, stream, p); break;
-            case 9: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1, false>), grid, dim3(64), 0, stream, p); break;
-            case 10: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2, false>), grid, dim3(64), 0, stream, p); break;
-            case 12: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 0, false>), grid, dim3(64), 0, stream, p); break;
-            case 13: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 1, false>), grid, dim3(64), 0, stream, p); break;
-            default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<3, 2, false>), grid, dim3(64), 0, stream, p); break;
+    } else {     // bf16 pools: the same two-buffer ring (the next step's loads in flight while one is computed)
+        switch (ppmode) {
+            case 0: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 0, false>), grid, dim3(64), 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 1, false>), grid, dim3(64), 0, stream, p); break;
+            default: hipLaunchKernelGGL((gqa_decode_bf16_kernel<2, 2, false>), grid, dim3(64), 0, stream, p); break;
         }
     }
     if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode)")) return st;

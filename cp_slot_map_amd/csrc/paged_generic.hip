@@ -238,23 +238,37 @@ __global__ void gather_stripe_kernel(const T* __restrict__ pool, PoolGeom geo, c
 
 using namespace cpattn;
 
-extern "C" int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe,
-                                          int64_t kv_stride_page, int64_t kv_stride_slot, int64_t kv_stride_head,
-                                          int32_t num_pages, const int32_t* block_table_row, int32_t ctx_len,
-                                          int32_t page_size, int32_t num_partners, int32_t interleave, int32_t r,
-                                          int32_t num_kv_heads, int32_t head_dim, void* dst, hipStream_t stream) {
-    if (num_partners < 1 || interleave < 1 || page_size < 1 || page_size % num_partners ||
+extern "C" int32_t cp_stripe_length(int32_t ctx_len, int32_t page_size, int32_t num_partners, int32_t interleave,
+                                    int32_t r, int32_t* len_out) {
+    if (num_partners < 1 || num_partners > 16 || interleave < 1 || page_size < 1 || page_size % num_partners ||
         (page_size / num_partners) % interleave)
         return fail(CPATTN_EINVAL, "bad geometry (page_size=%d, P=%d, interleave=%d)", page_size, num_partners,
                     interleave);
     if (r < 0 || r >= num_partners) return fail(CPATTN_EINVAL, "stripe %d outside [0, %d)", r, num_partners);
-    if (ctx_len < 0 || num_kv_heads < 1 || head_dim < 1 || num_pages < 1)
-        return fail(CPATTN_EINVAL, "negative or zero size");
+    if (ctx_len < 0) return fail(CPATTN_EINVAL, "ctx_len = %d is negative", ctx_len);
+    if (!len_out) return fail(CPATTN_EINVAL, "cp_stripe_length: len_out is null");
+    *len_out = stripe_length(ctx_len, r, num_partners, interleave);
+    return CPATTN_OK;
+}
+
+extern "C" int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe,
+                                          int64_t kv_stride_page, int64_t kv_stride_slot, int64_t kv_stride_head,
+                                          int32_t num_pages, const int32_t* block_table_row, int32_t ctx_len,
+                                          int32_t page_size, int32_t num_partners, int32_t interleave, int32_t r,
+                                          int32_t num_kv_heads, int32_t head_dim, void* dst, int64_t dst_rows,
+                                          int32_t* rows_out, hipStream_t stream) {
+    int32_t Lr = 0;
+    if (int32_t st = cp_stripe_length(ctx_len, page_size, num_partners, interleave, r, &Lr)) return st;
+    if (num_kv_heads < 1 || head_dim < 1 || num_pages < 1) return fail(CPATTN_EINVAL, "negative or zero size");
     if (kv_stride_stripe < 0 || kv_stride_page < 0 || kv_stride_slot < 0 || kv_stride_head < 0)
         return fail(CPATTN_EINVAL, "negative stride");
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16 && dtype != CPATTN_FP8_E4M3)
         return fail(CPATTN_EINVAL, "dtype %d unknown", dtype);
-    const int32_t Lr = stripe_length(ctx_len, r, num_partners, interleave);
+    if (!rows_out) return fail(CPATTN_EINVAL, "cp_debug_gather_stripe: rows_out is null");
+    if (dst_rows < Lr)
+        return fail(CPATTN_EINVAL, "cp_debug_gather_stripe: stripe %d holds %d tokens, dst has room for %lld", r, Lr,
+                    (long long)dst_rows);
+    *rows_out = Lr;
     if (Lr == 0) return CPATTN_OK;
     if (!k_pool || !block_table_row || !dst) return fail(CPATTN_EINVAL, "cp_debug_gather_stripe: null pointer");
     PoolGeom geo{kv_stride_stripe, kv_stride_page, kv_stride_slot, kv_stride_head, page_size / num_partners,

@@ -315,18 +315,33 @@ typedef struct cp_merge_args {
 int32_t cp_lse_merge(const cp_merge_args* args, hipStream_t stream);
 
 /*
+ * cp_stripe_length: how many of a row's context tokens stripe r holds (host call; nothing is enqueued).
+ *
+ * Source: the slot rule of mstar PR #1124 (PR description) places logical slot s on partner s mod P; with P dividing
+ * page_size the row's context position t lands on partner t mod P, so stripe r holds the positions r, r + P, ... below
+ * ctx_len: ceil((ctx_len - r) / P) of them (0 when ctx_len <= r). With an interleave size I (the placement of
+ * cp_slot_map) it holds the positions t with floor(t / I) mod P == r. This is the stripe length every attention kernel
+ * uses (the same function), exported so that callers and tests size per-stripe buffers from the library's own rule.
+ *   len_out  host int32: the stripe length.
+ * EINVAL: P outside [1, 16], I < 1, page_size % (I * P) != 0, r outside [0, P), ctx_len < 0, len_out null.
+ */
+int32_t cp_stripe_length(int32_t ctx_len, int32_t page_size, int32_t num_partners, int32_t interleave, int32_t r,
+                         int32_t* len_out);
+
+/*
  * cp_debug_gather_stripe (test support): copy stripe r's keys of one row, in local order, into a dense buffer, through
  * the same device addressing function the attention kernels use, so page addressing can be checked bit for bit.
- *   dst (i, g, d) at dst + (i*num_kv_heads + g)*head_dim + d for i below stripe r's length (ceil((ctx_len - r) / P)
- *   for I = 1), same dtype as the pool.
+ *   dst (i, g, d) at dst + (i*num_kv_heads + g)*head_dim + d for i below stripe r's length (cp_stripe_length), same
+ *   dtype as the pool; dst_rows is its capacity in rows (tokens).
+ *   rows_out: host int32, set to the number of rows written (the stripe length) when the call is accepted.
  *   block_table_row: device int32 [>= ceil(ctx_len / page_size)].
- * EINVAL: bad geometry, r outside [0, P), null pointers, negative sizes.
+ * EINVAL: bad geometry, r outside [0, P), null pointers, negative sizes, dst_rows below the stripe length.
  */
 int32_t cp_debug_gather_stripe(const void* k_pool, int32_t dtype, int64_t kv_stride_stripe, int64_t kv_stride_page,
                                int64_t kv_stride_slot, int64_t kv_stride_head, int32_t num_pages,
                                const int32_t* block_table_row, int32_t ctx_len, int32_t page_size,
                                int32_t num_partners, int32_t interleave, int32_t r, int32_t num_kv_heads,
-                               int32_t head_dim, void* dst, hipStream_t stream);
+                               int32_t head_dim, void* dst, int64_t dst_rows, int32_t* rows_out, hipStream_t stream);
 
 /*
  * cp_debug_stream_read (measurement support): read `bytes` bytes at `src` (device, 16-byte aligned, bytes a multiple

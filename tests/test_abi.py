@@ -204,10 +204,34 @@ def test_kv_write_refusals(lib):
 
 
 def test_debug_gather_refusals(lib):
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 1, 4, 1, 8, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 1, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 8, 0, 1, 8, None, None) == _lib.CPATTN_EINVAL
-    assert lib.cp_debug_gather_stripe(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 1, 8, None, None) == _lib.CPATTN_OK
+    n = C.c_int32(-1)
+    g = lib.cp_debug_gather_stripe
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 1, 4, 1, 8, None, 99, C.byref(n), None) == _lib.CPATTN_EINVAL
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 3, 1, 0, 1, 8, None, 99, C.byref(n), None) == _lib.CPATTN_EINVAL
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 8, 0, 1, 8, None, 99, C.byref(n), None) == _lib.CPATTN_EINVAL
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 0, 16, 4, 1, 1, 1, 8, None, 0, C.byref(n), None) == _lib.CPATTN_OK
+    assert n.value == 0
+    # stripe 1 of a 10-token row at P = 4 holds positions 1, 5, 9: a destination of two rows is refused
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 1, 1, 1, 8, None, 2, C.byref(n), None) == _lib.CPATTN_EINVAL
+    assert "room" in _err(lib)
+    assert g(None, 1, 0, 0, 0, 0, 4, None, 10, 16, 4, 1, 1, 1, 8, None, 3, None, None) == _lib.CPATTN_EINVAL
+
+
+def test_stripe_length_matches_the_oracle(lib):
+    """cp_stripe_length (the function every kernel uses) against the oracle's count of the positions a stripe holds,
+    for plain and interleaved placements."""
+    import oracle
+    n = C.c_int32(-1)
+    for P, I, ps in [(1, 1, 16), (2, 1, 16), (4, 1, 16), (8, 1, 16), (16, 1, 16), (4, 2, 16), (4, 4, 16), (2, 8, 16),
+                     (4, 16, 64), (3, 2, 12)]:
+        for L in list(range(0, 70)) + [255, 1031, 4096, 8193]:
+            for r in range(P):
+                assert lib.cp_stripe_length(L, ps, P, I, r, C.byref(n)) == _lib.CPATTN_OK
+                assert n.value == oracle.stripe_len(L, P, r, I), (P, I, L, r)
+    assert lib.cp_stripe_length(10, 16, 3, 1, 0, C.byref(n)) == _lib.CPATTN_EINVAL      # P does not divide 16
+    assert lib.cp_stripe_length(10, 16, 4, 1, 4, C.byref(n)) == _lib.CPATTN_EINVAL      # r outside [0, P)
+    assert lib.cp_stripe_length(-1, 16, 4, 1, 0, C.byref(n)) == _lib.CPATTN_EINVAL
+    assert lib.cp_stripe_length(10, 16, 4, 1, 0, None) == _lib.CPATTN_EINVAL
 
 
 def test_stream_read_host_checks(lib):
@@ -236,3 +260,107 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+# ------------------------------------------------------------------ binding checks (before any library call)
+# The binding checks shapes and dtypes before it hands pointers to the library, so a mismatched tensor never reaches a
+# kernel. CPU tensors serve here: with consistent shapes the binding gets as far as its device check.
+def _gqa_tensors(dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    P, pages, pp, hkv, D, T, Hq, B = 4, 6, 4, 2, 128, 3, 8, 2
+    return dict(
+        q=torch.zeros(T, Hq, D, dtype=dt), k_pool=torch.zeros(P, pages, pp, hkv, D, dtype=dt),
+        v_pool=torch.zeros(P, pages, pp, hkv, D, dtype=dt), q_row_start=torch.tensor([0, 1, 3], dtype=torch.int32),
+        ctx_len=torch.tensor([5, 9], dtype=torch.int32), block_table=torch.zeros(B, 3, dtype=torch.int32))
+
+
+def _partial(**over):
+    from cp_slot_map_amd import api
+    t = _gqa_tensors()
+    t.update(over)
+    return api.paged_attn_partial(t["q"], t["k_pool"], t["v_pool"], t["q_row_start"], t["ctx_len"],
+                                  t["block_table"], page_size=16, partners=4, scale=0.1, max_ctx_len=9,
+                                  max_row_tokens=2, out=over.get("out"), lse=over.get("lse"))
+
+
+def test_binding_partial_checks():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        _partial()                                                  # consistent shapes reach the device check
+    with pytest.raises(ValueError, match="head dim"):
+        _partial(q=torch.zeros(3, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="B \\+ 1"):
+        _partial(q_row_start=torch.tensor([0, 1], dtype=torch.int32))
+    with pytest.raises(ValueError, match="block_table"):
+        _partial(block_table=torch.zeros(1, 3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out must be"):
+        _partial(out=torch.zeros(4, 3, 8, 64), lse=torch.zeros(4, 3, 8))
+    with pytest.raises(ValueError, match="lse must be"):
+        _partial(out=torch.zeros(4, 3, 8, 128), lse=torch.zeros(4, 3, 7))
+    with pytest.raises(ValueError, match="out must be"):
+        _partial(out=torch.zeros(4, 3, 8, 128, dtype=torch.bfloat16), lse=torch.zeros(4, 3, 8))
+    with pytest.raises(TypeError):
+        _partial(q=torch.zeros(3, 8, 128, dtype=torch.float32))     # q and pools differ
+    with pytest.raises(TypeError):
+        _partial(ctx_len=torch.tensor([5, 9], dtype=torch.int64))
+    with pytest.raises(ValueError, match="stripes"):
+        _partial(k_pool=torch.zeros(2, 6, 4, 2, 128, dtype=torch.bfloat16),
+                 v_pool=torch.zeros(2, 6, 4, 2, 128, dtype=torch.bfloat16))
+
+
+def test_binding_kv_write_checks():
+    import torch
+    from cp_slot_map_amd import api
+    t = _gqa_tensors()
+    s = torch.arange(5, dtype=torch.int64)
+    k = torch.zeros(5, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        api.kv_write(s, k, k, t["k_pool"], t["v_pool"], 16, 4)
+    fp8 = torch.zeros(4, 6, 4, 2, 128, dtype=torch.float8_e4m3fn)
+    with pytest.raises(TypeError, match="dtype"):
+        api.kv_write(s, k, k, fp8, fp8, 16, 4)                      # bf16 rows into an fp8 pool
+    with pytest.raises(ValueError, match="heads"):
+        api.kv_write(s, torch.zeros(5, 4, 128, dtype=torch.bfloat16), None, t["k_pool"], None, 16, 4)
+    with pytest.raises(ValueError, match="rows"):
+        api.kv_write(s[:4], k, k, t["k_pool"], t["v_pool"], 16, 4)
+    with pytest.raises(ValueError, match="value pool"):
+        api.kv_write(s, k, torch.zeros(5, 2, 64, dtype=torch.bfloat16), t["k_pool"], t["v_pool"], 16, 4)
+    lat = torch.zeros(4, 6, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="latent"):
+        api.kv_write(s, torch.zeros(5, 512, dtype=torch.bfloat16), None, lat, None, 64, 4, kind="mla")
+
+
+def test_binding_merge_checks():
+    import torch
+    from cp_slot_map_amd import api
+    outs = [torch.zeros(3, 4, 8) for _ in range(2)]
+    lses = [torch.zeros(3, 4) for _ in range(2)]
+    with pytest.raises(ValueError, match="GPU"):
+        api.lse_merge(outs, lses)
+    with pytest.raises(ValueError, match="out must be"):
+        api.lse_merge(outs, lses, out=torch.zeros(3, 4, 4))
+    with pytest.raises(ValueError, match="lse_out"):
+        api.lse_merge(outs, lses, lse_out=torch.zeros(4, 3).t())    # heads not contiguous
+    with pytest.raises(ValueError, match="lses must be"):
+        api.lse_merge(outs, [lses[0], torch.zeros(3, 5)])
+    with pytest.raises(TypeError):
+        api.lse_merge(outs, lses, token_count=torch.zeros(1, dtype=torch.int64))
+
+
+def test_binding_own_token_checks():
+    import torch
+    from cp_slot_map_amd import api
+    q = torch.zeros(6, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(6, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 2, 5], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        api.own_token_attn(q, k, k, cu, scale=0.1)
+    with pytest.raises(ValueError, match="must be"):
+        api.own_token_attn(q, torch.zeros(5, 2, 128, dtype=torch.bfloat16), k, cu, scale=0.1)
+    with pytest.raises(ValueError, match="out must be"):
+        api.own_token_attn(q, k, k, cu, scale=0.1, out=torch.zeros(6, 8, 64))
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        api.own_token_attn(q, k, k, cu, scale=0.1, num_rows=3)
+    with pytest.raises(TypeError):
+        api.own_token_attn(q, k.float(), k, cu, scale=0.1)
