@@ -23,16 +23,21 @@
 //   * scores S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_bf16: A = latent rows (token per lane, 8 dims per
 //     lane group), B = the wave's query heads, held in registers for the whole unit. 36 MFMAs.
 //   * softmax in log2 units against a fixed per-head reference, the maximum of the unit's first tile; later scores
-//     may exceed it by up to 64 without rescaling anything (a unit whose scores rise further is repeated with the
-//     exact maximum as reference). The accumulators are thus written only by MFMAs and stay in the accumulation
-//     registers. The running sum adds the fp32 probabilities, so the lse keeps fp32 accuracy; the value product takes
-//     them rounded to bf16 (a relative change of at most 2^-9 per weight, which averages out over a stripe's tokens).
-//   * the probabilities (bf16) go to the wave's slot of the LDS probability buffer in the A-operand layout the score
+//     may exceed it by up to 15 without rescaling anything (p <= 2^15 stays inside the fp16 range; a unit whose
+//     scores rise further is repeated with the exact maximum as reference). The accumulators are thus written only by
+//     MFMAs and stay in the accumulation registers. The running sum adds the fp32 probabilities, so the lse keeps fp32
+//     accuracy.
+//   * the value product weights by the probabilities rounded to fp16 (11 significant bits) and the output is
+//     normalised by the sum of exactly those rounded weights, so the applied weights sum to one. One bf16 rounding
+//     (8 bits) put a two-token stripe 2.5e-3 away from the float64 result; with fp16 weights the error bound is
+//     eight times smaller, at the cost of widening each value operand from bf16 to fp16 in registers (exact for the
+//     latent's magnitudes: values must stay below 65504 in magnitude).
+//   * the probabilities (fp16) go to the wave's slot of the LDS probability buffer in the A-operand layout the score
 //     product leaves (k index 8c + e of lane group c is tile token 16 (e / 4) + 4c + e % 4); one barrier.
-//   * out += P . V with v_mfma_f32_16x16x32_bf16 over the wave's 32 / NW dim blocks and the NW head groups: A = a head
+//   * out += P . V with v_mfma_f32_16x16x32_f16 over the wave's 32 / NW dim blocks and the NW head groups: A = a head
 //     group's probabilities (one 16-byte LDS read per lane), B = a 16-dim value block from two transposed LDS reads
-//     (ds_read_b64_tr_b16) in the same k order, so no register staging or permutes are needed. 32 MFMAs into 128
-//     accumulator registers.
+//     (ds_read_b64_tr_b16) in the same k order, widened to fp16, so no register staging or permutes are needed. 32
+//     MFMAs into 128 accumulator registers.
 //
 // LDS layout of a tile (37,888 bytes; four buffers): the value dims [0, 512) of token t in a row of 1056 bytes at
 // 1056 t (1024 bytes of data, 32 of padding), the rope dims [512, 576) in a 128-byte row at 33,792 + 128 t whose eight
@@ -96,6 +101,23 @@ struct MlaParams {
 __device__ __forceinline__ int swz(int t) { return (t ^ (t >> 2)) & 7; }   // rope-region piece swizzle
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+
+// Eight bf16 values (packed pairs) to eight fp16 values in the same order: exact for magnitudes in [2^-14, 65504],
+// within 2^-25 absolute below that.
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(u32x4_t v) {
+    u32x4_t r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) r[d] = pack2_f16(__uint_as_float(v[d] << 16), __uint_as_float(v[d] & 0xffff0000u));
+    return __builtin_bit_cast(f16x8_t, r);
+}
 
 struct Unit {
     int32_t b, s, qtok, c;
@@ -397,7 +419,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     // only by MFMAs and stay in the accumulation registers. Should a head's scores rise further, the workgroup leaves
     // its outputs unwritten, records the exact maxima and a redo flag, and the REDO launch of this kernel computes the
     // unit again with the exact maxima as references.
-    constexpr float kRefSlack = 64.0f;
+    constexpr float kRefSlack = 15.0f;
     float m = REDO ? p.ws_max[int64_t(u) * p.Hq + hw + n16] : neg_inf();
     // l: the fp32 sum of the probabilities (for the LSE); lr: the sum of the bf16-rounded probabilities that the value
     // product actually weights by (for the normalisation, so that the applied weights sum to one).
@@ -472,14 +494,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fminf(sv[e] - m, kRefSlack));
 #pragma unroll
-                for (int d = 0; d < 4; ++d) pa[d] = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
+                for (int d = 0; d < 4; ++d) pa[d] = pack2_f16(pv[2 * d], pv[2 * d + 1]);
                 l += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                const f16x8_t ph = __builtin_bit_cast(f16x8_t, pa);
                 float pr[8];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    pr[2 * d] = __uint_as_float(pa[d] << 16);
-                    pr[2 * d + 1] = __uint_as_float(pa[d] & 0xffff0000u);
-                }
+                for (int e = 0; e < 8; ++e) pr[e] = float(ph[e]);
                 lr += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             }
 
@@ -493,33 +513,34 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             auto vop = [&](int b) __attribute__((always_inline)) {
                 const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 32 * b));
                 const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vb + 16 * kRowV + 32 * b));
-                return __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                return bf16x8_to_f16(
+                    __builtin_bit_cast(u32x4_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
             };
             auto pop = [&](int hg) __attribute__((always_inline)) {
-                return as_bf16x8(*(const __attribute__((address_space(3))) u32x4_t*)(prob_r + 1024 * hg));
+                return __builtin_bit_cast(f16x8_t, *(const __attribute__((address_space(3))) u32x4_t*)(prob_r + 1024 * hg));
             };
             if constexpr (NW >= 8) {                // hold the kDB value operands, stream the head groups
-                bf16x8_t vv[kDB];
+                f16x8_t vv[kDB];
 #pragma unroll
                 for (int b = 0; b < kDB; ++b) vv[b] = vop(b);
 #pragma unroll
                 for (int hg = 0; hg < NW; ++hg) {
-                    const bf16x8_t a = pop(hg);
+                    const f16x8_t a = pop(hg);
 #pragma unroll
                     for (int b = 0; b < kDB; ++b)
-                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vv[b], o[kDB * hg + b], 0, 0, 0);
+                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, vv[b], o[kDB * hg + b], 0, 0, 0);
                 }
                 sched_pv<kDB, NW, 2 * kDB + 2, 1>();  // value operands and two head groups ahead, then one read per group
             } else {                                // hold the NW probability operands, stream the value blocks
-                bf16x8_t pp[NW];
+                f16x8_t pp[NW];
 #pragma unroll
                 for (int hg = 0; hg < NW; ++hg) pp[hg] = pop(hg);
 #pragma unroll
                 for (int b = 0; b < kDB; ++b) {
-                    const bf16x8_t v = vop(b);
+                    const f16x8_t v = vop(b);
 #pragma unroll
                     for (int hg = 0; hg < NW; ++hg)
-                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[hg], v, o[kDB * hg + b], 0, 0, 0);
+                        o[kDB * hg + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[hg], v, o[kDB * hg + b], 0, 0, 0);
                 }
                 sched_pv<NW, kDB, NW + 4, 2>();       // probabilities and two value blocks ahead, then one block per group
             }

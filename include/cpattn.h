@@ -220,6 +220,11 @@ typedef struct cp_paged_args {
  * its descale in fp32 (the key descale folded into the score scale, the value descale applied to the normalised
  * output).
  *
+ * Precision. Scores and sums accumulate in fp32. The value product weights by the probabilities held to about 16
+ * significant bits (GQA: a bf16 pair high + residual) or 11 (bf16 MLA: fp16 weights, and the bf16 latent values widened
+ * to fp16 for that product, so bf16 MLA latent values must stay below 65504 in magnitude), and every output is
+ * normalised by the sum of the weights actually applied.
+ *
  * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, an unknown kv_format, fp8 pools with dtype other
  * than bf16, a descale that is not finite and positive or MLA with k_descale != v_descale, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
