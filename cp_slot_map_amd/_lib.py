@@ -73,6 +73,8 @@ EXPORTS = {
                            _i32, _i32, _i32, _i32, _i32, _i32, _i64, _p]),
     "cp_paged_attn_partial": (_i32, [C.POINTER(PagedArgs), _p]),
     "cp_paged_attn_workspace_size": (_i32, [C.POINTER(PagedArgs), C.POINTER(_i64)]),
+    "cp_paged_attn_partial_noalloc": (_i32, [C.POINTER(PagedArgs), _p]),
+    "cp_paged_attn_noalloc_scratch_bytes": (_i64, []),
     "cp_own_token_attn": (_i32, [C.POINTER(OwnArgs), _p]),
     "cp_lse_merge": (_i32, [C.POINTER(MergeArgs), _p]),
     "cp_stripe_length": (_i32, [_i32, _i32, _i32, _i32, _i32, C.POINTER(_i32)]),

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import CPATTN_BF16, CPATTN_F32, CPATTN_GQA, CPATTN_MLA, MAX_PARTIALS, PagedArgs, OwnArgs, MergeArgs
 
 __all__ = ["slot_map", "slot_map_rank", "kv_write", "paged_attn_partial", "paged_attn_workspace_size",
-           "own_token_attn", "lse_merge", "stripe_length", "debug_gather_stripe", "version"]
+           "own_token_attn", "lse_merge", "stripe_length", "debug_gather_stripe", "version",
+           "paged_attn_partial_noalloc", "noalloc_scratch_bytes"]
 
 
 def _lib_handle():
@@ -316,6 +317,32 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
         a.workspace_bytes = ws.numel() * ws.element_size()
     _lib.check(lib.cp_paged_attn_partial(C.byref(a), _stream(stream)))
     return out, lse
+
+
+def paged_attn_partial_noalloc(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
+                               kind="gqa", stripe_begin=0, stripe_count=None, max_ctx_len, max_row_tokens, out, lse,
+                               stream=None, fixed_splits=False, interleave=1, k_descale=1.0, v_descale=1.0):
+    """cp_paged_attn_partial_noalloc: the partial call with the library's static device scratch as its workspace.
+
+    Allocates nothing: the caller passes ``out`` [S, T, Hq, Dv] and ``lse`` [S, T, Hq] (fp32) and the host bounds
+    ``max_ctx_len`` and ``max_row_tokens`` (no device read)."""
+    lib = _lib_handle()
+    if kind == "mla" and v_pool is None:
+        v_pool = k_pool
+    sc = int(partners) - stripe_begin if stripe_count is None else int(stripe_count)
+    _need(out is not None and lse is not None, "the no-allocation call writes into caller-provided out and lse")
+    _validate_paged(q, k_pool, v_pool, q_row_start, ctx_len, block_table, kind, int(partners), sc, out, lse)
+    _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse)
+    a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=partners,
+                    scale=scale, kind=kind, stripe_begin=stripe_begin, stripe_count=sc, max_ctx_len=max_ctx_len,
+                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=q.shape[0],
+                    fixed_splits=fixed_splits, interleave=interleave, k_descale=k_descale, v_descale=v_descale)
+    _lib.check(lib.cp_paged_attn_partial_noalloc(C.byref(a), _stream(stream)))
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_lib_handle().cp_paged_attn_noalloc_scratch_bytes())
 
 
 def own_token_attn(q, k, v, cu_seqlens, *, scale, num_rows=None, max_row_tokens=None, out=None, lse=None,

@@ -2,9 +2,16 @@
 // can be made on the host passes; device-resident values are clamped inside the kernels.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
+
+// Scratch of cp_paged_attn_partial_noalloc: a file-scope device array, one copy on every device the library runs on,
+// held until the process ends. Host code never uses its name as an address: the address of the current device's copy
+// comes from hipGetSymbolAddress, once per device, and that pointer is what the kernels receive.
+#define CPATTN_NOALLOC_SCRATCH_BYTES (int64_t(64) << 20)
+static __device__ __align__(256) unsigned char scratch[CPATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace cpattn {
 
@@ -81,13 +88,18 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
             return fail(CPATTN_EUNSUPPORTED, "GQA is built for head_dim = head_dim_v in {64, 128} (got %d, %d)",
                         a.head_dim, a.head_dim_v);
     }
+    const int32_t pp = a.page_size / a.num_partners;
+    *geo = PoolGeom{a.kv_stride_stripe, a.kv_stride_page, a.kv_stride_slot, a.kv_stride_head, pp, ilog2_exact(pp),
+                    a.num_pages, ilv};
+    return CPATTN_OK;
+}
+
+// Pointer checks of a call that launches (the workspace-size query takes the shapes only).
+static int32_t check_paged_pointers(const cp_paged_args& a) {
     if (a.num_tokens > 0 && (!a.out || !a.lse)) return fail(CPATTN_EINVAL, "out/lse is null");
     if (a.num_rows > 0 && (!a.q_row_start || !a.ctx_len || !a.block_table || !a.q || !a.k_pool || !a.v_pool))
         return fail(CPATTN_EINVAL, "null device pointer");
     if (a.num_tokens > 0 && !a.q_row_start) return fail(CPATTN_EINVAL, "q_row_start is null");
-    const int32_t pp = a.page_size / a.num_partners;
-    *geo = PoolGeom{a.kv_stride_stripe, a.kv_stride_page, a.kv_stride_slot, a.kv_stride_head, pp, ilog2_exact(pp),
-                    a.num_pages, ilv};
     return CPATTN_OK;
 }
 
@@ -96,6 +108,44 @@ static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
     if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes(a);
     if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
     return 0;
+}
+
+// Scratch bytes a call touches on the current device (at most paged_workspace()).
+static int64_t paged_workspace_on_device(const cp_paged_args& a, const PoolGeom& geo) {
+    if (extend_bf16_eligible(a, geo)) return 0;
+    if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes_on_device(a, geo);
+    if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
+    return 0;
+}
+
+static int32_t dispatch_paged(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
+    if (a.num_tokens == 0) return CPATTN_OK;
+    if (extend_bf16_eligible(a, geo)) return launch_paged_extend_bf16(a, geo, stream);
+    if (decode_bf16_eligible(a, geo)) return launch_paged_decode_bf16(a, geo, stream);
+    if (mla_decode_eligible(a, geo)) return launch_mla_decode(a, geo, stream);
+    return launch_paged_generic(a, geo, stream);
+}
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch` (looked up once per device, with that device current).
+static int32_t device_scratch(void** out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CPATTN_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CPATTN_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (g != hipSuccess || !ptr)
+            return fail(CPATTN_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(g));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return CPATTN_OK;
 }
 
 }  // namespace cpattn
@@ -126,15 +176,35 @@ extern "C" int32_t cp_paged_attn_workspace_size(const cp_paged_args* a, int64_t*
 extern "C" int32_t cp_paged_attn_partial(const cp_paged_args* a, hipStream_t stream) {
     PoolGeom geo;
     if (int32_t st = check_paged(a, &geo)) return st;
+    if (int32_t st = check_paged_pointers(*a)) return st;
     const int64_t need = paged_workspace(*a, geo);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need))
         return fail(CPATTN_EINVAL, "workspace of %lld bytes needed (got %lld)", (long long)need,
                     (long long)a->workspace_bytes);
-    if (a->num_tokens == 0) return CPATTN_OK;
-    if (extend_bf16_eligible(*a, geo)) return launch_paged_extend_bf16(*a, geo, stream);
-    if (decode_bf16_eligible(*a, geo)) return launch_paged_decode_bf16(*a, geo, stream);
-    if (mla_decode_eligible(*a, geo)) return launch_mla_decode(*a, geo, stream);
-    return launch_paged_generic(*a, geo, stream);
+    return dispatch_paged(*a, geo, stream);
+}
+
+extern "C" int64_t cp_paged_attn_noalloc_scratch_bytes(void) { return CPATTN_NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int32_t cp_paged_attn_partial_noalloc(const cp_paged_args* a, hipStream_t stream) {
+    PoolGeom geo;
+    if (int32_t st = check_paged(a, &geo)) return st;
+    if (int32_t st = check_paged_pointers(*a)) return st;
+    const int64_t need = paged_workspace_on_device(*a, geo);
+    if (need > CPATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(CPATTN_EINVAL, "cp_paged_attn_partial_noalloc: this call needs %lld bytes of scratch, the static "
+                    "scratch holds %lld; use cp_paged_attn_partial with a workspace", (long long)need,
+                    (long long)CPATTN_NOALLOC_SCRATCH_BYTES);
+    cp_paged_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    if (need > 0) {
+        void* ptr = nullptr;
+        if (int32_t st = device_scratch(&ptr)) return st;
+        b.workspace = ptr;
+        b.workspace_bytes = CPATTN_NOALLOC_SCRATCH_BYTES;
+    }
+    return dispatch_paged(b, geo, stream);
 }
 
 extern "C" int32_t cp_own_token_attn(const cp_own_args* pa, hipStream_t stream) {

@@ -28,6 +28,7 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
 // Specialised bf16 GQA partial (head_dim = head_dim_v = 128) with MFMA score and value products and split chunks.
 bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
+int64_t decode_bf16_workspace_bytes_on_device(const cp_paged_args& a, const PoolGeom& geo);
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
 
 // Specialised bf16 GQA partial for rows that bring many query tokens (head_dim = head_dim_v = 128): 128 query rows per

@@ -1052,6 +1052,20 @@ static int32_t persistent_waves() {
     return cache[dev][0];
 }
 
+// Workspace bytes a launch on the current device actually touches: the persistent schedule writes records for the
+// waves it launches (the device's resident-wave count), not for the kMaxPersistWaves the shape-only query assumes.
+int64_t decode_bf16_workspace_bytes_on_device(const cp_paged_args& a, const PoolGeom& geo) {
+    const DecodeShape d = decode_shape(a);
+    if (!d.persistent) return decode_bf16_workspace_bytes(a);
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
+    int32_t nw;
+    if (ppmode == 2) nw = kv8 ? persistent_waves<2, true>() : persistent_waves<2, false>();
+    else if (ppmode == 1) nw = kv8 ? persistent_waves<1, true>() : persistent_waves<1, false>();
+    else nw = kv8 ? persistent_waves<0, true>() : persistent_waves<0, false>();
+    return kBlockPrefBytes + int64_t(nw) * 2 * d.rec_rows * 130 * 4;
+}
+
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
     const DecodeShape d = decode_shape(a);
     DecodeParams p{};

@@ -234,8 +234,28 @@ typedef struct cp_paged_args {
  */
 int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
 
-/* Workspace bytes cp_paged_attn_partial needs for `args` (depends on shapes and the host bounds only). */
+/* Workspace bytes cp_paged_attn_partial needs for `args` (depends on shapes and the host bounds only; the pointers in
+ * `args` are not looked at). EINVAL/EUNSUPPORTED as cp_paged_attn_partial for everything but pointers. */
 int32_t cp_paged_attn_workspace_size(const cp_paged_args* args, int64_t* bytes_out);
+
+/*
+ * cp_paged_attn_partial_noalloc: cp_paged_attn_partial for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same entry point, kernels and results,
+ * with the workspace taken from a static device array of cp_paged_attn_noalloc_scratch_bytes() bytes (64 MiB) that
+ * the library holds on every device it runs on until the process ends, instead of args->workspace (ignored).
+ *
+ * Nothing is allocated, by the library or any library it calls; the caller still passes q, the pools and the out/lse
+ * buffers. The scratch needs no initial contents. Every call on one device shares that device's scratch: calls that
+ * overlap on one device (different streams without ordering between them) race and give undefined results; calls
+ * ordered on one stream are safe.
+ * EINVAL: as cp_paged_attn_partial, and a call whose workspace would exceed the static scratch (see
+ * cp_paged_attn_workspace_size; the bf16 decode schedule needs about 4-17 MB on MI355X, MLA up to a few hundred MB
+ * for small batches whose stripes are split into many chunks). ELAUNCH: the scratch address could not be obtained.
+ */
+int32_t cp_paged_attn_partial_noalloc(const cp_paged_args* args, hipStream_t stream);
+
+/* Size in bytes of the static scratch of cp_paged_attn_partial_noalloc (per device). */
+int64_t cp_paged_attn_noalloc_scratch_bytes(void);
 
 /*
  * Arguments of cp_own_token_attn.

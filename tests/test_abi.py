@@ -109,8 +109,10 @@ def test_paged_refusals(lib, bad, code):
     a = _paged(**bad)
     assert lib.cp_paged_attn_partial(C.byref(a), None) == code
     assert _err(lib)
+    assert lib.cp_paged_attn_partial_noalloc(C.byref(a), None) == code
     n = C.c_int64(-1)
-    assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == code
+    # the workspace-size query looks at shapes only, not at pointers
+    assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == (_lib.CPATTN_OK if "q" in bad else code)
 
 
 def test_mla_over_fp8_passes_host_checks(lib):
@@ -124,6 +126,8 @@ def test_mla_over_fp8_passes_host_checks(lib):
 
 def test_paged_null_args(lib):
     assert lib.cp_paged_attn_partial(None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_paged_attn_partial_noalloc(None, None) == _lib.CPATTN_EINVAL
+    assert lib.cp_paged_attn_noalloc_scratch_bytes() == 64 << 20
 
 
 def test_paged_workspace_size_is_host_only(lib):
