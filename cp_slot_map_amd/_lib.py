@@ -63,6 +63,13 @@ class MergeArgs(C.Structure):
     ]
 
 
+class MergeOut(C.Structure):
+    _fields_ = [
+        ("out_dtype", _i32), ("reserved0", _i32), ("out", _p), ("out_stride_token", _i64), ("out_stride_head", _i64),
+        ("lse", _p), ("lse_stride_token", _i64),
+    ]
+
+
 EXPORTS = {
     "cpattn_last_error": (C.c_char_p, []),
     "cpattn_version": (C.c_char_p, []),
@@ -74,6 +81,7 @@ EXPORTS = {
     "cp_paged_attn_partial": (_i32, [C.POINTER(PagedArgs), _p]),
     "cp_paged_attn_workspace_size": (_i32, [C.POINTER(PagedArgs), C.POINTER(_i64)]),
     "cp_paged_attn_partial_noalloc": (_i32, [C.POINTER(PagedArgs), _p]),
+    "cp_paged_attn_merged": (_i32, [C.POINTER(PagedArgs), C.POINTER(MergeOut), _p]),
     "cp_paged_attn_noalloc_scratch_bytes": (_i64, []),
     "cp_own_token_attn": (_i32, [C.POINTER(OwnArgs), _p]),
     "cp_lse_merge": (_i32, [C.POINTER(MergeArgs), _p]),
@@ -105,8 +113,8 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    sizes = [lib.cpattn_struct_size(i) for i in range(3)]
-    mine = [C.sizeof(PagedArgs), C.sizeof(OwnArgs), C.sizeof(MergeArgs)]
+    sizes = [lib.cpattn_struct_size(i) for i in range(4)]
+    mine = [C.sizeof(PagedArgs), C.sizeof(OwnArgs), C.sizeof(MergeArgs), C.sizeof(MergeOut)]
     if sizes != mine:
         raise ImportError(f"libcpattn struct sizes {sizes} do not match the binding's {mine}")
     _LIB = lib

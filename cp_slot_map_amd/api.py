@@ -15,11 +15,11 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import CPATTN_BF16, CPATTN_F32, CPATTN_GQA, CPATTN_MLA, MAX_PARTIALS, PagedArgs, OwnArgs, MergeArgs
+from ._lib import CPATTN_BF16, CPATTN_F32, CPATTN_GQA, CPATTN_MLA, MAX_PARTIALS, PagedArgs, OwnArgs, MergeArgs, MergeOut
 
 __all__ = ["slot_map", "slot_map_rank", "kv_write", "paged_attn_partial", "paged_attn_workspace_size",
            "own_token_attn", "lse_merge", "stripe_length", "debug_gather_stripe", "version",
-           "paged_attn_partial_noalloc", "noalloc_scratch_bytes"]
+           "paged_attn_partial_noalloc", "noalloc_scratch_bytes", "paged_attn_merged"]
 
 
 def _lib_handle():
@@ -317,6 +317,68 @@ def paged_attn_partial(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, 
         a.workspace_bytes = ws.numel() * ws.element_size()
     _lib.check(lib.cp_paged_attn_partial(C.byref(a), _stream(stream)))
     return out, lse
+
+
+def paged_attn_merged(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,
+                      kind="gqa", max_ctx_len=None, max_row_tokens=None, out=None, lse=None, merged=None,
+                      merged_lse=None, out_dtype=torch.float32, workspace=None, stream=None, fixed_splits=False,
+                      interleave=1, k_descale=1.0, v_descale=1.0):
+    """cp_paged_attn_merged: every stripe's partial (into ``out``/``lse``) and their exact merge (into ``merged`` [T,
+    Hq, Dv] of ``out_dtype`` and ``merged_lse`` [T, Hq]) in one call; all P stripes are attended. The same bits as
+    :func:`paged_attn_partial` followed by :func:`lse_merge` with the real token count.
+
+    Returns (merged, merged_lse, out, lse)."""
+    lib = _lib_handle()
+    if kind == "mla" and v_pool is None:
+        v_pool = k_pool
+    P = int(partners)
+    _validate_paged(q, k_pool, v_pool, q_row_start, ctx_len, block_table, kind, P, P, out, lse)
+    T, Hq = q.shape[0], q.shape[1]
+    Dv = 512 if kind == "mla" else v_pool.shape[4]
+    if merged is not None:
+        _need(merged.dtype in (torch.float32, torch.bfloat16) and tuple(merged.shape) == (T, Hq, Dv) and
+              merged.stride(2) == 1, f"merged must be fp32 or bf16 [{T}, {Hq}, {Dv}] with a contiguous last dim")
+    if merged_lse is not None:
+        _need(merged_lse.dtype == torch.float32 and tuple(merged_lse.shape) == (T, Hq) and merged_lse.stride(1) == 1,
+              f"merged_lse must be fp32 [{T}, {Hq}] with a contiguous last dim")
+    _need_cuda(q, k_pool, v_pool, q_row_start, ctx_len, block_table, out, lse, merged, merged_lse)
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_len.max().item()) if ctx_len.numel() else 0
+    if max_row_tokens is None:
+        max_row_tokens = int((q_row_start[1:] - q_row_start[:-1]).max().item()) if ctx_len.numel() else 0
+    if out is None:
+        out = torch.empty((P, T, Hq, Dv), dtype=torch.float32, device=q.device)
+        lse = torch.empty((P, T, Hq), dtype=torch.float32, device=q.device)
+    if merged is None:
+        merged = torch.empty((T, Hq, Dv), dtype=out_dtype, device=q.device)
+    if merged_lse is None:
+        merged_lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    a = _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, page_size=page_size, partners=P,
+                    scale=scale, kind=kind, stripe_begin=0, stripe_count=P, max_ctx_len=max_ctx_len,
+                    max_row_tokens=max_row_tokens, out=out, lse=lse, num_tokens=T, fixed_splits=fixed_splits,
+                    interleave=interleave, k_descale=k_descale, v_descale=v_descale)
+    n = C.c_int64(0)
+    _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
+    if n.value > 0:
+        ws = workspace if workspace is not None else _WS.get(q.device, n.value)
+        if ws.numel() * ws.element_size() < n.value:
+            raise ValueError(f"workspace too small: {n.value} bytes needed")
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    m = _merge_out(merged, merged_lse)
+    _lib.check(lib.cp_paged_attn_merged(C.byref(a), C.byref(m), _stream(stream)))
+    return merged, merged_lse, out, lse
+
+
+def _merge_out(merged, merged_lse):
+    m = MergeOut()
+    m.out_dtype = _dtype_code(merged.dtype)
+    m.out = merged.data_ptr()
+    m.out_stride_token, m.out_stride_head = merged.stride(0), merged.stride(1)
+    if merged_lse is not None:
+        m.lse = merged_lse.data_ptr()
+        m.lse_stride_token = merged_lse.stride(0)
+    return m
 
 
 def paged_attn_partial_noalloc(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale,

@@ -161,6 +161,7 @@ extern "C" int64_t cpattn_struct_size(int32_t which) {
         case 0: return int64_t(sizeof(cp_paged_args));
         case 1: return int64_t(sizeof(cp_own_args));
         case 2: return int64_t(sizeof(cp_merge_args));
+        case 3: return int64_t(sizeof(cp_merge_out));
         default: return -1;
     }
 }
@@ -182,6 +183,52 @@ extern "C" int32_t cp_paged_attn_partial(const cp_paged_args* a, hipStream_t str
         return fail(CPATTN_EINVAL, "workspace of %lld bytes needed (got %lld)", (long long)need,
                     (long long)a->workspace_bytes);
     return dispatch_paged(*a, geo, stream);
+}
+
+extern "C" int32_t cp_paged_attn_merged(const cp_paged_args* a, const cp_merge_out* m, hipStream_t stream) {
+    PoolGeom geo;
+    if (int32_t st = check_paged(a, &geo)) return st;
+    if (int32_t st = check_paged_pointers(*a)) return st;
+    if (!m) return fail(CPATTN_EINVAL, "cp_paged_attn_merged: merged is null");
+    if (a->stripe_begin != 0 || a->stripe_count != a->num_partners)
+        return fail(CPATTN_EINVAL, "cp_paged_attn_merged merges all resident stripes: stripes [%d, %d) of %d",
+                    a->stripe_begin, a->stripe_begin + a->stripe_count, a->num_partners);
+    if (m->out_dtype != CPATTN_F32 && m->out_dtype != CPATTN_BF16)
+        return fail(CPATTN_EINVAL, "merged out_dtype = %d unknown", m->out_dtype);
+    if (a->num_tokens > 0 && !m->out) return fail(CPATTN_EINVAL, "merged out is null");
+    if ((reinterpret_cast<uintptr_t>(m->out) & 15) || (m->out_stride_token & 7) || (m->out_stride_head & 7) ||
+        m->out_stride_token < 0 || m->out_stride_head < 0 || m->lse_stride_token < 0)
+        return fail(CPATTN_EINVAL, "merged out must be 16-byte aligned with non-negative strides that are multiples of 8");
+    if (m->out == a->out) return fail(CPATTN_EINVAL, "merged out aliases the partials");
+    const int64_t need = paged_workspace(*a, geo);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+        return fail(CPATTN_EINVAL, "workspace of %lld bytes needed (got %lld)", (long long)need,
+                    (long long)a->workspace_bytes);
+    if (a->num_tokens == 0) return CPATTN_OK;
+    if (decode_bf16_eligible(*a, geo) && !extend_bf16_eligible(*a, geo) && decode_bf16_fuses_merge(*a))
+        return launch_paged_decode_bf16(*a, geo, stream, m);
+    if (int32_t st = dispatch_paged(*a, geo, stream)) return st;
+    cp_merge_args ma{};
+    ma.num_partials = a->stripe_count;
+    ma.num_tokens = a->num_tokens;
+    ma.num_heads = a->num_q_heads;
+    ma.head_dim_v = a->head_dim_v;
+    ma.out_dtype = m->out_dtype;
+    ma.token_count = a->q_row_start + a->num_rows;
+    for (int32_t i = 0; i < a->stripe_count; ++i) {
+        ma.part_out[i] = a->out + i * a->out_stride_stripe;
+        ma.part_lse[i] = a->lse + i * a->lse_stride_stripe;
+        ma.part_out_stride_token[i] = a->out_stride_token;
+        ma.part_out_stride_head[i] = a->out_stride_head;
+        ma.part_lse_stride_token[i] = a->lse_stride_token;
+        ma.part_lse_stride_head[i] = 1;
+    }
+    ma.out = m->out;
+    ma.out_stride_token = m->out_stride_token;
+    ma.out_stride_head = m->out_stride_head;
+    ma.lse_out = m->lse;
+    ma.lse_out_stride_token = m->lse_stride_token;
+    return cp_lse_merge(&ma, stream);
 }
 
 extern "C" int64_t cp_paged_attn_noalloc_scratch_bytes(void) { return CPATTN_NOALLOC_SCRATCH_BYTES; }

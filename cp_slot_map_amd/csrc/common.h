@@ -123,6 +123,42 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+// The exact LSE merge of cp_lse_merge over NMAX partials of KV float4s each (entries past the real partials carry
+// lse = -inf): M = max_i l_i, w_i = exp(l_i - M), out = sum_i (w_i / sum w) o_i, lse = M + log(sum w); a partial with
+// l_i = -inf is selected out (its row is never multiplied), and all of them -inf give (0, -inf). Entries with l = -inf
+// change neither sum, so the result is the same for any NMAX. Shared by the merge kernel and the fused decode finish,
+// with explicit fused multiply-adds, so that both give the same bits.
+template <int NMAX, int KV>
+__device__ __forceinline__ float lse_merge_rows(const float (&l)[NMAX], const f32x4_t (&o)[NMAX][KV],
+                                                f32x4_t (&acc)[KV]) {
+    float M = neg_inf();
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) M = fmaxf(M, l[i]);
+#pragma unroll
+    for (int v = 0; v < KV; ++v) acc[v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (M == neg_inf()) return neg_inf();
+    float w[NMAX];
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        w[i] = l[i] == neg_inf() ? 0.f : expf(l[i] - M);
+        tot += w[i];
+    }
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        const float c = w[i] * inv;
+#pragma unroll
+        for (int v = 0; v < KV; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = __builtin_fmaf(c, o[i][v][e], acc[v][e]);
+                acc[v][e] = w[i] != 0.f ? f : acc[v][e];
+            }
+    }
+    return M + logf(tot);
+}
+
 // Write (0, -inf) for padding query tokens [t_begin, t_end) of S partials (Hq heads, Dv dims each).
 __device__ __forceinline__ void fill_padding(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse,
                                              int64_t l_ss, int64_t l_st, int32_t S, int32_t Hq, int32_t Dv,

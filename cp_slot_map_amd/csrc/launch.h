@@ -29,7 +29,10 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
 bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a);
 int64_t decode_bf16_workspace_bytes_on_device(const cp_paged_args& a, const PoolGeom& geo);
-int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+// With m non-null (and decode_bf16_fuses_merge), the stripes' partials are also merged into m in the same launches.
+bool decode_bf16_fuses_merge(const cp_paged_args& a);
+int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream,
+                                 const cp_merge_out* m = nullptr);
 
 // Specialised bf16 GQA partial for rows that bring many query tokens (head_dim = head_dim_v = 128): 128 query rows per
 // workgroup, K/V tiles staged in LDS, MFMA score and value products. The same kernel serves the own-token part.

@@ -58,32 +58,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
             for (int v = 0; v < kV; ++v) o[i][v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         }
     }
-    float M = neg_inf();
-#pragma unroll
-    for (int i = 0; i < NMAX; ++i) M = fmaxf(M, l[i]);
     f32x4_t acc[kV];
-#pragma unroll
-    for (int v = 0; v < kV; ++v) acc[v] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float lse = neg_inf();
-    if (M != neg_inf()) {
-        float w[NMAX];
-        float tot = 0.f;
-#pragma unroll
-        for (int i = 0; i < NMAX; ++i) {
-            w[i] = l[i] == neg_inf() ? 0.f : expf(l[i] - M);
-            tot += w[i];
-        }
-        const float inv = 1.0f / tot;
-#pragma unroll
-        for (int i = 0; i < NMAX; ++i) {
-#pragma unroll
-            for (int v = 0; v < kV; ++v) {
-                const f32x4_t c = (w[i] * inv) * o[i][v];
-                if (w[i] != 0.f) acc[v] += c;
-            }
-        }
-        lse = M + logf(tot);
-    }
+    const float lse = lse_merge_rows<NMAX, kV>(l, o, acc);
     const int64_t off = int64_t(t) * p.out_st + int64_t(h) * p.out_sh + 4 * d4;
 #pragma unroll
     for (int v = 0; v < kV; ++v) {

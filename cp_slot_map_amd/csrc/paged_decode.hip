@@ -51,7 +51,7 @@ struct DecodeParams {
     float* lse;
     int64_t l_ss, l_st;
     float* ws_rec;
-    int32_t* ws_blockpref;        // persistent schedule: 64 block offsets + the total step count
+    int32_t* ws_rowpref;          // persistent schedule: step offset of every row (B + 1 entries, the last the total)
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G;
     int32_t max_pages, page_size, max_row_tokens;
     int32_t ctx_cap;              // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
@@ -61,6 +61,10 @@ struct DecodeParams {
     int32_t num_tiles, nwaves;    // persistent schedule
     float scale_log2;             // softmax scale (times the key descale for fp8 pools) in log2 units
     float v_scale;                // value descale of fp8 pools, else 1 (applied where output rows are written)
+    void* m_out;                  // fused finish: merged output [T, Hq, 128] (fp32 or bf16), its lse (nullable)
+    int64_t m_st, m_sh;
+    float* m_lse;
+    int64_t m_lst;
 };
 
 // s_waitcnt with vmcnt = 0 and the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14],
@@ -569,6 +573,7 @@ __device__ __forceinline__ int32_t tile_steps(const DecodeParams& p, int32_t T) 
 
 struct Tile {
     int32_t b, s, qt, tok0, nrows, Lr, n_steps;
+    int32_t q0, q1, cl;      // the row's q_row_start[b], q_row_start[b + 1] and ctx_len[b] as read
 };
 
 // Wave-uniform T: scalar loads through the constant address space.
@@ -580,13 +585,88 @@ __device__ __forceinline__ Tile load_tile(const DecodeParams& p, int32_t T) {
     const int32_t bs = T / p.n_qtiles;
     tl.s = bs % p.S;
     tl.b = bs / p.S;
-    tl.tok0 = min(max(qrs[tl.b], 0), p.T);
-    const int32_t tok1 = min(max(qrs[tl.b + 1], tl.tok0), p.T);
+    tl.q0 = qrs[tl.b];
+    tl.q1 = qrs[tl.b + 1];
+    tl.cl = cl[tl.b];
+    tl.tok0 = min(max(tl.q0, 0), p.T);
+    const int32_t tok1 = min(max(tl.q1, tl.tok0), p.T);
     tl.nrows = min(tok1 - tl.tok0, p.max_row_tokens) * p.G;
-    const int32_t L = min(max(cl[tl.b], 0), p.ctx_cap);
+    const int32_t L = min(max(tl.cl, 0), p.ctx_cap);
     tl.Lr = stripe_length(L, p.stripe_begin + tl.s, p.P, p.geo.interleave);
     tl.n_steps = tl.qt * 16 < tl.nrows ? (tl.Lr + 15) >> 4 : 0;
     return tl;
+}
+
+// Steps of all tiles of a row (every stripe, every query tile holding rows) from its q_row_start pair and ctx_len;
+// nq = its query tiles holding rows. Tiles of a row are ordered stripe-major, query tile minor.
+__device__ __forceinline__ int32_t row_steps_of(const DecodeParams& p, int32_t qrs0, int32_t qrs1, int32_t ctx,
+                                                int32_t& nq) {
+    const int32_t tok0 = min(max(qrs0, 0), p.T);
+    const int32_t tok1 = min(max(qrs1, tok0), p.T);
+    const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
+    nq = (nrows + 15) >> 4;
+    const int32_t L = min(max(ctx, 0), p.ctx_cap);
+    int32_t steps = 0;
+    for (int32_t s = 0; s < p.S; ++s) steps += (stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave) + 15) >> 4;
+    return nq * steps;
+}
+
+// The tile of row b holding the row's step `off` (0 <= off < the row's steps); off becomes the step inside the tile.
+__device__ __forceinline__ Tile tile_in_row(const DecodeParams& p, int32_t b, int32_t qrs0, int32_t qrs1, int32_t ctx,
+                                            int32_t& off) {
+    Tile tl;
+    tl.b = b;
+    tl.q0 = qrs0;
+    tl.q1 = qrs1;
+    tl.cl = ctx;
+    tl.tok0 = min(max(qrs0, 0), p.T);
+    const int32_t tok1 = min(max(qrs1, tl.tok0), p.T);
+    tl.nrows = min(tok1 - tl.tok0, p.max_row_tokens) * p.G;
+    const int32_t nq = (tl.nrows + 15) >> 4;
+    const int32_t L = min(max(ctx, 0), p.ctx_cap);
+    tl.s = 0;
+    tl.Lr = 0;
+    tl.n_steps = 0;
+    tl.qt = 0;
+    for (int32_t s = 0; s < p.S; ++s) {
+        const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
+        const int32_t n = (Lr + 15) >> 4;
+        if (off < nq * n) {
+            tl.s = s;
+            tl.Lr = Lr;
+            tl.n_steps = n;
+            tl.qt = off / n;
+            off -= tl.qt * n;
+            break;
+        }
+        off -= nq * n;
+    }
+    return tl;
+}
+
+// Step offset of every row (ws_rowpref[b], b <= B, the last entry the total), written by one wave of the persistent
+// kernel for the kernels that run after it: the lanes hold consecutive row blocks with their exclusive offsets.
+__device__ __forceinline__ void publish_row_prefix(const DecodeParams& p, int32_t r_lo, int32_t r_hi, int32_t excl,
+                                                   int32_t total, int lane) {
+    int32_t acc = excl;
+    for (int32_t b = r_lo; b < r_hi; ++b) {
+        p.ws_rowpref[b] = acc;
+        int32_t nq;
+        acc += row_steps_of(p, p.q_row_start[b], p.q_row_start[b + 1], p.ctx_len[b], nq);
+    }
+    if (lane == 0) p.ws_rowpref[p.B] = total;
+}
+
+// Step offset of tile (row b, stripe s, query tile qt) inside the step space of one kv head, from the published row
+// offsets.
+__device__ __forceinline__ int32_t tile_offset(const DecodeParams& p, int32_t b, int32_t s, int32_t qt, int32_t qrs0,
+                                               int32_t qrs1, int32_t ctx) {
+    int32_t nq;
+    (void)row_steps_of(p, qrs0, qrs1, ctx, nq);
+    const int32_t L = min(max(ctx, 0), p.ctx_cap);
+    int32_t off = p.ws_rowpref[b];
+    for (int32_t s2 = 0; s2 < s; ++s2) off += nq * ((stripe_length(L, p.stripe_begin + s2, p.P, p.geo.interleave) + 15) >> 4);
+    return off + qt * ((stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave) + 15) >> 4);
 }
 
 struct ItemAddr {
@@ -745,30 +825,40 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     const int32_t n16 = lane & 15, c4 = lane >> 4;
     const int32_t NT = p.num_tiles;
 
-    // Step counts of every tile: lane l sums a block of K consecutive tiles; a wave scan gives block offsets. Four
-    // tiles' loads are issued before any is used (indices clamped into the lane's block), so a block of K tiles costs
-    // ceil(K / 4) memory round trips rather than K: every wave runs this before its first K/V load.
-    const int32_t K = (NT + 63) >> 6;
-    const int32_t t_lo = min(lane * K, NT), t_hi = min(t_lo + K, NT);
+    // Step counts of every row (all its stripes and query tiles; the tiles of a row are contiguous in the step space):
+    // lane l sums rows [R l, R l + R), a wave scan gives the lanes' offsets. Four rows' loads are issued before any is
+    // used, so R rows cost ceil(R / 4) memory round trips; the first four rows' values stay in registers, so that the
+    // search for this wave's first tile below needs no further load when R <= 4 (up to 256 rows).
+    const int32_t R = (p.B + 63) >> 6;
+    const int32_t r_lo = min(lane * R, p.B), r_hi = min(r_lo + R, p.B);
+    int32_t kq0[4] = {0, 0, 0, 0}, kq1[4] = {0, 0, 0, 0}, kcl[4] = {0, 0, 0, 0};
     int32_t my_sum = 0;
-    for (int32_t t = t_lo; t < t_hi; t += 4) {
+    for (int32_t b = r_lo; b < r_hi; b += 4) {
         int32_t qa[4], qb[4], cl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int32_t b = (min(t + u, t_hi - 1) / p.n_qtiles) / p.S;
-            qa[u] = p.q_row_start[b];
-            qb[u] = p.q_row_start[b + 1];
-            cl[u] = p.ctx_len[b];
+            const int32_t bb = min(b + u, r_hi - 1);
+            qa[u] = p.q_row_start[bb];
+            qb[u] = p.q_row_start[bb + 1];
+            cl[u] = p.ctx_len[bb];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) my_sum += t + u < t_hi ? tile_steps_of(p, t + u, qa[u], qb[u], cl[u]) : 0;
+        for (int u = 0; u < 4; ++u) {
+            int32_t nq;
+            my_sum += b + u < r_hi ? row_steps_of(p, qa[u], qb[u], cl[u], nq) : 0;
+        }
+        if (b == r_lo) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kq0[u] = qa[u];
+                kq1[u] = qb[u];
+                kcl[u] = cl[u];
+            }
+        }
     }
     int32_t N = 0;
     const int32_t my_excl = wave_exclusive_scan(my_sum, lane, N);
-    if (w == 0) {                                    // block offsets for the fix-up kernel
-        p.ws_blockpref[lane] = my_excl;
-        if (lane == 0) p.ws_blockpref[64] = N;
-    }
+    if (w == 0) publish_row_prefix(p, r_lo, r_hi, my_excl, N, lane);
     const int64_t total = int64_t(p.Hkv) * N;
     const int64_t Q = (total + nw - 1) / nw;
     const int64_t start = int64_t(w) * Q;
@@ -777,24 +867,57 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     int32_t g = int32_t(start / N);
     const int32_t pos = int32_t(start - int64_t(g) * N);
 
-    // The tile holding `pos`: first the lane block, then the tile inside it (one tile per lane, one scan).
-    const uint64_t owner = __ballot(pos >= my_excl && pos < my_excl + my_sum);
+    // The row holding `pos`: first the lane, then the row among the lane's (from registers when R <= 4, else one row
+    // per lane and one scan), then the tile inside the row by arithmetic.
+    const uint64_t owner = __ballot(my_sum > 0 && pos >= my_excl && pos < my_excl + my_sum);
     const int32_t src = uniform(int32_t(__builtin_ctzll(owner)));
-    const int32_t b_lo = uniform(__shfl(t_lo, src)), b_hi = uniform(__shfl(t_hi, src)), b_ex = uniform(__shfl(my_excl, src));
-    const int32_t tt = b_lo + lane;
-    const int32_t tn = tt < b_hi ? tile_steps(p, tt) : 0;
-    int32_t dummy;
-    const int32_t tex = b_ex + wave_exclusive_scan(tn, lane, dummy);
-    const uint64_t hit = __ballot(tt < b_hi && tn > 0 && pos >= tex && pos < tex + tn);
-    const int32_t hl = uniform(int32_t(__builtin_ctzll(hit)));
-    int32_t T = b_lo + hl;
-    int32_t seg_begin = pos - uniform(__shfl(tex, hl));
+    const int32_t src_lo = uniform(__shfl(r_lo, src));
+    int32_t off = pos - uniform(__shfl(my_excl, src));
+    int32_t rb, rq0, rq1, rcl;
+    if (R <= 4) {
+        rb = src_lo;
+        rq0 = uniform(__shfl(kq0[0], src));
+        rq1 = uniform(__shfl(kq1[0], src));
+        rcl = uniform(__shfl(kcl[0], src));
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            int32_t nq;
+            const int32_t n = row_steps_of(p, rq0, rq1, rcl, nq);
+            if (off < n) break;
+            off -= n;
+            ++rb;
+            rq0 = uniform(__shfl(kq0[u + 1], src));
+            rq1 = uniform(__shfl(kq1[u + 1], src));
+            rcl = uniform(__shfl(kcl[u + 1], src));
+        }
+    } else {
+        const int32_t src_hi = uniform(__shfl(r_hi, src));
+        const int32_t bl = src_lo + lane;
+        int32_t q0v = 0, q1v = 0, clv = 0, n = 0, nq;
+        if (bl < src_hi) {
+            q0v = p.q_row_start[bl];
+            q1v = p.q_row_start[bl + 1];
+            clv = p.ctx_len[bl];
+            n = row_steps_of(p, q0v, q1v, clv, nq);
+        }
+        int32_t dummy;
+        const int32_t ex = wave_exclusive_scan(n, lane, dummy);
+        const uint64_t hit = __ballot(n > 0 && off >= ex && off < ex + n);
+        const int32_t hl = uniform(int32_t(__builtin_ctzll(hit)));
+        off -= uniform(__shfl(ex, hl));
+        rb = src_lo + hl;
+        rq0 = uniform(__shfl(q0v, hl));
+        rq1 = uniform(__shfl(q1v, hl));
+        rcl = uniform(__shfl(clv, hl));
+    }
+    Tile tl = tile_in_row(p, rb, rq0, rq1, rcl, off);
+    int32_t T = (tl.b * p.S + tl.s) * p.n_qtiles + tl.qt;
+    int32_t seg_begin = off;
 
     const int32_t lane_slot = PPMODE == 2 ? c4 : (PPMODE == 1 ? (c4 & 1) : 0);
     const uint32_t lane_off = uint32_t(lane_slot * p.geo.s_slot + 8 * n16);
     float* const rec_base = p.ws_rec + int64_t(w) * 2 * p.rec_rows * 130;
 
-    Tile tl = load_tile(p, T);
     ItemAddr ia = item_addr(p, tl, g);
     int32_t seg_end = int32_t(min<int64_t>(tl.n_steps, seg_begin + remaining));
     bool first_seg = true;
@@ -883,16 +1006,49 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     }
 }
 
-// Prefix (in steps) of tile T from the published block offsets: one block walk, one tile per lane.
-__device__ __forceinline__ int32_t tile_prefix(const DecodeParams& p, int32_t T, int lane) {
-    const int32_t K = (p.num_tiles + 63) >> 6;
-    const int32_t blk = T / K;
-    const int32_t t = blk * K + lane;
-    const int32_t n = (t < T) ? tile_steps(p, t) : 0;
-    int32_t sum = n;
+// Merge the records of an item split over waves wA..wB (A: its first step in the step space, Q: steps per wave) for
+// record row rrow and head dims [8 d8, +8): one online pass over the covering waves' records, four loaded together
+// (an item split over two waves, the usual case, costs one memory round trip); M is the running maximum (log2 units),
+// earlier sums are rescaled when it rises. Records hold finite maxima (every segment has at least one key); unused
+// batch entries carry -inf and weigh 0.
+__device__ __forceinline__ void merge_records(const DecodeParams& p, int64_t A, int64_t Q, int64_t wA, int64_t wB,
+                                              int32_t rrow, int32_t d8, float& M, float& Lsum, f32x4_t& a0,
+                                              f32x4_t& a1) {
+    const int32_t RR = p.rec_rows;
+    const int64_t rec_floats = int64_t(RR) * 130;
+    M = neg_inf();
+    Lsum = 0.f;
+    a0 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    a1 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int64_t w0 = wA; w0 <= wB; w0 += 4) {
+        float mc[4], lc[4];
+        f32x4_t o0[4], o1[4];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-    return p.ws_blockpref[blk] + sum;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t wv = min(w0 + u, wB);
+            const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
+            mc[u] = rc[RR * 128 + rrow];
+            lc[u] = rc[RR * 128 + RR + rrow];
+            o0[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
+            o1[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
+            if (w0 + u > wB) mc[u] = neg_inf();
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mc[u]);
+        const float f = M == neg_inf() ? 0.f : exp2f(M - Mn);
+        Lsum *= f;
+        a0 *= f;
+        a1 *= f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wgt = mc[u] == neg_inf() ? 0.f : exp2f(mc[u] - Mn);
+            Lsum += wgt * lc[u];
+            a0 += wgt * o0[u];
+            a1 += wgt * o1[u];
+        }
+        M = Mn;
+    }
 }
 
 // Items split over several waves are merged from their records; tiles with query rows but no context get (0, -inf);
@@ -927,53 +1083,19 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
         }
         return;
     }
-    const int32_t N = p.ws_blockpref[64];
+    const int32_t N = p.ws_rowpref[p.B];
     const int64_t total = int64_t(p.Hkv) * N;
     const int64_t Q = (total + p.nwaves - 1) / p.nwaves;
-    const int64_t A = int64_t(g) * N + tile_prefix(p, T, lane);
+    const int64_t A = int64_t(g) * N + tile_offset(p, tl.b, tl.s, tl.qt, tl.q0, tl.q1, tl.cl);
     const int64_t Bend = A + tl.n_steps;
     const int64_t wA = A / Q, wB = (Bend - 1) / Q;
     if (wA == wB) return;                            // one wave covered it and wrote it
-    const int32_t RR = p.rec_rows;
-    const int64_t rec_floats = int64_t(RR) * 130;
     for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
         const int32_t row = 4 * rg + rsub;
         const bool active = row < tile_rows;
-        const int32_t rrow = min(row, RR - 1);
-        // One online pass over the covering waves' records, four loaded together (an item split over two waves, the
-        // usual case, costs one memory round trip): M is the running maximum, earlier sums are rescaled when it rises.
-        // Records hold finite maxima (every segment has at least one key); unused batch entries carry -inf and weigh 0.
-        float M = neg_inf(), Lsum = 0.f;
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t w0 = wA; w0 <= wB; w0 += 4) {
-            float mc[4], lc[4];
-            f32x4_t o0[4], o1[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t wv = min(w0 + u, wB);
-                const float* rc = p.ws_rec + (wv * 2 + (wv * Q >= A ? 0 : 1)) * rec_floats;
-                mc[u] = rc[RR * 128 + rrow];
-                lc[u] = rc[RR * 128 + RR + rrow];
-                o0[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8);
-                o1[u] = *reinterpret_cast<const f32x4_t*>(rc + rrow * 128 + 8 * d8 + 4);
-                if (w0 + u > wB) mc[u] = neg_inf();
-            }
-            float Mn = M;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mc[u]);
-            const float f = M == neg_inf() ? 0.f : exp2f(M - Mn);
-            Lsum *= f;
-            a0 *= f;
-            a1 *= f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float wgt = mc[u] == neg_inf() ? 0.f : exp2f(mc[u] - Mn);
-                Lsum += wgt * lc[u];
-                a0 += wgt * o0[u];
-                a1 += wgt * o1[u];
-            }
-            M = Mn;
-        }
+        float M, Lsum;
+        f32x4_t a0, a1;
+        merge_records(p, A, Q, wA, wB, min(row, p.rec_rows - 1), d8, M, Lsum, a0, a1);
         if (active) {
             const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
             const float vals[8] = {a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv,
@@ -984,12 +1106,125 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
     }
 }
 
+// Fused finish of the persistent schedule when the call also merges the stripes (cp_paged_attn_merged): one wave per
+// (row, query tile, kv head) assembles every stripe's partial of its rows - read back from the partial buffer where
+// one wave covered the item, merged from the records where several did, (0, -inf) where the stripe holds no context -
+// and combines them with the exact LSE merge of cp_lse_merge (the same helper), writing the merged output and lse. It
+// also writes the split items' and empty stripes' partials, so the partial buffer ends as after cp_paged_attn_partial.
+// Extra blocks write padding tokens: (0, -inf) in every partial and in the merged output.
+template <bool BF16OUT, int SMAX>
+__global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x;
+    const int32_t idx = blockIdx.x;
+    const int32_t n_items = p.B * p.n_qtiles * p.Hkv;
+    const int32_t d8 = lane & 15, rsub = lane >> 4;
+    auto merged_row = [&](int32_t t, int32_t h, const f32x4_t (&acc)[2]) __attribute__((always_inline)) {
+        const int64_t off = int64_t(t) * p.m_st + int64_t(h) * p.m_sh + 8 * d8;
+        if (BF16OUT) {
+            const u32x4_t b = {pack2_bf16(acc[0][0], acc[0][1]), pack2_bf16(acc[0][2], acc[0][3]),
+                               pack2_bf16(acc[1][0], acc[1][1]), pack2_bf16(acc[1][2], acc[1][3])};
+            *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.m_out) + off) = b;
+        } else {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.m_out) + off) = acc[0];
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.m_out) + off + 4) = acc[1];
+        }
+    };
+    if (idx >= n_items) {
+        const int32_t k = idx - n_items;
+        const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
+        const int32_t t0 = max(k * p.pad_tokens_per_block, first);
+        const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
+        if (t0 >= t1) return;
+        fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        const f32x4_t zero[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int32_t t = t0; t < t1; ++t)
+            for (int32_t h = rsub; h < p.Hq; h += 4) merged_row(t, h, zero);
+        if (p.m_lse)
+            for (int32_t t = t0; t < t1; ++t)
+                for (int32_t h = lane; h < p.Hq; h += 64) p.m_lse[int64_t(t) * p.m_lst + h] = neg_inf();
+        return;
+    }
+    const int32_t g = idx % p.Hkv;
+    const int32_t qt = (idx / p.Hkv) % p.n_qtiles;
+    const int32_t b = (idx / p.Hkv) / p.n_qtiles;
+    const const_i32_ptr qrs = (const_i32_ptr)p.q_row_start;
+    const const_i32_ptr clp = (const_i32_ptr)p.ctx_len;
+    const int32_t q0 = qrs[b], q1 = qrs[b + 1], cl = clp[b];
+    const int32_t rowpref = p.ws_rowpref[b], N = p.ws_rowpref[p.B];
+    const int32_t tok0 = min(max(q0, 0), p.T);
+    const int32_t tok1 = min(max(q1, tok0), p.T);
+    const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
+    const int32_t row0 = qt * 16;
+    if (row0 >= nrows) return;
+    const int32_t tile_rows = min(16, nrows - row0);
+    const int32_t nq = (nrows + 15) >> 4;
+    const int32_t L = min(max(cl, 0), p.ctx_cap);
+    const int64_t total = int64_t(p.Hkv) * N;
+    const int64_t Q = (total + p.nwaves - 1) / p.nwaves;
+    for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
+        const int32_t row = 4 * rg + rsub;
+        const bool active = row < tile_rows;
+        const int32_t rho = row0 + min(row, tile_rows - 1);
+        const int32_t t = tok0 + rho / p.G;
+        const int32_t h = g * p.G + rho % p.G;
+        float ls[SMAX];
+        f32x4_t os[SMAX][2];
+        int64_t off = int64_t(g) * N + rowpref;
+#pragma unroll
+        for (int32_t s = 0; s < SMAX; ++s) {
+            ls[s] = neg_inf();
+            os[s][0] = os[s][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            if (s >= p.S) continue;
+            const int32_t n = (stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave) + 15) >> 4;
+            const int64_t A = off + int64_t(qt) * n;
+            off += int64_t(nq) * n;
+            float* o = p.out + s * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * d8;
+            float* lp = p.lse + s * p.l_ss + int64_t(t) * p.l_st + h;
+            if (n == 0) {                            // no context in this stripe: (0, -inf)
+                if (active) {
+                    *reinterpret_cast<f32x4_t*>(o) = os[s][0];
+                    *reinterpret_cast<f32x4_t*>(o + 4) = os[s][1];
+                    if (d8 == 0) *lp = neg_inf();
+                }
+                continue;
+            }
+            const int64_t wA = A / Q, wB = (A + n - 1) / Q;
+            if (wA == wB) {                          // one wave covered it and wrote the partial
+                os[s][0] = *reinterpret_cast<const f32x4_t*>(o);
+                os[s][1] = *reinterpret_cast<const f32x4_t*>(o + 4);
+                ls[s] = *lp;
+                continue;
+            }
+            float M, Lsum;
+            f32x4_t a0, a1;
+            merge_records(p, A, Q, wA, wB, min(row, p.rec_rows - 1), d8, M, Lsum, a0, a1);
+            // The values write_row and write_lse store for this partial.
+            const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+            const float c = p.v_scale;
+            os[s][0] = (f32x4_t){(a0[0] * inv) * c, (a0[1] * inv) * c, (a0[2] * inv) * c, (a0[3] * inv) * c};
+            os[s][1] = (f32x4_t){(a1[0] * inv) * c, (a1[1] * inv) * c, (a1[2] * inv) * c, (a1[3] * inv) * c};
+            ls[s] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf();
+            if (active) {
+                *reinterpret_cast<f32x4_t*>(o) = os[s][0];
+                *reinterpret_cast<f32x4_t*>(o + 4) = os[s][1];
+                if (d8 == 0) *lp = ls[s];
+            }
+        }
+        if (!active) continue;
+        f32x4_t acc[2];
+        const float lse = lse_merge_rows<SMAX, 2>(ls, os, acc);
+        merged_row(t, h, acc);
+        if (d8 == 0 && p.m_lse) p.m_lse[int64_t(t) * p.m_lst + h] = lse;
+    }
+}
+
 // Steps (16 keys each) of one chunk of the fixed-split schedule: splits fall every 1024 keys of a stripe.
 constexpr int32_t kChunkSteps = 64;
 
 constexpr int64_t kMaxPersistWaves = 8192;
 constexpr int64_t kMaxPersistTiles = 4096;
-constexpr int64_t kBlockPrefBytes = 512;   // 65 int32 block offsets, padded
+// Workspace of the persistent schedule: the row offsets (B + 1 int32, padded to 256 bytes), then two records per wave.
+inline int64_t rowpref_bytes(const cp_paged_args& a) { return (int64_t(a.num_rows + 1) * 4 + 255) / 256 * 256; }
 
 struct DecodeShape {
     int64_t n_qtiles, n_chunks, total_items, rec_rows, triples, num_tiles;
@@ -1029,7 +1264,7 @@ bool decode_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
 
 int64_t decode_bf16_workspace_bytes(const cp_paged_args& a) {
     const DecodeShape d = decode_shape(a);
-    if (d.persistent) return kBlockPrefBytes + kMaxPersistWaves * 2 * d.rec_rows * 130 * 4;
+    if (d.persistent) return rowpref_bytes(a) + kMaxPersistWaves * 2 * d.rec_rows * 130 * 4;
     if (d.n_chunks <= 1) return 0;
     return d.total_items * d.rec_rows * 130 * 4;
 }
@@ -1063,10 +1298,13 @@ int64_t decode_bf16_workspace_bytes_on_device(const cp_paged_args& a, const Pool
     if (ppmode == 2) nw = kv8 ? persistent_waves<2, true>() : persistent_waves<2, false>();
     else if (ppmode == 1) nw = kv8 ? persistent_waves<1, true>() : persistent_waves<1, false>();
     else nw = kv8 ? persistent_waves<0, true>() : persistent_waves<0, false>();
-    return kBlockPrefBytes + int64_t(nw) * 2 * d.rec_rows * 130 * 4;
+    return rowpref_bytes(a) + int64_t(nw) * 2 * d.rec_rows * 130 * 4;
 }
 
-int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
+bool decode_bf16_fuses_merge(const cp_paged_args& a) { return decode_shape(a).persistent && a.num_partners <= 16; }
+
+int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream,
+                                 const cp_merge_out* m) {
     const DecodeShape d = decode_shape(a);
     DecodeParams p{};
     p.q = static_cast<const uint16_t*>(a.q);
@@ -1112,8 +1350,8 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
 
     if (d.persistent) {
-        p.ws_blockpref = static_cast<int32_t*>(a.workspace);
-        p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + kBlockPrefBytes);
+        p.ws_rowpref = static_cast<int32_t*>(a.workspace);
+        p.ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + rowpref_bytes(a));
         if (d.num_tiles > 0) {
             auto launch = [&](auto pp, auto k8) {
                 constexpr int PP = decltype(pp)::value;
@@ -1131,6 +1369,28 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
             else
                 kv8 ? launch(std::integral_constant<int, 0>{}, T8{}) : launch(std::integral_constant<int, 0>{}, F8{});
             if (int32_t st = check_launch("cp_paged_attn_partial (bf16 decode, persistent)")) return st;
+        }
+        if (m) {                                     // fix-up and stripe merge in one launch
+            p.m_out = m->out;
+            p.m_st = m->out_stride_token;
+            p.m_sh = m->out_stride_head;
+            p.m_lse = m->lse;
+            p.m_lst = m->lse_stride_token;
+            const int64_t blocks = int64_t(a.num_rows) * d.n_qtiles * a.num_kv_heads + p.pad_blocks;
+            if (blocks == 0) return CPATTN_OK;
+            const dim3 grid{uint32_t(blocks), 1, 1};
+            const bool bf = m->out_dtype == CPATTN_BF16;
+            if (a.stripe_count <= 4) {
+                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 4>), grid, dim3(64), 0, stream, p);
+                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 4>), grid, dim3(64), 0, stream, p);
+            } else if (a.stripe_count <= 8) {
+                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 8>), grid, dim3(64), 0, stream, p);
+                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 8>), grid, dim3(64), 0, stream, p);
+            } else {
+                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 16>), grid, dim3(64), 0, stream, p);
+                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 16>), grid, dim3(64), 0, stream, p);
+            }
+            return check_launch("cp_paged_attn_merged (finish)");
         }
         const int64_t fix_blocks = d.num_tiles * a.num_kv_heads + p.pad_blocks;
         if (fix_blocks > 0) {

@@ -155,7 +155,7 @@ class StepPlan:
     Outputs (partials, own-token partial, merged result) are allocated once and overwritten by every run.
     """
 
-    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None, fixed_splits=False):
+    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None, fixed_splits=False, fused=True):
         import ctypes as C
         from . import _lib
 
@@ -222,20 +222,31 @@ class StepPlan:
         self.merge = m
         self._check = _lib.check
         self.stream = stream
+        # Without an own-token partial every merged partial is a stripe's: one cp_paged_attn_merged call computes them
+        # and merges them (the same bits as the partial call followed by the merge call).
+        self.fused = bool(fused) and self.own is None
+        self.merged_out = api._merge_out(self.merged, self.merged_lse)
 
     def _s(self):
         s = torch.cuda.current_stream() if self.stream is None else self.stream
         return self.C.c_void_p(s.cuda_stream)
 
     def partial(self):
-        self._check(self.lib.cp_paged_attn_partial(self.C.byref(self.paged), self._s()))
+        """The partial call (with the fused plan: the merged call, which also writes the merged output)."""
+        if self.fused:
+            self._check(self.lib.cp_paged_attn_merged(self.C.byref(self.paged), self.C.byref(self.merged_out),
+                                                      self._s()))
+        else:
+            self._check(self.lib.cp_paged_attn_partial(self.C.byref(self.paged), self._s()))
 
     def own_token(self):
         if self.own is not None:
             self._check(self.lib.cp_own_token_attn(self.C.byref(self.own), self._s()))
 
     def combine(self):
-        self._check(self.lib.cp_lse_merge(self.C.byref(self.merge), self._s()))
+        """The merge call (nothing with the fused plan: the merged call did it)."""
+        if not self.fused:
+            self._check(self.lib.cp_lse_merge(self.C.byref(self.merge), self._s()))
 
     def run(self):
         self.partial()

@@ -69,7 +69,7 @@ const char* cpattn_last_error(void);
 const char* cpattn_version(void);
 
 /* sizeof() of the argument structs, for bindings to check their layout: which = 0 cp_paged_args, 1 cp_own_args,
- * 2 cp_merge_args. Returns -1 for an unknown `which`. */
+ * 2 cp_merge_args, 3 cp_merge_out. Returns -1 for an unknown `which`. */
 int64_t cpattn_struct_size(int32_t which);
 
 /*
@@ -237,6 +237,39 @@ int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
 /* Workspace bytes cp_paged_attn_partial needs for `args` (depends on shapes and the host bounds only; the pointers in
  * `args` are not looked at). EINVAL/EUNSUPPORTED as cp_paged_attn_partial for everything but pointers. */
 int32_t cp_paged_attn_workspace_size(const cp_paged_args* args, int64_t* bytes_out);
+
+/*
+ * Merged output of cp_paged_attn_merged.
+ *   out (t, h, d) at out + t*out_stride_token + h*out_stride_head + d, fp32 or bf16 (round to nearest even);
+ *   lse (t, h) at lse + t*lse_stride_token + h (fp32, natural log; nullable).
+ */
+typedef struct cp_merge_out {
+    int32_t out_dtype;        /* CPATTN_F32 or CPATTN_BF16 */
+    int32_t reserved0;
+    void* out;
+    int64_t out_stride_token, out_stride_head;
+    float* lse;
+    int64_t lse_stride_token;
+} cp_merge_out;
+
+/*
+ * cp_paged_attn_merged: every stripe's partial and their exact merge, in one call, when all P stripes are resident on
+ * the device (stripe_begin = 0, stripe_count = P).
+ *
+ * Source: each partner's partial with its log-sum-exp, then the exact merge of the partials (mstar PR #1124, PR
+ * description); on one device the exchange between partners is the merge reading resident partials, so the step can
+ * finish the split pieces of each stripe and merge the stripes in the same pass.
+ *
+ * Results: exactly those of cp_paged_attn_partial(args) followed by cp_lse_merge of its S partials with token_count =
+ * q_row_start + num_rows (the same bits): args->out / args->lse receive the per-stripe partials and `merged` the merged
+ * output; tokens at or past q_row_start[num_rows] come out as (0, -inf). On the bf16 head_dim-128 decode path with the
+ * default schedule the fix-up of split pieces and the merge run as one kernel after the partial kernel; every other
+ * path runs the partial call and the merge call back to back.
+ * EINVAL: as cp_paged_attn_partial; a null `merged` or merged->out (num_tokens > 0); stripe_begin != 0 or
+ * stripe_count != P; an unknown out_dtype; merged->out not 16-byte aligned or strides not multiples of 8 elements;
+ * merged->out equal to args->out.
+ */
+int32_t cp_paged_attn_merged(const cp_paged_args* args, const cp_merge_out* merged, hipStream_t stream);
 
 /*
  * cp_paged_attn_partial_noalloc: cp_paged_attn_partial for callers that cannot allocate device memory (code under HIP

@@ -39,7 +39,29 @@ def test_struct_layouts_match(lib):
     assert lib.cpattn_struct_size(0) == C.sizeof(_lib.PagedArgs)
     assert lib.cpattn_struct_size(1) == C.sizeof(_lib.OwnArgs)
     assert lib.cpattn_struct_size(2) == C.sizeof(_lib.MergeArgs)
+    assert lib.cpattn_struct_size(3) == C.sizeof(_lib.MergeOut)
     assert lib.cpattn_struct_size(7) == -1
+
+
+def test_merged_call_refusals(lib):
+    """cp_paged_attn_merged refuses a stripe subset, a missing or misaligned merged output and an unknown dtype, on
+    the host."""
+    m = _lib.MergeOut()
+    m.out_dtype, m.out = 1, 4096
+    a = _paged()
+    assert lib.cp_paged_attn_merged(C.byref(a), None, None) == _lib.CPATTN_EINVAL
+    b = _paged(stripe_begin=1, stripe_count=3)
+    assert lib.cp_paged_attn_merged(C.byref(b), C.byref(m), None) == _lib.CPATTN_EINVAL
+    assert "resident stripes" in _err(lib)
+    m.out_dtype = 5
+    assert lib.cp_paged_attn_merged(C.byref(a), C.byref(m), None) == _lib.CPATTN_EINVAL
+    m.out_dtype, m.out = 1, 4104                                 # not 16-byte aligned
+    assert lib.cp_paged_attn_merged(C.byref(a), C.byref(m), None) == _lib.CPATTN_EINVAL
+    m.out, m.out_stride_head = 4096, 4                           # head stride not a multiple of 8
+    assert lib.cp_paged_attn_merged(C.byref(a), C.byref(m), None) == _lib.CPATTN_EINVAL
+    m.out_stride_head, m.out = 128, 16                           # the partial buffer itself
+    assert lib.cp_paged_attn_merged(C.byref(a), C.byref(m), None) == _lib.CPATTN_EINVAL
+    assert "alias" in _err(lib)
 
 
 def test_version(lib):
