@@ -16,6 +16,7 @@ CPATTN_KV_SAME, CPATTN_KV_FP8_E4M3 = 0, 1
 CPATTN_GQA, CPATTN_MLA = 0, 1
 MAX_PARTIALS = 17
 CPATTN_FLAG_FIXED_SPLITS = 1
+CPATTN_FLAG_PAD_LSE_ONLY = 2
 
 _p = C.c_void_p
 _i32 = C.c_int32
@@ -43,7 +44,7 @@ class PagedArgs(C.Structure):
 class OwnArgs(C.Structure):
     _fields_ = [
         ("dtype", _i32), ("num_rows", _i32), ("bucket_tokens", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
-        ("head_dim", _i32), ("scale", C.c_float), ("max_row_tokens", _i32),
+        ("head_dim", _i32), ("scale", C.c_float), ("max_row_tokens", _i32), ("flags", _i32), ("reserved0", _i32),
         ("cu_seqlens", _p), ("q", _p), ("q_stride_token", _i64), ("q_stride_head", _i64),
         ("k", _p), ("v", _p), ("kv_stride_token", _i64), ("kv_stride_head", _i64),
         ("out", _p), ("out_stride_token", _i64), ("out_stride_head", _i64),

@@ -146,9 +146,9 @@ def kv_write(logical_slot, k_src, v_src, k_pool, v_pool, page_size: int, partner
 
 def _paged_args(q, k_pool, v_pool, q_row_start, ctx_len, block_table, *, page_size, partners, scale, kind,
                 stripe_begin, stripe_count, max_ctx_len, max_row_tokens, out, lse, num_tokens, fixed_splits=False,
-                interleave=1, k_descale=1.0, v_descale=1.0):
+                interleave=1, k_descale=1.0, v_descale=1.0, pad_lse_only=False):
     a = PagedArgs()
-    a.flags = _lib.CPATTN_FLAG_FIXED_SPLITS if fixed_splits else 0
+    a.flags = (_lib.CPATTN_FLAG_FIXED_SPLITS if fixed_splits else 0) | (_lib.CPATTN_FLAG_PAD_LSE_ONLY if pad_lse_only else 0)
     a.interleave = int(interleave)
     a.kind = CPATTN_MLA if kind == "mla" else CPATTN_GQA
     a.dtype = _dtype_code(q.dtype)

@@ -45,7 +45,8 @@ static int32_t check_paged(const cp_paged_args* pa, PoolGeom* geo) {
     const cp_paged_args& a = *pa;
     if (a.kind != CPATTN_GQA && a.kind != CPATTN_MLA) return fail(CPATTN_EINVAL, "kind = %d unknown", a.kind);
     if (a.dtype != CPATTN_F32 && a.dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype = %d unknown", a.dtype);
-    if (a.flags & ~CPATTN_FLAG_FIXED_SPLITS) return fail(CPATTN_EINVAL, "flags = %#x has unknown bits", a.flags);
+    if (a.flags & ~(CPATTN_FLAG_FIXED_SPLITS | CPATTN_FLAG_PAD_LSE_ONLY))
+        return fail(CPATTN_EINVAL, "flags = %#x has unknown bits", a.flags);
     if (a.num_rows < 0 || a.num_tokens < 0 || a.max_ctx_len < 0 || a.max_row_tokens < 0 || a.max_pages < 0)
         return fail(CPATTN_EINVAL, "negative size");
     if (a.num_partners < 1 || a.num_partners > 16)
@@ -259,6 +260,7 @@ extern "C" int32_t cp_own_token_attn(const cp_own_args* pa, hipStream_t stream) 
     const cp_own_args& a = *pa;
     if (a.dtype != CPATTN_F32 && a.dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype = %d unknown", a.dtype);
     if (a.num_rows < 0 || a.bucket_tokens < 0 || a.max_row_tokens < 0) return fail(CPATTN_EINVAL, "negative size");
+    if (a.flags & ~CPATTN_FLAG_PAD_LSE_ONLY) return fail(CPATTN_EINVAL, "flags = %#x has unknown bits", a.flags);
     if (a.num_q_heads < 1 || a.num_kv_heads < 1 || a.num_q_heads % a.num_kv_heads)
         return fail(CPATTN_EINVAL, "num_q_heads = %d must be a positive multiple of num_kv_heads = %d", a.num_q_heads,
                     a.num_kv_heads);

@@ -160,12 +160,14 @@ __device__ __forceinline__ float lse_merge_rows(const float (&l)[NMAX], const f3
 }
 
 // Write (0, -inf) for padding query tokens [t_begin, t_end) of S partials (Hq heads, Dv dims each).
+// With lse_only (CPATTN_FLAG_PAD_LSE_ONLY) the out rows are left as they are.
 __device__ __forceinline__ void fill_padding(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse,
                                              int64_t l_ss, int64_t l_st, int32_t S, int32_t Hq, int32_t Dv,
-                                             int32_t t_begin, int32_t t_end, int lane, int nlanes) {
+                                             int32_t t_begin, int32_t t_end, int lane, int nlanes,
+                                             bool lse_only = false) {
     for (int32_t t = t_begin; t < t_end; ++t) {
         for (int32_t s = 0; s < S; ++s) {
-            for (int32_t h = 0; h < Hq; ++h) {
+            for (int32_t h = 0; h < Hq && !lse_only; ++h) {
                 float* o = out + s * o_ss + int64_t(t) * o_st + int64_t(h) * o_sh;
                 for (int32_t d = lane; d < Dv; d += nlanes) o[d] = 0.0f;
             }

@@ -19,14 +19,16 @@
 //
 // Per tile and wave (32 rows x 32 tokens):
 //   * scores S^T[token][row] = K . Q^T with v_mfma_f32_16x16x32_bf16 (16 MFMAs): A = K rows from LDS, B = query rows.
-//   * online softmax with a lazily moved running max (moved when a tile maximum exceeds it by more than 8 in log2
-//     units; the scale enters each exponent through one fused multiply-add; row maxima and sums over the four lane
-//     groups use the gfx950 lane swaps); keys past the end and, in the own-token part, keys after the query's own
-//     token are masked (only on the tiles that reach them).
-//   * out += P . V with the same MFMA: the score layout is the A-operand layout (k index 8c + e of lane group c is tile
-//     token 16 (e / 4) + 4c + e % 4), the B operand of a 16-dim output tile comes from two transposed LDS reads
-//     (ds_read_b64_tr_b16). P enters as a bf16 pair hi + lo (about 16 significant bits), so a softmax peaked on a few
-//     keys keeps fp32-level accuracy (32 MFMAs).
+//   * softmax against a fixed per-row reference (the maximum of the unit's first tile; the scale enters each exponent
+//     through one fused multiply-add; row maxima and sums over the four lane groups use the gfx950 lane swaps); keys
+//     past the end and, in the own-token part, keys after the query's own token are masked (only on the tiles that
+//     reach them).
+//   * out += P . V with v_mfma_f32_16x16x32_f16: the score layout is the A-operand layout (k index 8c + e of lane
+//     group c is tile token 16 (e / 4) + 4c + e % 4), the B operand of a 16-dim output tile comes from two transposed
+//     LDS reads (ds_read_b64_tr_b16) widened from bf16 to fp16 in registers (exact: value magnitudes must stay below
+//     65504). P enters rounded to fp16 (11 significant bits) and each row is normalised by the sum of exactly those
+//     rounded weights, so they sum to one; one bf16 rounding of P (8 bits) put a softmax peaked on a few keys past
+//     2e-3 of the float64 result, and the earlier bf16 pair (hi + residual, 16 bits) took twice the MFMAs (16 MFMAs).
 //
 // LDS layout of a tile: K rows of 256 bytes at 256 t, V rows at 8192 + 256 t; the sixteen 16-byte pieces of token t
 // are stored XOR f(t) = 2t mod 16. Measured on gfx950, the score reads (sixteen tokens at one piece) and the transposed
@@ -79,12 +81,30 @@ struct ExtParams {
     int32_t B, T, P, stripe_begin, S, Hq, Hkv, G, max_pages, page_size, max_row_tokens;
     int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_qblocks, n_units, pad_tokens_per_block;
+    int32_t pad_lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get their lse only
     float scale_log2;
 };
 
 __device__ __forceinline__ int swz(int t) { return (2 * t) & 15; }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed fp16 pair, round to nearest even (inf past the fp16 range).
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+
+// Eight bf16 values to eight fp16 values in the same order: exact for magnitudes in [2^-14, 65504], within 2^-25
+// absolute below that.
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(u32x4_t v) {
+    u32x4_t r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) r[d] = pack2_f16(__uint_as_float(v[d] << 16), __uint_as_float(v[d] & 0xffff0000u));
+    return __builtin_bit_cast(f16x8_t, r);
+}
 
 // s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
 template <int N>
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
         if (t0 < t1)
             fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, kD, t0, t1, threadIdx.x,
-                         blockDim.x);
+                         blockDim.x, p.pad_lse_only);
         return;
     }
 
@@ -295,8 +315,9 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
                                                                                      : (lds_char_ptr)s_tile3;
     };
     f32x4_t o[2][8];                                        // o[rb][db][i]: row 16 rb + 4 c4 + i, dim 16 db + n16
-    // m: softmax reference of each row in raw score units (p = 2^((s - m) * scale_log2)); l: the rows' sums of p.
-    float m[2], l[2];
+    // m: softmax reference of each row in raw score units (p = 2^((s - m) * scale_log2)); l: the rows' sums of p (for
+    // the lse); lr: the rows' sums of the fp16-rounded p that weight the values (for the normalisation).
+    float m[2], l[2], lr[2];
     auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -304,6 +325,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
             for (int db = 0; db < 8; ++db) o[rb][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             m[rb] = neg_inf();
             l[rb] = 0.f;
+            lr[rb] = 0.f;
         }
     };
 
@@ -376,8 +398,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         tile_scores(tile, kt, sv);
         const float c = p.scale_log2;
         // p = 2^((s - m) * scale_log2): one fused multiply-add per score (the launch requires scale_log2 > 0, which
-        // keeps the order of the scores); P as a bf16 pair hi = bf16(p), lo = bf16(p - hi).
-        u32x4_t phi[2], plo[2];
+        // keeps the order of the scores); P enters the value product rounded to fp16 (11 significant bits).
+        u32x4_t ph[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const float mc = -m[rb] * c;
@@ -386,28 +408,26 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
             for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][e], c, mc));
             l[rb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t hw = pack2_bf16(pv[2 * d], pv[2 * d + 1]);
-                phi[rb][d] = hw;
-                plo[rb][d] = pack2_bf16(pv[2 * d] - __uint_as_float(hw << 16), pv[2 * d + 1] - __uint_as_float(hw & 0xffff0000u));
-            }
+            for (int d = 0; d < 4; ++d) ph[rb][d] = pack2_f16(pv[2 * d], pv[2 * d + 1]);
+            const f16x8_t pr = __builtin_bit_cast(f16x8_t, ph[rb]);
+            lr[rb] += ((float(pr[0]) + float(pr[1])) + (float(pr[2]) + float(pr[3]))) +
+                      ((float(pr[4]) + float(pr[5])) + (float(pr[6]) + float(pr[7])));
         }
 
-        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads. The lo product
-        // follows the hi product into the same accumulator; the matrix core forwards the accumulator between them.
+        // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads, widened from bf16
+        // to fp16 in registers.
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[1][db]));
-            const bf16x8_t bop =
-                __builtin_bit_cast(bf16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            const f16x8_t bop = bf16x8_to_f16(
+                __builtin_bit_cast(u32x4_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rb]), bop, o[rb][db], 0, 0, 0);
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rb]), bop, o[rb][db], 0, 0, 0);
-            }
+            for (int rb = 0; rb < 2; ++rb)
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ph[rb]), bop, o[rb][db],
+                                                                  0, 0, 0);
         }
-        sched_pipeline<32, 2, 8>();
+        sched_pipeline<16, 1, 8>();
     };
 
     // One iteration with buffer bb (compile time): wait for tile kt, issue the loads of tile kt + kAhead into buffer
@@ -452,11 +472,12 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         for (int rb = 0; rb < 2; ++rb) {
             float ls = l[rb];
             ls = group_sum(ls);
+            const float lrs = group_sum(lr[rb]);
             z += 0.f * ls;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int32_t rho = wrow0 + 16 * rb + 4 * c4 + i;
-                const float li = __shfl(ls, 4 * c4 + i);
+                const float li = __shfl(lrs, 4 * c4 + i);
 #pragma unroll
                 for (int db = 0; db < 8; ++db) z += 0.f * o[rb][db][i];
                 if (rho < nrows) {
@@ -478,8 +499,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     };
 
     // The reference m of each row is the maximum of its first tile's scores (key 0 is valid for every row, so it is
-    // finite), and the loop never moves it. A later score above the reference by more than about 128 (log2 units)
-    // overflows p, the sums or the accumulators to inf or NaN; the workgroup then finds the exact row maxima with a
+    // finite), and the loop never moves it. A later score above the reference by more than about 16 (log2 units)
+    // overflows the fp16 weights (and further on p and the sums) to inf; the workgroup then finds the exact row maxima with a
     // scores-only pass and runs the loop once more (every p now at most 1), overwriting the rows it stored. Any other
     // outcome is the same softmax with a different reference.
     reset();
@@ -585,6 +606,7 @@ int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;
+    p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
     return launch_extend(p, kFromPool, stream);
 }
 
@@ -630,6 +652,7 @@ int32_t launch_own_token_bf16(const cp_own_args& a, hipStream_t stream) {
     p.page_size = 1;
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;
+    p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
     return launch_extend(p, kFromOwn, stream);
 }
 

@@ -52,7 +52,7 @@ int32_t launch_pad_partials(const cp_paged_args& a, hipStream_t stream);
 
 // (0, -inf) for tokens [starts[B], T) of S outputs with Hq heads of Dv values (starts is a device array).
 int32_t launch_pad(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse, int64_t l_ss, int64_t l_st,
-                   const int32_t* starts, int32_t B, int32_t T, int32_t S, int32_t Hq, int32_t Dv,
+                   const int32_t* starts, int32_t B, int32_t T, int32_t S, int32_t Hq, int32_t Dv, bool lse_only,
                    hipStream_t stream);
 
 // Own-token causal attention (generic: f32/bf16, head_dim 64 or 128).

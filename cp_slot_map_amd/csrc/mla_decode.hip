@@ -95,6 +95,7 @@ struct MlaParams {
     int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_chunks, chunk_tokens, n_units, pad_blocks, pad_tokens_per_block;
     int32_t head_groups, work_blocks;   // workgroups per unit (1 or 2) and blocks before the padding role
+    int32_t pad_lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get their lse only
     float scale_log2;
 };
 
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
         if (t0 < t1)
             fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, kDv, t0, t1, threadIdx.x,
-                         blockDim.x);
+                         blockDim.x, p.pad_lse_only);
         return;
     }
     const int32_t rank = blk, hg = 0;                       // one workgroup serves all query heads of a unit
@@ -769,6 +770,7 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.head_groups = int32_t(d.head_groups);
     p.work_blocks = int32_t(d.work_blocks);
     p.scale_log2 = a.scale * kLog2e;
+    p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
 
     if (p.order) {
         hipLaunchKernelGGL(mla_plan_kernel, dim3(uint32_t((d.n_units + 63) / 64)), dim3(256), 0, stream, p);

@@ -125,7 +125,8 @@ int32_t launch_own_token_generic(const cp_own_args& a, hipStream_t stream) {
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;
     if (int32_t st = launch_pad(a.out, 0, a.out_stride_token, a.out_stride_head, a.lse, 0, a.lse_stride_token,
-                                a.cu_seqlens, a.num_rows, a.bucket_tokens, 1, a.num_q_heads, a.head_dim, stream))
+                                a.cu_seqlens, a.num_rows, a.bucket_tokens, 1, a.num_q_heads, a.head_dim,
+                                (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) != 0, stream))
         return st;
     if (a.num_rows == 0 || a.max_row_tokens == 0) return CPATTN_OK;
     constexpr int R = 8;

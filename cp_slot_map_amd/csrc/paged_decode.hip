@@ -61,6 +61,7 @@ struct DecodeParams {
     int32_t num_tiles, nwaves;    // persistent schedule
     float scale_log2;             // softmax scale (times the key descale for fp8 pools) in log2 units
     float v_scale;                // value descale of fp8 pools, else 1 (applied where output rows are written)
+    int32_t pad_lse_only;         // CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get their lse only
     void* m_out;                  // fused finish: merged output [T, Hq, 128] (fp32 or bf16), its lse (nullable)
     int64_t m_st, m_sh;
     float* m_lse;
@@ -326,7 +327,9 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
         const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
         const int32_t t0 = max(k * p.pad_tokens_per_block, first);
         const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
-        if (t0 < t1) fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        if (t0 < t1)
+            fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64,
+                         p.pad_lse_only);
         return;
     }
 
@@ -859,12 +862,14 @@ __global__ __launch_bounds__(64, 2) void gqa_decode_persist_kernel(const DecodeP
     int32_t N = 0;
     const int32_t my_excl = wave_exclusive_scan(my_sum, lane, N);
     if (w == 0) publish_row_prefix(p, r_lo, r_hi, my_excl, N, lane);
-    const int64_t total = int64_t(p.Hkv) * N;
-    const int64_t Q = (total + nw - 1) / nw;
-    const int64_t start = int64_t(w) * Q;
+    // The host keeps Hkv * N below 2^31 for this schedule, so the step-space arithmetic is 32-bit (64-bit divisions
+    // are long software sequences).
+    const uint32_t total = uint32_t(p.Hkv) * uint32_t(N);
+    const uint32_t Q = (total + uint32_t(nw) - 1) / uint32_t(nw);
+    const uint32_t start = uint32_t(w) * Q;
     if (start >= total) return;
     int64_t remaining = min(Q, total - start);
-    int32_t g = int32_t(start / N);
+    int32_t g = int32_t(start / uint32_t(N));
     const int32_t pos = int32_t(start - int64_t(g) * N);
 
     // The row holding `pos`: first the lane, then the row among the lane's (from registers when R <= 4, else one row
@@ -1062,7 +1067,9 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
         const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
         const int32_t t0 = max(k * p.pad_tokens_per_block, first);
         const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
-        if (t0 < t1) fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        if (t0 < t1)
+            fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64,
+                         p.pad_lse_only);
         return;
     }
     const int32_t T = idx / p.Hkv;
@@ -1084,10 +1091,10 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
         return;
     }
     const int32_t N = p.ws_rowpref[p.B];
-    const int64_t total = int64_t(p.Hkv) * N;
-    const int64_t Q = (total + p.nwaves - 1) / p.nwaves;
-    const int64_t A = int64_t(g) * N + tile_offset(p, tl.b, tl.s, tl.qt, tl.q0, tl.q1, tl.cl);
-    const int64_t Bend = A + tl.n_steps;
+    const uint32_t total = uint32_t(p.Hkv) * uint32_t(N);
+    const uint32_t Q = (total + uint32_t(p.nwaves) - 1) / uint32_t(p.nwaves);
+    const uint32_t A = uint32_t(g) * uint32_t(N) + uint32_t(tile_offset(p, tl.b, tl.s, tl.qt, tl.q0, tl.q1, tl.cl));
+    const uint32_t Bend = A + uint32_t(tl.n_steps);
     const int64_t wA = A / Q, wB = (Bend - 1) / Q;
     if (wA == wB) return;                            // one wave covered it and wrote it
     for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
@@ -1135,7 +1142,8 @@ __global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParam
         const int32_t t0 = max(k * p.pad_tokens_per_block, first);
         const int32_t t1 = min((k + 1) * p.pad_tokens_per_block, p.T);
         if (t0 >= t1) return;
-        fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64);
+        fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, 128, t0, t1, lane, 64,
+                     p.pad_lse_only);
         const f32x4_t zero[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         for (int32_t t = t0; t < t1; ++t)
             for (int32_t h = rsub; h < p.Hq; h += 4) merged_row(t, h, zero);
@@ -1147,10 +1155,11 @@ __global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParam
     const int32_t g = idx % p.Hkv;
     const int32_t qt = (idx / p.Hkv) % p.n_qtiles;
     const int32_t b = (idx / p.Hkv) / p.n_qtiles;
+    // The row's offsets, length and step offset in one round trip (scalar loads, all issued before any is used).
     const const_i32_ptr qrs = (const_i32_ptr)p.q_row_start;
     const const_i32_ptr clp = (const_i32_ptr)p.ctx_len;
-    const int32_t q0 = qrs[b], q1 = qrs[b + 1], cl = clp[b];
-    const int32_t rowpref = p.ws_rowpref[b], N = p.ws_rowpref[p.B];
+    const const_i32_ptr rp = (const_i32_ptr)p.ws_rowpref;
+    const int32_t q0 = qrs[b], q1 = qrs[b + 1], cl = clp[b], rowpref = rp[b], N = rp[p.B];
     const int32_t tok0 = min(max(q0, 0), p.T);
     const int32_t tok1 = min(max(q1, tok0), p.T);
     const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
@@ -1159,58 +1168,105 @@ __global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParam
     const int32_t tile_rows = min(16, nrows - row0);
     const int32_t nq = (nrows + 15) >> 4;
     const int32_t L = min(max(cl, 0), p.ctx_cap);
-    const int64_t total = int64_t(p.Hkv) * N;
-    const int64_t Q = (total + p.nwaves - 1) / p.nwaves;
+    const uint32_t total = uint32_t(p.Hkv) * uint32_t(N);
+    const uint32_t Q = (total + uint32_t(p.nwaves) - 1) / uint32_t(p.nwaves);
+    // Per stripe: its steps n, the item's first step A in the step space and the covering waves wA..wB. All loads of a
+    // row group (partials of items one wave covered, the first two records of split items) are issued before anything
+    // is stored, so a wave waits for one memory round trip rather than one per stripe.
+    int32_t n_s[SMAX];
+    uint32_t A_s[SMAX], wA_s[SMAX], wB_s[SMAX];
+    {
+        uint32_t off = uint32_t(g) * uint32_t(N) + uint32_t(rowpref);
+#pragma unroll
+        for (int32_t s = 0; s < SMAX; ++s) {
+            const int32_t n = s < p.S ? (stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave) + 15) >> 4 : 0;
+            n_s[s] = n;
+            A_s[s] = off + uint32_t(qt * n);
+            off += uint32_t(nq * n);
+            wA_s[s] = n > 0 ? A_s[s] / Q : 0;
+            wB_s[s] = n > 0 ? (A_s[s] + uint32_t(n) - 1) / Q : 0;
+        }
+    }
+    const int32_t RR = p.rec_rows;
+    const int64_t rec_floats = int64_t(RR) * 130;
     for (int32_t rg = 0; 4 * rg < tile_rows; ++rg) {
         const int32_t row = 4 * rg + rsub;
         const bool active = row < tile_rows;
         const int32_t rho = row0 + min(row, tile_rows - 1);
         const int32_t t = tok0 + rho / p.G;
         const int32_t h = g * p.G + rho % p.G;
-        float ls[SMAX];
-        f32x4_t os[SMAX][2];
-        int64_t off = int64_t(g) * N + rowpref;
+        const int32_t rrow = min(row, RR - 1);
+        // Loads, all unconditional (to addresses inside the buffers) so that they issue together: the partial row the
+        // persistent kernel wrote, and the first two records of the item's covering waves (most items are split over
+        // two waves at most; more take the general record merge below). What the item needs is selected after.
+        float ls[SMAX], m0[SMAX], l0[SMAX], m1[SMAX], l1[SMAX];
+        f32x4_t os[SMAX][2], r0[SMAX][2], r1[SMAX][2];
 #pragma unroll
         for (int32_t s = 0; s < SMAX; ++s) {
+            const int32_t sc = min(s, p.S - 1);
+            const float* o = p.out + sc * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * d8;
+            const float* lp = p.lse + sc * p.l_ss + int64_t(t) * p.l_st + h;
+            const int64_t wA = wA_s[s];                  // (64-bit for the record addresses)
+            const int64_t wA1 = min(wA + 1, int64_t(p.nwaves) - 1);
+            const float* rc0 = p.ws_rec + (wA * 2 + (wA_s[s] * Q >= A_s[s] ? 0 : 1)) * rec_floats;
+            const float* rc1 = p.ws_rec + (wA1 * 2) * rec_floats;   // the second wave starts inside the item
+            os[s][0] = *reinterpret_cast<const f32x4_t*>(o);
+            os[s][1] = *reinterpret_cast<const f32x4_t*>(o + 4);
+            ls[s] = *lp;
+            m0[s] = rc0[RR * 128 + rrow];
+            l0[s] = rc0[RR * 128 + RR + rrow];
+            r0[s][0] = *reinterpret_cast<const f32x4_t*>(rc0 + rrow * 128 + 8 * d8);
+            r0[s][1] = *reinterpret_cast<const f32x4_t*>(rc0 + rrow * 128 + 8 * d8 + 4);
+            m1[s] = rc1[RR * 128 + rrow];
+            l1[s] = rc1[RR * 128 + RR + rrow];
+            r1[s][0] = *reinterpret_cast<const f32x4_t*>(rc1 + rrow * 128 + 8 * d8);
+            r1[s][1] = *reinterpret_cast<const f32x4_t*>(rc1 + rrow * 128 + 8 * d8 + 4);
+        }
+#pragma unroll
+        for (int32_t s = 0; s < SMAX; ++s) {
+            if (s < p.S && n_s[s] > 0 && wA_s[s] == wB_s[s]) continue;    // the partial row as loaded
+            os[s][0] = os[s][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};          // empty stripe (or past S): (0, -inf)
             ls[s] = neg_inf();
-            os[s][0] = os[s][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            if (s >= p.S) continue;
-            const int32_t n = (stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave) + 15) >> 4;
-            const int64_t A = off + int64_t(qt) * n;
-            off += int64_t(nq) * n;
-            float* o = p.out + s * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * d8;
-            float* lp = p.lse + s * p.l_ss + int64_t(t) * p.l_st + h;
-            if (n == 0) {                            // no context in this stripe: (0, -inf)
-                if (active) {
-                    *reinterpret_cast<f32x4_t*>(o) = os[s][0];
-                    *reinterpret_cast<f32x4_t*>(o + 4) = os[s][1];
-                    if (d8 == 0) *lp = neg_inf();
-                }
-                continue;
-            }
-            const int64_t wA = A / Q, wB = (A + n - 1) / Q;
-            if (wA == wB) {                          // one wave covered it and wrote the partial
-                os[s][0] = *reinterpret_cast<const f32x4_t*>(o);
-                os[s][1] = *reinterpret_cast<const f32x4_t*>(o + 4);
-                ls[s] = *lp;
-                continue;
-            }
+        }
+        // Stripe partials of split items (the arithmetic of merge_records and of the partial writes), then stores.
+#pragma unroll
+        for (int32_t s = 0; s < SMAX; ++s) {
+            if (n_s[s] == 0 || wA_s[s] == wB_s[s]) continue;
             float M, Lsum;
             f32x4_t a0, a1;
-            merge_records(p, A, Q, wA, wB, min(row, p.rec_rows - 1), d8, M, Lsum, a0, a1);
+            if (wB_s[s] == wA_s[s] + 1) {
+                // merge_records over two records: the first batch of its loop with entries 2, 3 at -inf
+                M = fmaxf(fmaxf(neg_inf(), m0[s]), m1[s]);
+                const float w0 = m0[s] == neg_inf() ? 0.f : exp2f(m0[s] - M);
+                const float w1 = m1[s] == neg_inf() ? 0.f : exp2f(m1[s] - M);
+                Lsum = 0.f;
+                a0 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                a1 = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                Lsum += w0 * l0[s];
+                a0 += w0 * r0[s][0];
+                a1 += w0 * r0[s][1];
+                Lsum += w1 * l1[s];
+                a0 += w1 * r1[s][0];
+                a1 += w1 * r1[s][1];
+            } else {
+                merge_records(p, A_s[s], Q, wA_s[s], wB_s[s], rrow, d8, M, Lsum, a0, a1);
+            }
             // The values write_row and write_lse store for this partial.
             const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
             const float c = p.v_scale;
             os[s][0] = (f32x4_t){(a0[0] * inv) * c, (a0[1] * inv) * c, (a0[2] * inv) * c, (a0[3] * inv) * c};
             os[s][1] = (f32x4_t){(a1[0] * inv) * c, (a1[1] * inv) * c, (a1[2] * inv) * c, (a1[3] * inv) * c};
             ls[s] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf();
-            if (active) {
-                *reinterpret_cast<f32x4_t*>(o) = os[s][0];
-                *reinterpret_cast<f32x4_t*>(o + 4) = os[s][1];
-                if (d8 == 0) *lp = ls[s];
-            }
         }
         if (!active) continue;
+#pragma unroll
+        for (int32_t s = 0; s < SMAX; ++s) {
+            if (s >= p.S || (n_s[s] > 0 && wA_s[s] == wB_s[s])) continue;   // written by the persistent kernel
+            float* o = p.out + s * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + 8 * d8;
+            *reinterpret_cast<f32x4_t*>(o) = os[s][0];
+            *reinterpret_cast<f32x4_t*>(o + 4) = os[s][1];
+            if (d8 == 0) p.lse[s * p.l_ss + int64_t(t) * p.l_st + h] = ls[s];
+        }
         f32x4_t acc[2];
         const float lse = lse_merge_rows<SMAX, 2>(ls, os, acc);
         merged_row(t, h, acc);
@@ -1237,7 +1293,10 @@ static DecodeShape decode_shape(const cp_paged_args& a) {
     const int64_t rows = int64_t(a.max_row_tokens) * G;
     d.n_qtiles = std::max<int64_t>(1, (rows + 15) / 16);
     d.num_tiles = int64_t(a.num_rows) * a.stripe_count * d.n_qtiles;
-    d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && d.num_tiles <= kMaxPersistTiles;
+    // The persistent schedule's step space (kv heads x tiles x 16-key steps) is addressed with 32-bit arithmetic.
+    const int64_t max_steps = (max_stripe_length(a) + 15) / 16;
+    d.persistent = !(a.flags & CPATTN_FLAG_FIXED_SPLITS) && d.num_tiles <= kMaxPersistTiles &&
+                   int64_t(a.num_kv_heads) * d.num_tiles * max_steps + kMaxPersistWaves < (int64_t(1) << 31);
     const int64_t max_lr = max_stripe_length(a);
     const int64_t CH = int64_t(kChunkSteps) * 16;
     d.n_chunks = d.persistent ? 1 : std::max<int64_t>(1, (max_lr + CH - 1) / CH);
@@ -1301,7 +1360,8 @@ int64_t decode_bf16_workspace_bytes_on_device(const cp_paged_args& a, const Pool
     return rowpref_bytes(a) + int64_t(nw) * 2 * d.rec_rows * 130 * 4;
 }
 
-bool decode_bf16_fuses_merge(const cp_paged_args& a) { return decode_shape(a).persistent && a.num_partners <= 16; }
+// The fused finish holds every stripe's rows in registers: up to 8 stripes (more run the partial and merge calls).
+bool decode_bf16_fuses_merge(const cp_paged_args& a) { return decode_shape(a).persistent && a.stripe_count <= 8; }
 
 int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream,
                                  const cp_merge_out* m) {
@@ -1347,6 +1407,7 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
     p.scale_log2 = a.scale * (kv8 ? a.k_descale : 1.0f) * kLog2e;
     p.v_scale = kv8 ? a.v_descale : 1.0f;
+    p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
     const int ppmode = geo.pp_shift >= 2 ? 2 : geo.pp_shift;
 
     if (d.persistent) {
@@ -1383,12 +1444,9 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
             if (a.stripe_count <= 4) {
                 if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 4>), grid, dim3(64), 0, stream, p);
                 else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 4>), grid, dim3(64), 0, stream, p);
-            } else if (a.stripe_count <= 8) {
+            } else {
                 if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 8>), grid, dim3(64), 0, stream, p);
                 else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 8>), grid, dim3(64), 0, stream, p);
-            } else {
-                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 16>), grid, dim3(64), 0, stream, p);
-                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 16>), grid, dim3(64), 0, stream, p);
             }
             return check_launch("cp_paged_attn_merged (finish)");
         }

@@ -121,6 +121,7 @@ struct PadParams {
     int64_t l_ss, l_st;
     const int32_t* q_row_start;
     int32_t B, T, S, Hq, Dv, tokens_per_block;
+    int32_t lse_only;    // CPATTN_FLAG_PAD_LSE_ONLY
 };
 
 __global__ __launch_bounds__(64) void pad_partials_kernel(const PadParams p) {
@@ -128,14 +129,15 @@ __global__ __launch_bounds__(64) void pad_partials_kernel(const PadParams p) {
     const int32_t t0 = max(int32_t(blockIdx.x) * p.tokens_per_block, first);
     const int32_t t1 = min(int32_t(blockIdx.x + 1) * p.tokens_per_block, p.T);
     if (t0 >= t1) return;
-    fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, p.Dv, t0, t1, threadIdx.x, 64);
+    fill_padding(p.out, p.o_ss, p.o_st, p.o_sh, p.lse, p.l_ss, p.l_st, p.S, p.Hq, p.Dv, t0, t1, threadIdx.x, 64,
+                 p.lse_only);
 }
 
 int32_t launch_pad(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* lse, int64_t l_ss, int64_t l_st,
-                   const int32_t* starts, int32_t B, int32_t T, int32_t S, int32_t Hq, int32_t Dv,
+                   const int32_t* starts, int32_t B, int32_t T, int32_t S, int32_t Hq, int32_t Dv, bool lse_only,
                    hipStream_t stream) {
     if (T == 0) return CPATTN_OK;
-    PadParams p{out, o_ss, o_st, o_sh, lse, l_ss, l_st, starts, B, T, S, Hq, Dv, 4};
+    PadParams p{out, o_ss, o_st, o_sh, lse, l_ss, l_st, starts, B, T, S, Hq, Dv, 4, lse_only ? 1 : 0};
     const dim3 grid(uint32_t((T + 3) / 4));
     hipLaunchKernelGGL(pad_partials_kernel, grid, dim3(64), 0, stream, p);
     return check_launch("padding fill");
@@ -144,7 +146,7 @@ int32_t launch_pad(float* out, int64_t o_ss, int64_t o_st, int64_t o_sh, float* 
 int32_t launch_pad_partials(const cp_paged_args& a, hipStream_t stream) {
     return launch_pad(a.out, a.out_stride_stripe, a.out_stride_token, a.out_stride_head, a.lse, a.lse_stride_stripe,
                       a.lse_stride_token, a.q_row_start, a.num_rows, a.num_tokens, a.stripe_count, a.num_q_heads,
-                      a.head_dim_v, stream);
+                      a.head_dim_v, (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) != 0, stream);
 }
 
 template <typename T, typename TKV, int NQ, int NV, int R>

@@ -150,12 +150,15 @@ def run_step(batch: Batch, *, out=None, lse=None, merged=None, merged_lse=None, 
 
 
 class StepPlan:
-    """A prepared hot-path step for one batch: argument structs are built once, each run() is 2-3 C calls.
+    """A prepared hot-path step for one batch: argument structs are built once, each run() is 1-3 C calls.
 
-    Outputs (partials, own-token partial, merged result) are allocated once and overwritten by every run.
+    Outputs (partials, own-token partial, merged result) are allocated once and overwritten by every run. With
+    ``pad_lse_only`` (the default, CPATTN_FLAG_PAD_LSE_ONLY) the partials of padding tokens get their -inf lse only;
+    the merge, told the real token count, writes the padding tokens' merged output as (0, -inf) without reading them.
     """
 
-    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None, fixed_splits=False, fused=True):
+    def __init__(self, batch: Batch, out_dtype=torch.float32, stream=None, fixed_splits=False, fused=True,
+                 pad_lse_only=True):
         import ctypes as C
         from . import _lib
 
@@ -176,7 +179,7 @@ class StepPlan:
                                      kind=wl.kind, stripe_begin=0, stripe_count=P, max_ctx_len=batch.max_ctx_len,
                                      max_row_tokens=batch.max_row_tokens, out=self.out, lse=self.lse, num_tokens=T,
                                      fixed_splits=fixed_splits, interleave=wl.interleave, k_descale=wl.k_descale,
-                                     v_descale=wl.v_descale)
+                                     v_descale=wl.v_descale, pad_lse_only=pad_lse_only)
         n = C.c_int64(0)
         _lib.check(self.lib.cp_paged_attn_workspace_size(C.byref(self.paged), C.byref(n)))
         self.workspace_bytes = int(n.value)
@@ -195,6 +198,7 @@ class StepPlan:
             a.num_rows, a.bucket_tokens = wl.batch, T
             a.num_q_heads, a.num_kv_heads, a.head_dim = Hq, batch.k_new.shape[1], batch.k_new.shape[2]
             a.scale, a.max_row_tokens = float(wl.scale), batch.max_row_tokens
+            a.flags = _lib.CPATTN_FLAG_PAD_LSE_ONLY if pad_lse_only else 0
             a.cu_seqlens, a.q = batch.cu_seqlens.data_ptr(), batch.q.data_ptr()
             a.q_stride_token, a.q_stride_head = batch.q.stride(0), batch.q.stride(1)
             a.k, a.v = batch.k_new.data_ptr(), batch.v_new.data_ptr()

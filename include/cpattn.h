@@ -61,6 +61,9 @@ extern "C" {
 
 /* cp_paged_args.flags */
 #define CPATTN_FLAG_FIXED_SPLITS 1   /* see cp_paged_attn_partial: results independent of the rest of the call */
+#define CPATTN_FLAG_PAD_LSE_ONLY 2   /* padding tokens get lse = -inf only; their out rows are not written (cp_lse_merge
+                                        selects a -inf partial out and never reads its row, and with token_count it
+                                        reads no padding token at all) */
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* cpattn_last_error(void);
@@ -166,7 +169,7 @@ typedef struct cp_paged_args {
                                  ctx_len exceeds it is taken as its first max_ctx_len tokens (every kernel clamps) */
     int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
     int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
-    int32_t flags;            /* 0 or CPATTN_FLAG_FIXED_SPLITS; other bits are EINVAL */
+    int32_t flags;            /* CPATTN_FLAG_FIXED_SPLITS | CPATTN_FLAG_PAD_LSE_ONLY; other bits are EINVAL */
     int32_t interleave;       /* KV-cache interleave size I (0 or 1: none); the placement of cp_slot_map; I * P must
                                  divide page_size */
     int32_t kv_format;        /* CPATTN_KV_SAME or CPATTN_KV_FP8_E4M3 (dtype bf16 only) */
@@ -205,8 +208,8 @@ typedef struct cp_paged_args {
  * floor(p / I) mod P == r (p mod P == r without interleave: the slots partner r holds); local token i of stripe r is
  * position floor(i / I) * I * P + r * I + i mod I (i*P + r for I = 1), found at page block_table[b][i / (page_size/P)],
  * slot i % (page_size/P) of r's pool, for every I. Every query token of a row sees the whole
- * context (no mask). Rows with ctx_len[b] <= r give (0, -inf). Padding tokens get out = 0 and lse = -inf and their
- * queries are not read.
+ * context (no mask). Rows with ctx_len[b] <= r give (0, -inf). Padding tokens get out = 0 and lse = -inf (with
+ * CPATTN_FLAG_PAD_LSE_ONLY lse = -inf only, their out rows untouched) and their queries are not read.
  *
  * Rounding. A stripe's keys may be split into pieces that are merged exactly; only the rounding of the result depends
  * on where the splits fall. By default the bf16 head_dim-128 decode path balances the whole call's work over the
@@ -305,6 +308,8 @@ typedef struct cp_own_args {
     int32_t head_dim;         /* 64 or 128 */
     float scale;
     int32_t max_row_tokens;   /* host upper bound of a row's tokens (sizes the launch; longer rows are clamped) */
+    int32_t flags;            /* 0 or CPATTN_FLAG_PAD_LSE_ONLY; other bits are EINVAL */
+    int32_t reserved0;
     const int32_t* cu_seqlens;   /* device int32 [num_rows + 1], non-decreasing; values are clamped to the bucket */
     const void* q;
     int64_t q_stride_token, q_stride_head;
@@ -327,8 +332,10 @@ typedef struct cp_own_args {
  * compare view passes the query offsets as the key offsets.
  *
  * Query i of a row (0-based within the row) sees the row's keys 0..i. Keys and queries of padding tokens are never
- * read; padding tokens get out = 0 and lse = -inf.
- * EINVAL: null pointers, negative sizes, Hq % Hkv != 0. EUNSUPPORTED: head_dim other than 64 or 128.
+ * read; padding tokens get out = 0 and lse = -inf (with CPATTN_FLAG_PAD_LSE_ONLY lse = -inf only, their out rows
+ * untouched).
+ * EINVAL: null pointers, negative sizes, Hq % Hkv != 0, unknown flag bits. EUNSUPPORTED: head_dim other than 64 or
+ * 128.
  */
 int32_t cp_own_token_attn(const cp_own_args* args, hipStream_t stream);
 

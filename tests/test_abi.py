@@ -116,7 +116,7 @@ def _paged(**kw):
     (dict(q=0), _lib.CPATTN_EINVAL),
     (dict(num_rows=-1), _lib.CPATTN_EINVAL),
     (dict(kv_stride_page=-8), _lib.CPATTN_EINVAL),
-    (dict(flags=2), _lib.CPATTN_EINVAL),
+    (dict(flags=4), _lib.CPATTN_EINVAL),
     (dict(flags=-1), _lib.CPATTN_EINVAL),
     (dict(interleave=-1), _lib.CPATTN_EINVAL),
     (dict(interleave=8), _lib.CPATTN_EINVAL),          # I * P = 32 does not divide page_size 16
@@ -183,6 +183,10 @@ def test_own_token_refusals(lib):
     assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EINVAL
     a.num_q_heads = 32
     assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EINVAL       # null pointers
+    a.flags = 4
+    assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_EINVAL       # unknown flag bits
+    assert "flags" in _err(lib)
+    a.flags = 0
     a.bucket_tokens = 0
     assert lib.cp_own_token_attn(C.byref(a), None) == _lib.CPATTN_OK
     assert lib.cp_own_token_attn(None, None) == _lib.CPATTN_EINVAL

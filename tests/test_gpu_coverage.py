@@ -186,3 +186,69 @@ def test_mla_short_peaked_stripes(heads):
             check_lse(res[3][r, t0:t0 + 1], parts[r][1], f"row {b} stripe {r} lse")
         check_out(res[0][t0:t0 + 1], merged[0], f"row {b} merged out")
         check_lse(res[1][t0:t0 + 1], merged[1], f"row {b} merged lse")
+
+
+# ---------------------------------------------------------------------- padding tokens: lse-only flag
+PAD_FLAG = [
+    ("llama8b", dict(batch=4, ctx_lengths=[3, 17, 300, 2100], pad_rows=2, bucket=4 + 7), {}, False),
+    ("llama8b", dict(batch=4, ctx_lengths=[3, 17, 300, 2100], pad_rows=2, bucket=4 + 7), {}, True),
+    ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000], pad_rows=2, bucket=3 + 5), {}, False),
+    ("tiny", dict(pad_rows=2, bucket=4 + 3), {}, False),
+    ("mixed", dict(batch=5, new_lengths=[1, 3, 40, 1, 130], ctx_lengths=[0, 19, 300, 1000, 2], pad_rows=2), {}, False),
+    ("mixed", dict(batch=5, new_lengths=[1, 3, 40, 1, 130], ctx_lengths=[0, 19, 300, 1000, 2], pad_rows=2),
+     dict(dtype="f32"), False),
+]
+
+
+@pytest.mark.parametrize("name,kw,over,fixed", PAD_FLAG,
+                         ids=["decode", "decode-fixed", "mla", "generic", "extend-own", "generic-own-f32"])
+def test_pad_lse_only_flag(name, kw, over, fixed):
+    """CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get lse = -inf and their out rows are left untouched, in every kernel's
+    padding role (partial and own-token calls); real tokens' results are the same bits as without the flag."""
+    from cp_slot_map_amd import _lib
+    wl = dataclasses.replace(workloads.make(name, **kw), **over)
+    say(f"pad lse only {name} {over} fixed={fixed}")
+    batch = pool.build_batch(wl, DEV)
+    t = wl.num_tokens
+    T, Hq = wl.bucket, wl.num_q_heads
+    common = dict(page_size=wl.page_size, partners=wl.partners, scale=wl.scale, kind=wl.kind,
+                  max_ctx_len=batch.max_ctx_len, max_row_tokens=batch.max_row_tokens, fixed_splits=fixed,
+                  interleave=wl.interleave)
+    ref_o, ref_l = api.paged_attn_partial(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
+                                          batch.block_table, **common)
+    o = torch.full_like(ref_o, 7.0)
+    l = torch.full_like(ref_l, 7.0)
+    a = api._paged_args(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len, batch.block_table,
+                        page_size=wl.page_size, partners=wl.partners, scale=wl.scale, kind=wl.kind, stripe_begin=0,
+                        stripe_count=wl.partners, max_ctx_len=batch.max_ctx_len, max_row_tokens=batch.max_row_tokens,
+                        out=o, lse=l, num_tokens=T, fixed_splits=fixed, interleave=wl.interleave, pad_lse_only=True)
+    import ctypes as C
+    lib = _lib.load()
+    n = C.c_int64(0)
+    _lib.check(lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)))
+    ws = torch.zeros(max(1, n.value), dtype=torch.uint8, device=DEV)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _lib.check(lib.cp_paged_attn_partial(C.byref(a), C.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :t], ref_o[:, :t]) and torch.equal(l[:, :t], ref_l[:, :t])
+    assert torch.all(torch.isneginf(l[:, t:])) and torch.all(o[:, t:] == 7.0)
+    if wl.own_token:
+        ro, rl = api.own_token_attn(batch.q, batch.k_new, batch.v_new, batch.cu_seqlens, scale=wl.scale,
+                                    num_rows=wl.batch, max_row_tokens=batch.max_row_tokens)
+        oo = torch.full_like(ro, 7.0)
+        ol = torch.full_like(rl, 7.0)
+        b = api.OwnArgs()
+        b.dtype = api._dtype_code(batch.q.dtype)
+        b.num_rows, b.bucket_tokens, b.num_q_heads = wl.batch, T, Hq
+        b.num_kv_heads, b.head_dim = batch.k_new.shape[1], batch.k_new.shape[2]
+        b.scale, b.max_row_tokens, b.flags = float(wl.scale), batch.max_row_tokens, _lib.CPATTN_FLAG_PAD_LSE_ONLY
+        b.cu_seqlens, b.q = batch.cu_seqlens.data_ptr(), batch.q.data_ptr()
+        b.q_stride_token, b.q_stride_head = batch.q.stride(0), batch.q.stride(1)
+        b.k, b.v = batch.k_new.data_ptr(), batch.v_new.data_ptr()
+        b.kv_stride_token, b.kv_stride_head = batch.k_new.stride(0), batch.k_new.stride(1)
+        b.out, b.out_stride_token, b.out_stride_head = oo.data_ptr(), oo.stride(0), oo.stride(1)
+        b.lse, b.lse_stride_token = ol.data_ptr(), ol.stride(0)
+        _lib.check(lib.cp_own_token_attn(C.byref(b), C.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        torch.cuda.synchronize()
+        assert torch.equal(oo[:t], ro[:t]) and torch.equal(ol[:t], rl[:t])
+        assert torch.all(torch.isneginf(ol[t:])) and torch.all(oo[t:] == 7.0)

@@ -19,6 +19,7 @@ CASES = [
     ("llama8b-fp8", dict(batch=5, ctx_lengths=[1, 9, 255, 1031, 4100], kv_dtype="fp8"), False),
     ("llama8b-fixed", dict(batch=7, ctx_lengths=[1, 3, 4, 17, 255, 1031, 4100]), True),
     ("longctx", dict(batch=4, ctx_lengths=[5, 100, 4097, 9001]), False),
+    ("llama8b-p16", dict(batch=3, ctx_lengths=[5, 300, 2000], partners=16), False),   # more than 8 stripes: two calls
     ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000]), False),
     ("tiny", dict(), False),
 ]

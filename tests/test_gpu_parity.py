@@ -403,19 +403,29 @@ def test_step_plan_matches_run_step(name, kw):
     wl = workloads.make(name, **kw)
     batch = pool.build_batch(wl, DEV)
     mo, ml, po, pl, own = pool.run_step(batch)
-    plan = pool.StepPlan(batch)
-    for rep in range(3):        # repeated steps into poisoned buffers: every output is rewritten every time
-        plan.out.fill_(7.0)
-        plan.merged.fill_(7.0)
-        if own is not None:
-            plan.own_out.fill_(float("nan"))
-            plan.own_lse.fill_(7.0)
-        pm, pml = plan.run()
-        torch.cuda.synchronize()
-        assert torch.equal(plan.out, po) and torch.equal(plan.lse, pl)
-        assert torch.equal(pm, mo) and torch.equal(pml, ml)
-        if own is not None:
-            assert torch.equal(plan.own_out, own[0]) and torch.equal(plan.own_lse, own[1])
+    t = wl.num_tokens
+    for pad_lse_only in (False, True):
+        plan = pool.StepPlan(batch, pad_lse_only=pad_lse_only)
+        for rep in range(3):    # repeated steps into poisoned buffers: every output is rewritten every time
+            plan.out.fill_(7.0)
+            plan.lse.fill_(7.0)
+            plan.merged.fill_(7.0)
+            if own is not None:
+                plan.own_out.fill_(float("nan"))
+                plan.own_lse.fill_(7.0)
+            pm, pml = plan.run()
+            torch.cuda.synchronize()
+            assert torch.equal(pm, mo) and torch.equal(pml, ml)
+            assert torch.equal(plan.lse, pl)
+            if pad_lse_only:    # padding tokens' partial rows are not written (they keep the poison)
+                assert torch.equal(plan.out[:, :t], po[:, :t]) and torch.all(plan.out[:, t:] == 7.0)
+            else:
+                assert torch.equal(plan.out, po)
+            if own is not None:
+                assert torch.equal(plan.own_lse, own[1])
+                assert torch.equal(plan.own_out[:t], own[0][:t])
+                if not pad_lse_only:
+                    assert torch.equal(plan.own_out, own[0])
 
 
 def test_empty_batch_and_empty_context():
@@ -486,7 +496,7 @@ def test_full_size_bench_configuration(name, nsample):
     res = (plan.merged, plan.merged_lse, plan.out, plan.lse, own)
     part_rows = _sample_rows(wl, nsample, 11)
     w = compare_rows(wl, batch, res, range(wl.batch), DEV, check_partials=part_rows)
-    check_padding(wl, res)
+    check_padding(wl, res, partial_rows_written=False)
     say(f"  partial rows {part_rows} worst {w}")
     del plan, batch, res
     torch.cuda.empty_cache()
