@@ -164,6 +164,24 @@ __device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pag
     }
 }
 
+// Widen the V rows this wave loaded into a tile (tokens [kTokPerWave w, +kTokPerWave), 256 bytes each, pieces stored
+// swizzled) from bf16 to fp16 in place: the value product then reads fp16 operands straight from LDS, and each V
+// element is converted once per workgroup instead of once per wave that reads it. Elementwise, so the swizzle of the
+// pieces is unchanged.
+__device__ __forceinline__ void widen_v_to_f16(lds_char_ptr tile, int32_t w, int lane) {
+    constexpr int kBytes = kTokPerWave * kRowBytes;            // this wave's V rows
+    static_assert(kBytes % (64 * 16) == 0, "whole 16-byte pieces per lane");
+#pragma unroll
+    for (int i = 0; i < kBytes / (64 * 16); ++i) {
+        __attribute__((address_space(3))) u32x4_t* ptr =
+            (__attribute__((address_space(3))) u32x4_t*)(tile + kVOff + kTokPerWave * w * kRowBytes + 16 * (64 * i + lane));
+        *ptr = __builtin_bit_cast(u32x4_t, bf16x8_to_f16(*ptr));
+    }
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed (the other counters at their maximum).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Maximum of three floats in one instruction. fmaxf would first quiet each operand (IEEE mode), one extra instruction
 // per operand; scores and their maxima are never signalling NaNs, so that step is not needed here.
 __device__ __forceinline__ float max3(float a, float b, float c) {
@@ -348,6 +366,10 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
                          opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
         issue_tile<MODE>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
                          opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
+        wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile 0 are in LDS
+        asm volatile("" ::: "memory");                      // (the LDS reads below stay after the wait)
+        widen_v_to_f16(opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
+        wait_lgkm0();
     };
     static_assert(kAhead == 3 && kBufs == 4, "ring");
 
@@ -409,9 +431,15 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
             l[rb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 #pragma unroll
             for (int d = 0; d < 4; ++d) ph[rb][d] = pack2_f16(pv[2 * d], pv[2 * d + 1]);
-            const f16x8_t pr = __builtin_bit_cast(f16x8_t, ph[rb]);
-            lr[rb] += ((float(pr[0]) + float(pr[1])) + (float(pr[2]) + float(pr[3]))) +
-                      ((float(pr[4]) + float(pr[5])) + (float(pr[6]) + float(pr[7])));
+            typedef __fp16 h2_t __attribute__((ext_vector_type(2)));
+            const h2_t one2 = __builtin_bit_cast(h2_t, 0x3c003c00u);       // (1.0, 1.0)
+            float lsum = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t pd = ph[rb][d];
+                lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, pd), one2, lsum, false);
+            }
+            lr[rb] += lsum;
         }
 
         // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads, widened from bf16
@@ -420,8 +448,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         for (int db = 0; db < 8; ++db) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[1][db]));
-            const f16x8_t bop = bf16x8_to_f16(
-                __builtin_bit_cast(u32x4_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
+            const f16x8_t bop =
+                __builtin_bit_cast(f16x8_t, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
                 o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ph[rb]), bop, o[rb][db],
@@ -436,10 +464,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
     auto step = [&](auto bc, auto live, auto maxonly, int32_t kt) __attribute__((always_inline)) {
         constexpr int bb = decltype(bc)::value;
-        wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile kt are in LDS
-        lds_barrier();                                      // ... and every wave's; tile kt - 1's buffer is free
+        // This wave's pieces of tiles kt and kt + 1 are in LDS (tile kt's V already widened by every wave before the
+        // barrier below; tile kt + 1's V is widened now, before the next step's barrier).
+        wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
+        wait_lgkm0();
+        lds_barrier();                                      // every wave's too; tile kt - 1's buffer is free
         issue_tile<MODE>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
                          tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
+        widen_v_to_f16(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
         if constexpr (decltype(live)::value) {
             if constexpr (decltype(maxonly)::value) {
                 float sv[2][8];
@@ -505,7 +537,6 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     // outcome is the same softmax with a different reference.
     reset();
     prologue();
-    wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
     lds_barrier();
     if (wave_live) {
         float sv[2][8];
