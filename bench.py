@@ -280,7 +280,7 @@ def summarize(wl, m, traffic=None):
         wl.head_dim + wl.head_dim_v)
     kernel = KERNEL_NAMES.get(wl.name, "cp_paged_attn_partial")
     if wl.kind == "mla" and wl.kv_dtype == "fp8":
-        kernel = "cp_paged_attn_partial (paged_generic_kernel over the fp8 latent pool)"
+        kernel = "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel over the fp8 latent pool)"
     # The roofline that bounds the partial: HBM below the ridge point (peak flops / peak bytes), MFMA above it.
     mfma_bound = flops / kv_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) if kv_bytes else False
     tf = flops / (part_avg * 1e-3) / 1e12

@@ -66,6 +66,7 @@ constexpr int kMaxChunkPages = 512;            // page ids of one chunk staged i
 constexpr int kKSteps = kD / 32;               // k-steps of the score product
 constexpr int kMaxPlanUnits = 1024;            // units sorted by the plan kernel (block order above)
 constexpr int kTargetUnits = 512;              // about two units per compute unit before chunks are split
+constexpr int kFp8Off = kRowV - kD;            // fp8 tiles: a token's 576 codes land in [kFp8Off, kRowV) of its row
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -76,7 +77,7 @@ typedef const __attribute__((address_space(3))) int32_t* lds_i32_ptr;
 struct MlaParams {
     const uint16_t* q;
     int64_t q_st, q_sh;
-    const uint16_t* kv;
+    const char* kv;         // latent pool (bytes): bf16 rows, or fp8 E4M3 codes
     PoolGeom geo;
     const int32_t* q_row_start;
     const int32_t* ctx_len;
@@ -96,7 +97,8 @@ struct MlaParams {
     int32_t n_chunks, chunk_tokens, n_units, pad_blocks, pad_tokens_per_block;
     int32_t head_groups, work_blocks;   // workgroups per unit (1 or 2) and blocks before the padding role
     int32_t pad_lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get their lse only
-    float scale_log2;
+    float scale_log2;       // softmax scale (times the latent descale for fp8 pools) in log2 units
+    float v_scale;          // latent descale of fp8 pools (applied to the output), else 1
 };
 
 __device__ __forceinline__ int swz(int t) { return (t ^ (t >> 2)) & 7; }   // rope-region piece swizzle
@@ -168,13 +170,14 @@ __device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
 
 // Byte address of tile token L % 32's latent row in lane L, from the chunk's page ids staged in LDS (tokens past the
 // chunk end take its last token, whose values are masked out; invalid page ids read page 0).
+template <bool KV8>
 __device__ __forceinline__ uint64_t token_rows(const MlaParams& p, lds_i32_ptr s_pages, int32_t pidx0, int32_t tile0,
                                                int32_t j_last, const char* kv_r, int lane) {
     const int32_t j = min(tile0 + (lane & 31), j_last);
     int32_t page = s_pages[(j >> p.geo.pp_shift) - pidx0];
     page = (page >= 0 && page < p.geo.num_pages) ? page : 0;
     const int64_t row = int64_t(page) * p.geo.s_page + int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot;   // elements
-    return reinterpret_cast<uint64_t>(kv_r) + uint64_t(row) * 2u;
+    return reinterpret_cast<uint64_t>(kv_r) + (uint64_t(row) << (KV8 ? 0 : 1));
 }
 
 // Cache policy of the latent loads: nontemporal (CPATTN_MLA_NONTEMPORAL, default on), as every latent row is read
@@ -191,10 +194,26 @@ constexpr int kLatentCpol = CPATTN_MLA_NONTEMPORAL ? 2 : 0;     // 2: the nt bit
 //   * rope dims [512, 576): 4-byte loads, 32 lanes per token, two tokens per instruction (16 per tile, shared evenly
 //     by the waves, so every wave issues the same loads and no lane is masked); lane l fills dword l % 32 of its
 //     token's rope row, i.e. stored piece (l % 32) / 4, with the matching dword of logical piece ((l % 32) / 4) ^ g(t).
-template <int NW>
+template <int NW, bool KV8>
 __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int32_t w, int lane) {
     constexpr int kTpw = kTile / NW;
     const uint32_t alo = uint32_t(rows), ahi = uint32_t(rows >> 32);
+    if constexpr (KV8) {
+        // fp8 latent rows (576 one-byte codes): one instruction per token, lanes 0..35 loading 16 bytes each into
+        // the upper part [kFp8Off, kRowV) of the token's LDS row; widen_tile_fp8 turns them into the bf16 layout.
+#pragma unroll
+        for (int i = 0; i < kTpw; ++i) {
+            const int32_t t = kTpw * w + i;                                      // wave-uniform
+            const uint64_t base = (uint64_t(uint32_t(__builtin_amdgcn_readlane(ahi, t))) << 32) |
+                                  uint32_t(__builtin_amdgcn_readlane(alo, t));
+            if (lane < kD / 16) {
+                const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * lane);
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t + kFp8Off), 16, 0,
+                                                 kLatentCpol);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kTpw; ++i) {
         const int32_t t = kTpw * w + i;                                          // wave-uniform
@@ -216,9 +235,44 @@ __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int
 }
 
 // Direct-to-LDS loads a wave issues per tile (the same for every wave).
-template <int NW>
+template <int NW, bool KV8>
 __device__ __forceinline__ constexpr int tile_loads() {
-    return kTile / NW + (kTile / 2) / NW;
+    return KV8 ? kTile / NW : kTile / NW + (kTile / 2) / NW;
+}
+
+// fp8 tiles: widen the rows this wave loaded (tokens [32 w / NW, +32 / NW)) from the E4M3 codes at [kFp8Off, kRowV)
+// of each row to the bf16 layout the products read: value dims [0, 512) at the start of the row, rope dims in the
+// swizzled rope row. Sixteen lanes a token, each taking 32 value codes and 4 rope codes; every read of a pass is done
+// before its writes (they depend on the read data), so the in-place overlap of source and destination is safe. The
+// conversion is exact (E4M3 values are bf16 values); the descale is applied in fp32 elsewhere.
+template <int NW>
+__device__ __forceinline__ void widen_tile_fp8(lds_char_ptr tile, int32_t w, int lane) {
+    constexpr int kTpw = kTile / NW;
+    const int32_t j = lane & 15;
+#pragma unroll
+    for (int pass = 0; pass < kTpw / 4; ++pass) {
+        const int32_t t = kTpw * w + 4 * pass + (lane >> 4);
+        const lds_char_ptr row = tile + kRowV * t;
+        const u32x4_t c0 = *(const __attribute__((address_space(3))) u32x4_t*)(row + kFp8Off + 32 * j);
+        const u32x4_t c1 = *(const __attribute__((address_space(3))) u32x4_t*)(row + kFp8Off + 32 * j + 16);
+        const uint32_t cr = *(const __attribute__((address_space(3))) uint32_t*)(row + kFp8Off + kDv + 4 * j);
+        auto wide = [](uint32_t c) __attribute__((always_inline)) {
+            return (u32x2_t){__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true))};
+        };
+        u32x4_t out[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2_t a = wide(q < 2 ? c0[2 * q] : c1[2 * (q - 2)]);
+            const u32x2_t b = wide(q < 2 ? c0[2 * q + 1] : c1[2 * (q - 2) + 1]);
+            out[q] = (u32x4_t){a[0], a[1], b[0], b[1]};
+        }
+        const u32x2_t rr = wide(cr);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(__attribute__((address_space(3))) u32x4_t*)(row + 64 * j + 16 * q) = out[q];
+        *(__attribute__((address_space(3))) u32x2_t*)(tile + kRegionV + kRowR * t + 16 * ((j >> 1) ^ swz(t)) +
+                                                      8 * (j & 1)) = rr;
+    }
 }
 
 // s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
@@ -233,9 +287,10 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 // Wait until at most the loads of kAhead - 1 tiles are outstanding (the counter saturates at 63: with one or two
 // waves a little more than the oldest tile is waited for).
-template <int NW>
+// fp8 tiles: also the next tile (it is widened during this step), so at most kAhead - 2 tiles stay outstanding.
+template <int NW, bool KV8>
 __device__ __forceinline__ void wait_tile() {
-    constexpr int kN = (kAhead - 1) * tile_loads<NW>();
+    constexpr int kN = (kAhead - (KV8 ? 2 : 1)) * tile_loads<NW, KV8>();
     wait_vmcnt<(kN < 63 ? kN : 63)>();
 }
 
@@ -313,7 +368,7 @@ __global__ __launch_bounds__(256) void mla_plan_kernel(const MlaParams p) {
 }
 
 // One workgroup per (unit, group of 16 NW heads); wave w of group hg owns heads hg 16 NW + 16 w + [0, 16).
-template <int NW, bool REDO>
+template <int NW, bool REDO, bool KV8>
 __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams p) {
     // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
     // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
@@ -366,7 +421,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     }
 
     const int32_t r = p.stripe_begin + x.s;
-    const char* kv_r = reinterpret_cast<const char*>(p.kv + int64_t(r) * p.geo.s_stripe);
+    const char* kv_r = p.kv + (int64_t(r) * p.geo.s_stripe << (KV8 ? 0 : 1));
     const int32_t* bt_row = p.bt + int64_t(x.b) * p.bt_stride;
     const int32_t j_last = x.j1 - 1;
     const int32_t ntiles = (x.j1 - x.j0 + kTile - 1) / kTile;
@@ -442,13 +497,19 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             return t;
         };
         const lds_i32_ptr pages = (lds_i32_ptr)s_pages;
-        issue_tile<NW>(token_rows(p, pages, pidx0, x.j0, j_last, kv_r, lane),
-                       opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
-        issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + kTile, last_tile0), j_last, kv_r, lane),
-                       opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
-        issue_tile<NW>(token_rows(p, pages, pidx0, min(x.j0 + 2 * kTile, last_tile0), j_last, kv_r, lane),
-                       opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
+        issue_tile<NW, KV8>(token_rows<KV8>(p, pages, pidx0, x.j0, j_last, kv_r, lane),
+                            opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
+        issue_tile<NW, KV8>(token_rows<KV8>(p, pages, pidx0, min(x.j0 + kTile, last_tile0), j_last, kv_r, lane),
+                            opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
+        issue_tile<NW, KV8>(token_rows<KV8>(p, pages, pidx0, min(x.j0 + 2 * kTile, last_tile0), j_last, kv_r, lane),
+                            opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
         static_assert(kAhead == 3 && kBufs == 4, "ring");
+        if constexpr (KV8) {                        // tile 0 is widened before the first step's barrier
+            constexpr int kN0 = (kAhead - 1) * tile_loads<NW, KV8>();
+            wait_vmcnt<(kN0 < 63 ? kN0 : 63)>();
+            asm volatile("" ::: "memory");          // (the LDS reads of the widening stay after the wait)
+            widen_tile_fp8<NW>(opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
+        }
 
         // Compute tile kt from `tile`.
         auto tile_compute = [&](lds_char_ptr tile, int32_t kt) __attribute__((always_inline)) {
@@ -552,12 +613,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
         auto step = [&](auto bc, int32_t kt) __attribute__((always_inline)) {
             constexpr int b = decltype(bc)::value;
             // This wave's pieces of tile kt are in LDS: the loads of the kAhead - 1 newer tiles may stay in flight.
-            wait_tile<NW>();
+            wait_tile<NW, KV8>();
             wait_lgkm0();                           // this wave's reads of tile kt - 1 and of the probabilities are done
             lds_barrier();                          // ... and every wave's: tile kt - 1's buffer is free
             const int32_t tn0 = min(x.j0 + (kt + kAhead) * kTile, last_tile0);
-            issue_tile<NW>(token_rows(p, pages, pidx0, tn0, j_last, kv_r, lane),
-                           tile_buf(std::integral_constant<int, b + kAhead>{}), w, lane);
+            issue_tile<NW, KV8>(token_rows<KV8>(p, pages, pidx0, tn0, j_last, kv_r, lane),
+                                tile_buf(std::integral_constant<int, b + kAhead>{}), w, lane);
+            // fp8: widen this wave's rows of tile kt + 1 (loaded); the next step's barrier publishes them
+            if constexpr (KV8) widen_tile_fp8<NW>(tile_buf(std::integral_constant<int, b + 1>{}), w, lane);
             tile_compute(tile_buf(std::integral_constant<int, b>{}), kt);
         };
         for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
@@ -605,7 +668,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float li = s_rowsum[16 * hg + 4 * c4 + i];
-            const float inv = split ? 1.0f : (li > 0.f ? 1.0f / li : 0.f);
+            const float inv = (split ? 1.0f : (li > 0.f ? 1.0f / li : 0.f)) * p.v_scale;
             float* dst = base + (16 * hg + i) * hs;
 #pragma unroll
             for (int b = 0; b < kDB; ++b) dst[16 * b] = o[kDB * hg + b][i] * inv;
@@ -694,12 +757,13 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 bool mla_decode_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_MLA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kDv) return false;
-    if (a.kv_format != CPATTN_KV_SAME) return false;   // fp8 latent pools: the generic kernel
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
     if (a.num_q_heads != 16 && a.num_q_heads != 32 && a.num_q_heads != 64 && a.num_q_heads != 128) return false;
     if (geo.pp_shift < 0) return false;
     auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
     if (!al16(a.q) || !al16(a.k_pool) || !al16(a.out)) return false;
-    if ((a.q_stride_token | a.q_stride_head | a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot) & 7) return false;
+    if ((a.q_stride_token | a.q_stride_head) & 7) return false;
+    if ((a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot) & (kv8 ? 15 : 7)) return false;   // 16-byte rows
     if ((a.out_stride_stripe | a.out_stride_token | a.out_stride_head) & 3) return false;
     const MlaShape d = mla_shape(a);
     if (d.work_blocks + (a.num_tokens + 3) / 4 > (int64_t(1) << 31) - 1) return false;
@@ -726,13 +790,31 @@ int64_t mla_decode_workspace_bytes(const cp_paged_args& a) {
     return d.n_units > 0 ? mla_workspace(d, a.num_q_heads).total : 0;
 }
 
+// The kernel instance for NW waves, the redo role and the pool element type.
+template <bool REDO>
+void launch_mla_variant(int64_t nw, bool kv8, dim3 grid, hipStream_t stream, const MlaParams& p) {
+    auto go = [&](auto nwc, auto k8) {
+        constexpr int NW = decltype(nwc)::value;
+        constexpr bool K8 = decltype(k8)::value;
+        hipLaunchKernelGGL((mla_decode_kernel<NW, REDO, K8>), grid, dim3(64 * NW), 0, stream, p);
+    };
+    using T8 = std::true_type;
+    using F8 = std::false_type;
+    switch (nw) {
+        case 1: kv8 ? go(std::integral_constant<int, 1>{}, T8{}) : go(std::integral_constant<int, 1>{}, F8{}); break;
+        case 2: kv8 ? go(std::integral_constant<int, 2>{}, T8{}) : go(std::integral_constant<int, 2>{}, F8{}); break;
+        case 4: kv8 ? go(std::integral_constant<int, 4>{}, T8{}) : go(std::integral_constant<int, 4>{}, F8{}); break;
+        default: kv8 ? go(std::integral_constant<int, 8>{}, T8{}) : go(std::integral_constant<int, 8>{}, F8{}); break;
+    }
+}
+
 int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
     const MlaShape d = mla_shape(a);
     MlaParams p{};
     p.q = static_cast<const uint16_t*>(a.q);
     p.q_st = a.q_stride_token;
     p.q_sh = a.q_stride_head;
-    p.kv = static_cast<const uint16_t*>(a.k_pool);
+    p.kv = static_cast<const char*>(a.k_pool);
     p.geo = geo;
     p.q_row_start = a.q_row_start;
     p.ctx_len = a.ctx_len;
@@ -769,7 +851,9 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.pad_blocks = (a.num_tokens + 3) / 4;
     p.head_groups = int32_t(d.head_groups);
     p.work_blocks = int32_t(d.work_blocks);
-    p.scale_log2 = a.scale * kLog2e;
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    p.scale_log2 = a.scale * (kv8 ? a.k_descale : 1.0f) * kLog2e;
+    p.v_scale = kv8 ? a.v_descale : 1.0f;
     p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
 
     if (p.order) {
@@ -779,22 +863,12 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     const int64_t blocks = d.work_blocks + p.pad_blocks;
     if (blocks > 0) {
         const dim3 grid{uint32_t(blocks), 1, 1};
-        switch (d.nw) {
-            case 1: hipLaunchKernelGGL((mla_decode_kernel<1, false>), grid, dim3(64), 0, stream, p); break;
-            case 2: hipLaunchKernelGGL((mla_decode_kernel<2, false>), grid, dim3(128), 0, stream, p); break;
-            case 4: hipLaunchKernelGGL((mla_decode_kernel<4, false>), grid, dim3(256), 0, stream, p); break;
-            default: hipLaunchKernelGGL((mla_decode_kernel<8, false>), grid, dim3(512), 0, stream, p); break;
-        }
+        launch_mla_variant<false>(d.nw, kv8, grid, stream, p);
         if (int32_t st = check_launch("cp_paged_attn_partial (MLA decode)")) return st;
     }
     if (d.work_blocks > 0) {                         // workgroups whose scores outgrew their reference, if any
         const dim3 grid{uint32_t(d.work_blocks), 1, 1};
-        switch (d.nw) {
-            case 1: hipLaunchKernelGGL((mla_decode_kernel<1, true>), grid, dim3(64), 0, stream, p); break;
-            case 2: hipLaunchKernelGGL((mla_decode_kernel<2, true>), grid, dim3(128), 0, stream, p); break;
-            case 4: hipLaunchKernelGGL((mla_decode_kernel<4, true>), grid, dim3(256), 0, stream, p); break;
-            default: hipLaunchKernelGGL((mla_decode_kernel<8, true>), grid, dim3(512), 0, stream, p); break;
-        }
+        launch_mla_variant<true>(d.nw, kv8, grid, stream, p);
         if (int32_t st = check_launch("cp_paged_attn_partial (MLA redo)")) return st;
     }
     if (d.n_chunks > 1 && d.n_items > 0) {

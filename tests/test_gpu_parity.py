@@ -115,6 +115,8 @@ FP8 = [
                    kv_dtype="fp8")),
     ("mla", dict(batch=4, ctx_lengths=[1, 3, 70, 700], kv_dtype="fp8")),
     ("mla", dict(batch=2, ctx_lengths=[65, 1500], kv_dtype="fp8", num_q_heads=16, interleave=2)),
+    ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000], kv_dtype="fp8", num_q_heads=64)),
+    ("mla", dict(batch=3, ctx_lengths=[2, 31, 900], kv_dtype="fp8", num_q_heads=32, interleave=4)),
 ]
 
 
