@@ -176,4 +176,14 @@ __device__ __forceinline__ void fill_padding(float* out, int64_t o_ss, int64_t o
     }
 }
 
+// Tokens [tok0 + max_row_tokens, tok1) of a row whose real token count exceeds the host bound max_row_tokens are not
+// attended (launches are sized by the bound): they are written as padding, (0, -inf) (their lse only with lse_only),
+// in one partial (out and lse already offset to it).
+__device__ __forceinline__ void fill_excess_tokens(float* out, int64_t o_st, int64_t o_sh, float* lse, int64_t l_st,
+                                                   int32_t tok0, int32_t tok1, int32_t max_row_tokens, int32_t Hq,
+                                                   int32_t Dv, int lane, int nlanes, bool lse_only) {
+    const int32_t t_begin = tok0 + max(max_row_tokens, 0);
+    if (t_begin < tok1) fill_padding(out, 0, o_st, o_sh, lse, 0, l_st, 1, Hq, Dv, t_begin, tok1, lane, nlanes, lse_only);
+}
+
 }  // namespace cpattn

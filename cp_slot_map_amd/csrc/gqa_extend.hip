@@ -247,6 +247,9 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     const const_i32_ptr rs = (const_i32_ptr)p.row_start;
     const int32_t tok0 = min(max(rs[b], 0), p.T);
     const int32_t tok1 = min(max(rs[b + 1], tok0), p.T);
+    if (g == 0 && qb == p.n_qblocks - 1)
+        fill_excess_tokens(p.out + int64_t(s) * p.o_ss, p.o_st, p.o_sh, p.lse + int64_t(s) * p.l_ss, p.l_st, tok0, tok1,
+                           p.max_row_tokens, p.Hq, kD, threadIdx.x, blockDim.x, p.pad_lse_only);
     const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
     const int32_t nrows = ntok * p.G;
     const int32_t row0 = qb * kBlockRows;

@@ -93,6 +93,7 @@ struct MlaParams {
     float* ws_max;          // per (unit, query head): exact score maximum (log2 units) of a unit to redo
     int64_t rec_floats;
     int32_t B, T, P, stripe_begin, S, Hq, max_pages, page_size, max_row_tokens;
+    int32_t unit_tokens;   // query tokens per (row, stripe) in the unit space: max(1, max_row_tokens)
     int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_chunks, chunk_tokens, n_units, pad_blocks, pad_tokens_per_block;
     int32_t head_groups, work_blocks;   // workgroups per unit (1 or 2) and blocks before the padding role
@@ -127,6 +128,7 @@ struct Unit {
     int32_t t;           // query token (bucket index)
     int32_t Lr;          // stripe length
     int32_t j0, j1;      // chunk range of local tokens
+    int32_t tok0, tok1;  // the row's tokens in the bucket
     bool live;           // the row has this query token
 };
 
@@ -136,8 +138,8 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     Unit x;
     x.c = u % p.n_chunks;
     int32_t v = u / p.n_chunks;
-    x.qtok = v % p.max_row_tokens;
-    v /= p.max_row_tokens;
+    x.qtok = v % p.unit_tokens;
+    v /= p.unit_tokens;
     x.s = v % p.S;
     x.b = v / p.S;
     const int32_t tok0 = min(max(qrs[x.b], 0), p.T);
@@ -145,6 +147,8 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
     x.live = x.qtok < ntok;
     x.t = tok0 + x.qtok;
+    x.tok0 = tok0;
+    x.tok1 = tok1;
     const int32_t L = min(max(cl[x.b], 0), p.ctx_cap);
     x.Lr = stripe_length(L, p.stripe_begin + x.s, p.P, p.geo.interleave);
     x.j0 = x.c * p.chunk_tokens;
@@ -156,8 +160,8 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
 __device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
     const int32_t c = u % p.n_chunks;
     int32_t v = u / p.n_chunks;
-    const int32_t qtok = v % p.max_row_tokens;
-    v /= p.max_row_tokens;
+    const int32_t qtok = v % p.unit_tokens;
+    v /= p.unit_tokens;
     const int32_t s = v % p.S;
     const int32_t b = v / p.S;
     const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
@@ -405,6 +409,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     if (REDO && !p.ws_redo[rank]) return;
     const int32_t u = p.order ? __builtin_amdgcn_readfirstlane(((const_i32_ptr)p.order)[rank]) : rank;
     const Unit x = decode_unit(p, u);
+    if (!REDO && x.c == 0 && x.qtok == p.unit_tokens - 1)
+        fill_excess_tokens(p.out + int64_t(x.s) * p.o_ss, p.o_st, p.o_sh, p.lse + int64_t(x.s) * p.l_ss, p.l_st, x.tok0,
+                           x.tok1, p.max_row_tokens, p.Hq, kDv, threadIdx.x, blockDim.x, p.pad_lse_only);
     if (!x.live) return;
     const int32_t n16 = lane & 15, c4 = lane >> 4;
     const int32_t hw = hg * 16 * NW + 16 * w;               // first query head of this wave
@@ -843,7 +850,8 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.max_pages = a.max_pages;
     p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
-    p.max_row_tokens = std::max(1, a.max_row_tokens);
+    p.max_row_tokens = a.max_row_tokens;
+    p.unit_tokens = std::max(1, a.max_row_tokens);
     p.n_chunks = int32_t(d.n_chunks);
     p.chunk_tokens = int32_t(d.chunk_tokens);
     p.n_units = int32_t(d.n_units);

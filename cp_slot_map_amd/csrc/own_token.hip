@@ -25,6 +25,7 @@ struct OwnParams {
     const int32_t* cu;
     int32_t B, T, Hq, Hkv, G, max_row_tokens;
     float scale_log2;
+    int32_t lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY
 };
 
 template <typename T, int ND, int R>
@@ -35,6 +36,9 @@ __global__ __launch_bounds__(64) void own_token_generic_kernel(const OwnParams p
     const int g = blockIdx.y % p.Hkv;
     const int32_t tok0 = min(max(p.cu[b], 0), p.T);
     const int32_t tok1 = min(max(p.cu[b + 1], tok0), p.T);
+    if (g == 0 && rb == int(gridDim.x) - 1)
+        fill_excess_tokens(p.out, p.o_st, p.o_sh, p.lse, p.l_st, tok0, tok1, p.max_row_tokens, p.Hq, ND * 64, lane, 64,
+                           p.lse_only);
     const int32_t n = min(tok1 - tok0, p.max_row_tokens);
     const int32_t nrows = n * p.G;
     if (rb * R >= nrows) return;
@@ -124,13 +128,15 @@ int32_t launch_own_token_generic(const cp_own_args& a, hipStream_t stream) {
     p.G = a.num_q_heads / a.num_kv_heads;
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;
+    p.lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
     if (int32_t st = launch_pad(a.out, 0, a.out_stride_token, a.out_stride_head, a.lse, 0, a.lse_stride_token,
                                 a.cu_seqlens, a.num_rows, a.bucket_tokens, 1, a.num_q_heads, a.head_dim,
                                 (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) != 0, stream))
         return st;
-    if (a.num_rows == 0 || a.max_row_tokens == 0) return CPATTN_OK;
+    if (a.num_rows == 0) return CPATTN_OK;
     constexpr int R = 8;
-    const int64_t rows = int64_t(a.max_row_tokens) * p.G;
+    // (at least one block of query rows: it also writes tokens past an understated max_row_tokens as padding)
+    const int64_t rows = int64_t(std::max(1, a.max_row_tokens)) * p.G;
     const dim3 grid(uint32_t((rows + R - 1) / R), uint32_t(a.num_rows * a.num_kv_heads));
     const bool f32 = a.dtype == CPATTN_F32;
     if (a.head_dim == 64) {

@@ -346,6 +346,9 @@ __global__ __launch_bounds__(64) void gqa_decode_bf16_kernel(const DecodeParams 
 
     const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
     const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    if (g == 0 && c == 0 && qt == p.n_qtiles - 1)
+        fill_excess_tokens(p.out + s * p.o_ss, p.o_st, p.o_sh, p.lse + s * p.l_ss, p.l_st, tok0, tok1, p.max_row_tokens,
+                           p.Hq, 128, lane, 64, p.pad_lse_only);
     const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
     const int32_t nrows = ntok * p.G;
     const int32_t row0 = qt * 16;
@@ -1075,6 +1078,9 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
     const int32_t T = idx / p.Hkv;
     const int32_t g = idx % p.Hkv;
     const Tile tl = load_tile(p, T);
+    if (g == 0 && tl.qt == p.n_qtiles - 1)
+        fill_excess_tokens(p.out + tl.s * p.o_ss, p.o_st, p.o_sh, p.lse + tl.s * p.l_ss, p.l_st, tl.tok0,
+                           min(max(tl.q1, tl.tok0), p.T), p.max_row_tokens, p.Hq, 128, lane, 64, p.pad_lse_only);
     const int32_t row0 = tl.qt * 16;
     if (row0 >= tl.nrows) return;
     const int32_t tile_rows = min(16, tl.nrows - row0);
@@ -1162,6 +1168,17 @@ __global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParam
     const int32_t q0 = qrs[b], q1 = qrs[b + 1], cl = clp[b], rowpref = rp[b], N = rp[p.B];
     const int32_t tok0 = min(max(q0, 0), p.T);
     const int32_t tok1 = min(max(q1, tok0), p.T);
+    if (g == 0 && qt == p.n_qtiles - 1 && tok0 + p.max_row_tokens < tok1) {   // tokens past the host bound: padding
+        for (int32_t s = 0; s < p.S; ++s)
+            fill_excess_tokens(p.out + s * p.o_ss, p.o_st, p.o_sh, p.lse + s * p.l_ss, p.l_st, tok0, tok1,
+                               p.max_row_tokens, p.Hq, 128, lane, 64, p.pad_lse_only);
+        const f32x4_t zero[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int32_t t = tok0 + p.max_row_tokens; t < tok1; ++t) {
+            for (int32_t h = rsub; h < p.Hq; h += 4) merged_row(t, h, zero);
+            if (p.m_lse)
+                for (int32_t h = lane; h < p.Hq; h += 64) p.m_lse[int64_t(t) * p.m_lst + h] = neg_inf();
+        }
+    }
     const int32_t nrows = min(tok1 - tok0, p.max_row_tokens) * p.G;
     const int32_t row0 = qt * 16;
     if (row0 >= nrows) return;

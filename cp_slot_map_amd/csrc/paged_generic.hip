@@ -30,6 +30,7 @@ struct GenericParams {
     int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     float scale_log2;   // softmax scale (times the key descale for fp8 pools) in log2 units
     float v_scale;      // value descale of fp8 pools, else 1
+    int32_t lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY
 };
 
 // T: element type of q; TKV: element type of the pools (T itself, or uint8_t for fp8 codes).
@@ -43,6 +44,9 @@ __global__ __launch_bounds__(64) void paged_generic_kernel(const GenericParams p
 
     int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
     int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
+    if (g == 0 && rb == int(gridDim.x) - 1)
+        fill_excess_tokens(p.out + s * p.o_ss, p.o_st, p.o_sh, p.lse + s * p.l_ss, p.l_st, tok0, tok1, p.max_row_tokens,
+                           p.Hq, NV * 64, lane, 64, p.lse_only);
     const int32_t ntok = min(tok1 - tok0, p.max_row_tokens);
     const int32_t nrows = ntok * p.G;
     if (rb * R >= nrows) return;
@@ -187,10 +191,12 @@ int32_t launch_paged_generic(const cp_paged_args& a, const PoolGeom& geo, hipStr
     const bool fp8 = a.kv_format == CPATTN_KV_FP8_E4M3;
     p.scale_log2 = a.scale * (fp8 ? a.k_descale : 1.0f) * kLog2e;
     p.v_scale = fp8 ? a.v_descale : 1.0f;
+    p.lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
 
     if (int32_t st = launch_pad_partials(a, stream)) return st;
-    if (a.num_rows == 0 || a.max_row_tokens == 0) return CPATTN_OK;
-    const int64_t rows = int64_t(a.max_row_tokens) * p.G;
+    if (a.num_rows == 0) return CPATTN_OK;
+    // (at least one block of query rows: it also writes tokens past an understated max_row_tokens as padding)
+    const int64_t rows = int64_t(std::max(1, a.max_row_tokens)) * p.G;
     const bool f32 = a.dtype == CPATTN_F32;
     if (a.kind == CPATTN_MLA) {
         constexpr int R = 8;

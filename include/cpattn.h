@@ -167,7 +167,8 @@ typedef struct cp_paged_args {
     float scale;              /* softmax scale applied to q.k */
     int32_t max_ctx_len;      /* host upper bound of ctx_len[b]; sizes the launch and the workspace. A row whose device
                                  ctx_len exceeds it is taken as its first max_ctx_len tokens (every kernel clamps) */
-    int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; larger rows are clamped */
+    int32_t max_row_tokens;   /* host upper bound of a row's query tokens, sizes the launch; a row's tokens past it are
+                                 not attended and come out as padding (0, -inf) */
     int32_t max_pages;        /* block-table entries used per row; ctx_len[b] is clamped to max_pages * page_size */
     int32_t flags;            /* CPATTN_FLAG_FIXED_SPLITS | CPATTN_FLAG_PAD_LSE_ONLY; other bits are EINVAL */
     int32_t interleave;       /* KV-cache interleave size I (0 or 1: none); the placement of cp_slot_map; I * P must
@@ -307,7 +308,8 @@ typedef struct cp_own_args {
     int32_t num_kv_heads;
     int32_t head_dim;         /* 64 or 128 */
     float scale;
-    int32_t max_row_tokens;   /* host upper bound of a row's tokens (sizes the launch; longer rows are clamped) */
+    int32_t max_row_tokens;   /* host upper bound of a row's tokens (sizes the launch); a row's tokens past it are not
+                                 attended and come out as padding (0, -inf) */
     int32_t flags;            /* 0 or CPATTN_FLAG_PAD_LSE_ONLY; other bits are EINVAL */
     int32_t reserved0;
     const int32_t* cu_seqlens;   /* device int32 [num_rows + 1], non-decreasing; values are clamped to the bucket */

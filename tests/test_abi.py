@@ -138,12 +138,13 @@ def test_paged_refusals(lib, bad, code):
 
 
 def test_mla_over_fp8_passes_host_checks(lib):
-    """MLA over an fp8 latent pool with one descale is accepted (the generic kernel reads it)."""
+    """MLA over an fp8 latent pool with one descale is accepted; the MFMA MLA kernel reads it, with a workspace for its
+    split records."""
     a = _paged(kv_format=1, kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, head_dim_v=512, k_descale=0.5,
                v_descale=0.5)
     n = C.c_int64(-1)
     assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == _lib.CPATTN_OK
-    assert n.value == 0
+    assert n.value > 0
 
 
 def test_paged_null_args(lib):
