@@ -33,6 +33,12 @@
 // LDS layout of a tile: K rows of 256 bytes at 256 t, V rows at 8192 + 256 t; the sixteen 16-byte pieces of token t
 // are stored XOR f(t) = 2t mod 16. Measured on gfx950, the score reads (sixteen tokens at one piece) and the transposed
 // value reads then run at the full rate of their instruction; without the swizzle they run at an eighth of it.
+//
+// fp8 pools (context part): a wave's 8 tokens of K codes (128 bytes a token) arrive with one direct-to-LDS instruction
+// in the upper half of the wave's K rows, and likewise for V; once they have landed the loading wave widens them in
+// place, K to bf16 and V to fp16 (both exact for every E4M3 code), into the same swizzled rows, so the products read
+// the same operands as over bf16 pools. The key descale is folded into the score scale and the value descale into the
+// output normalisation, both in fp32.
 #include "launch.h"
 
 #include <type_traits>
@@ -53,7 +59,10 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockRows = kNW * kRowsPerWave;  // query rows per unit
 constexpr int kMaxPages = 2048;                 // page ids of a stripe staged in LDS
 constexpr int kTokPerWave = kTile / kNW;        // tokens of a tile each wave loads
-constexpr int kLoadsPerTile = 2 * (kTokPerWave / 4);   // direct-to-LDS instructions per wave and tile (K and V)
+// Direct-to-LDS instructions per wave and tile (K and V): 1 KB each, so four tokens of bf16 rows or eight of fp8 rows.
+template <bool KV8>
+constexpr int loads_per_tile() { return KV8 ? 2 : 2 * (kTokPerWave / 4); }
+constexpr int kStage8 = kTokPerWave * kRowBytes / 2;   // fp8 codes of a wave's tokens: upper half of its rows
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) char* lds_char_ptr;
@@ -82,7 +91,8 @@ struct ExtParams {
     int32_t ctx_cap;        // context lengths are clamped to min(max_pages * page_size, max_ctx_len)
     int32_t n_qblocks, n_units, pad_tokens_per_block;
     int32_t pad_lse_only;   // CPATTN_FLAG_PAD_LSE_ONLY: padding tokens get their lse only
-    float scale_log2;
+    float scale_log2;       // softmax scale in log2 units (fp8 pools: times the key descale)
+    float v_scale;          // fp8 pools: the value descale (1 otherwise)
 };
 
 __device__ __forceinline__ int swz(int t) { return (2 * t) & 15; }
@@ -150,10 +160,22 @@ __device__ __forceinline__ int64_t key_row(const ExtParams& p, lds_i32_ptr s_pag
 
 // Issue the direct-to-LDS loads of one tile: wave w loads tokens [kTokPerWave w, kTokPerWave (w + 1)) of K and of V,
 // four tokens (64 lanes x 16 bytes) an instruction; lane l fills stored piece l % 16 of its token with logical piece
-// (l % 16) ^ f(t). Keys past the end take the last key's row (their scores are masked out).
-template <int MODE>
+// (l % 16) ^ f(t). Keys past the end take the last key's row (their scores are masked out). fp8 pools: one
+// instruction per wave for K and one for V, lane l loading codes [16 (l % 8), +16) of token l / 8, in token order
+// into the staging half of the wave's rows.
+template <int MODE, bool KV8>
 __device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
                                            int32_t tile0, int32_t last_key, lds_char_ptr tile, int32_t w, int lane) {
+    if constexpr (KV8) {
+        const int32_t t = kTokPerWave * w + (lane >> 3);
+        const int64_t off = key_row<MODE>(p, s_pages, r, g, tok0, min(tile0 + t, last_key)) + 16 * (lane & 7);
+        const int32_t dst = kRowBytes * kTokPerWave * w + kStage8;
+        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(p.kp) + off),
+                                         (lds_ptr)(tile + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(p.vp) + off),
+                                         (lds_ptr)(tile + kVOff + dst), 16, 0, 0);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kTokPerWave / 4; ++i) {
         const int32_t t = kTokPerWave * w + 4 * i + (lane >> 4);
@@ -177,6 +199,46 @@ __device__ __forceinline__ void widen_v_to_f16(lds_char_ptr tile, int32_t w, int
             (__attribute__((address_space(3))) u32x4_t*)(tile + kVOff + kTokPerWave * w * kRowBytes + 16 * (64 * i + lane));
         *ptr = __builtin_bit_cast(u32x4_t, bf16x8_to_f16(*ptr));
     }
+}
+
+// Widen the fp8 K and V codes this wave staged into a tile (tokens [kTokPerWave w, +kTokPerWave)) into the layout of
+// bf16 tiles: K to bf16, V to fp16, both exact for every E4M3 code. Lane l takes codes [16 j, +16) of token i
+// (i = l / 8, j = l % 8), i.e. logical pieces 2j and 2j + 1 of the token's row, which the swizzle (f(t) even) keeps
+// adjacent. Each lane's codes are read before any lane writes (one read instruction per tensor, whose results the
+// writes wait for), so widening over the staging bytes is safe.
+__device__ __forceinline__ void widen_kv_fp8(lds_char_ptr tile, int32_t w, int lane) {
+    typedef __attribute__((address_space(3))) u32x4_t* lds_u32x4_ptr;
+    const int32_t i = lane >> 3, j = lane & 7;
+    const int32_t t = kTokPerWave * w + i;
+    const int32_t stage = kRowBytes * kTokPerWave * w + kStage8 + 16 * lane;
+    const u32x4_t ck = *(lds_u32x4_ptr)(tile + stage);
+    const u32x4_t cv = *(lds_u32x4_ptr)(tile + kVOff + stage);
+    u32x4_t k2[2], v2[2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t kl = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ck[d], 1.0f, false));
+        const uint32_t kh = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ck[d], 1.0f, true));
+        const uint32_t vl = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cv[d], 1.0f, false));
+        const uint32_t vh = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cv[d], 1.0f, true));
+        k2[d >> 1][2 * (d & 1)] = kl;
+        k2[d >> 1][2 * (d & 1) + 1] = kh;
+        v2[d >> 1][2 * (d & 1)] = vl;
+        v2[d >> 1][2 * (d & 1) + 1] = vh;
+    }
+    const int32_t row = kRowBytes * t + 16 * ((2 * j) ^ swz(t));
+    *(lds_u32x4_ptr)(tile + row) = k2[0];
+    *(lds_u32x4_ptr)(tile + row + 16) = k2[1];
+    *(lds_u32x4_ptr)(tile + kVOff + row) = v2[0];
+    *(lds_u32x4_ptr)(tile + kVOff + row + 16) = v2[1];
+}
+
+// Make a tile this wave loaded ready for the products: V rows to fp16 (bf16 pools) or K and V codes widened (fp8).
+template <bool KV8>
+__device__ __forceinline__ void widen_tile(lds_char_ptr tile, int32_t w, int lane) {
+    if constexpr (KV8)
+        widen_kv_fp8(tile, w, lane);
+    else
+        widen_v_to_f16(tile, w, lane);
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed (the other counters at their maximum).
@@ -209,8 +271,10 @@ __device__ __forceinline__ float group_sum(float x) {
 
 }  // namespace
 
-template <int MODE>
+template <int MODE, bool KV8>
 __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams p) {
+    static_assert(MODE == kFromPool || !KV8, "fp8 codes come from the pools only");
+    constexpr int kLoadsPerTile = loads_per_tile<KV8>();
     // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
     // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
     __shared__ __attribute__((aligned(16))) char s_tile0[kTileBytes];
@@ -363,15 +427,15 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         return t;
     };
     auto prologue = [&]() __attribute__((always_inline)) {
-        issue_tile<MODE>(p, pages, r, g, tok0, 0, last_key, opaque(tile_buf(std::integral_constant<int, 0>{})), w,
-                         lane);
-        issue_tile<MODE>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
-                         opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
-        issue_tile<MODE>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
-                         opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
+        issue_tile<MODE, KV8>(p, pages, r, g, tok0, 0, last_key, opaque(tile_buf(std::integral_constant<int, 0>{})), w,
+                              lane);
+        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
+                              opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
+        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
+                              opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
         wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile 0 are in LDS
         asm volatile("" ::: "memory");                      // (the LDS reads below stay after the wait)
-        widen_v_to_f16(opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
+        widen_tile<KV8>(opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
         wait_lgkm0();
     };
     static_assert(kAhead == 3 && kBufs == 4, "ring");
@@ -467,14 +531,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
     auto step = [&](auto bc, auto live, auto maxonly, int32_t kt) __attribute__((always_inline)) {
         constexpr int bb = decltype(bc)::value;
-        // This wave's pieces of tiles kt and kt + 1 are in LDS (tile kt's V already widened by every wave before the
-        // barrier below; tile kt + 1's V is widened now, before the next step's barrier).
+        // This wave's pieces of tiles kt and kt + 1 are in LDS (tile kt already widened by every wave before the
+        // barrier below; tile kt + 1 is widened now, before the next step's barrier).
         wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
         wait_lgkm0();
         lds_barrier();                                      // every wave's too; tile kt - 1's buffer is free
-        issue_tile<MODE>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
-                         tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
-        widen_v_to_f16(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
+        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
+                              tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
+        widen_tile<KV8>(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
         if constexpr (decltype(live)::value) {
             if constexpr (decltype(maxonly)::value) {
                 float sv[2][8];
@@ -516,7 +580,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
 #pragma unroll
                 for (int db = 0; db < 8; ++db) z += 0.f * o[rb][db][i];
                 if (rho < nrows) {
-                    const float inv = li > 0.f ? 1.0f / li : 0.f;
+                    const float inv = li > 0.f ? (KV8 ? p.v_scale : 1.0f) / li : 0.f;
                     const int32_t t = tok0 + rho / p.G, h = g * p.G + rho % p.G;
                     float* dst = p.out + int64_t(s) * p.o_ss + int64_t(t) * p.o_st + int64_t(h) * p.o_sh + n16;
 #pragma unroll
@@ -569,7 +633,7 @@ namespace {
 
 bool al16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
-int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
+int32_t launch_extend(ExtParams& p, int mode, bool kv8, hipStream_t stream) {
     const int64_t rows = int64_t(std::max(1, p.max_row_tokens)) * p.G;
     p.n_qblocks = int32_t((rows + kBlockRows - 1) / kBlockRows);
     const int64_t units = int64_t(p.B) * p.S * p.Hkv * p.n_qblocks;
@@ -578,10 +642,12 @@ int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
     const int64_t blocks = units + (p.T + 3) / 4;
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
-    if (mode == kFromPool)
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool>), grid, dim3(64 * kNW), 0, stream, p);
+    if (mode == kFromPool && kv8)
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, true>), grid, dim3(64 * kNW), 0, stream, p);
+    else if (mode == kFromPool)
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, false>), grid, dim3(64 * kNW), 0, stream, p);
     else
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn>), grid, dim3(64 * kNW), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn, false>), grid, dim3(64 * kNW), 0, stream, p);
     return check_launch(mode == kFromPool ? "cp_paged_attn_partial (bf16 extend)" : "cp_own_token_attn (bf16)");
 }
 
@@ -589,8 +655,11 @@ int32_t launch_extend(ExtParams& p, int mode, hipStream_t stream) {
 
 bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     if (a.kind != CPATTN_GQA || a.dtype != CPATTN_BF16 || a.head_dim != kD || a.head_dim_v != kD) return false;
-    if (a.kv_format != CPATTN_KV_SAME) return false;
-    if (!(a.scale > 0.f && a.scale < INFINITY)) return false;   // the softmax tracks the max of unscaled scores
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    if (a.kv_format != CPATTN_KV_SAME && !kv8) return false;
+    // The softmax tracks the maximum of unscaled scores, so the scale (times the key descale) must be positive.
+    if (!(a.scale > 0.f && a.scale < INFINITY)) return false;
+    if (kv8 && !(a.scale * a.k_descale > 0.f && a.scale * a.k_descale < INFINITY)) return false;
     const int32_t G = a.num_q_heads / a.num_kv_heads;
     if (kBlockRows % G != 0) return false;
     if (int64_t(a.max_row_tokens) * G <= 16) return false;   // decode-shaped: the decode kernel serves it
@@ -598,9 +667,9 @@ bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     const int64_t max_lr = max_stripe_length(a);
     if ((max_lr + geo.pp - 1) / geo.pp > kMaxPages) return false;
     if (!al16(a.q) || !al16(a.k_pool) || !al16(a.v_pool)) return false;
-    if ((a.q_stride_token | a.q_stride_head | a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot |
-         a.kv_stride_head) & 7)
-        return false;
+    if ((a.q_stride_token | a.q_stride_head) & 7) return false;
+    // 16-byte pieces of every pool row: 8 bf16 elements or 16 fp8 codes
+    if ((a.kv_stride_stripe | a.kv_stride_page | a.kv_stride_slot | a.kv_stride_head) & (kv8 ? 15 : 7)) return false;
     if (int64_t(a.num_rows) * a.stripe_count * a.num_kv_heads * ((int64_t(a.max_row_tokens) * G + kBlockRows - 1) /
                                                                   kBlockRows) + (a.num_tokens + 3) / 4 >
         (int64_t(1) << 31) - 1)
@@ -639,9 +708,11 @@ int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
     p.ctx_cap = ctx_cap_of(a);
     p.page_size = a.page_size;
     p.max_row_tokens = a.max_row_tokens;
-    p.scale_log2 = a.scale * kLog2e;
+    const bool kv8 = a.kv_format == CPATTN_KV_FP8_E4M3;
+    p.scale_log2 = a.scale * (kv8 ? a.k_descale : 1.0f) * kLog2e;
+    p.v_scale = kv8 ? a.v_descale : 1.0f;
     p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
-    return launch_extend(p, kFromPool, stream);
+    return launch_extend(p, kFromPool, kv8, stream);
 }
 
 bool own_bf16_eligible(const cp_own_args& a) {
@@ -686,8 +757,9 @@ int32_t launch_own_token_bf16(const cp_own_args& a, hipStream_t stream) {
     p.page_size = 1;
     p.max_row_tokens = a.max_row_tokens;
     p.scale_log2 = a.scale * kLog2e;
+    p.v_scale = 1.0f;
     p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
-    return launch_extend(p, kFromOwn, stream);
+    return launch_extend(p, kFromOwn, false, stream);
 }
 
 }  // namespace cpattn

@@ -225,16 +225,16 @@ typedef struct cp_paged_args {
  * output).
  *
  * Precision. Scores and sums accumulate in fp32. The value product weights by the probabilities held to about 16
- * significant bits (GQA: a bf16 pair high + residual) or 11 (bf16 MLA: fp16 weights, and the bf16 latent values widened
- * to fp16 for that product, so bf16 MLA latent values must stay below 65504 in magnitude), and every output is
- * normalised by the sum of the weights actually applied.
+ * significant bits (bf16 GQA calls with at most 16 query rows, Hq / Hkv per token, per row and kv head: a bf16 pair
+ * high + residual) or 11 (bf16 GQA calls with more query rows, and bf16 MLA: fp16 weights, with the values widened to
+ * fp16 for that product, so bf16 value elements must stay below 65504 in magnitude; every E4M3 code fits), and every
+ * output is normalised by the sum of the weights actually applied.
  *
  * EINVAL: a null args/pointer, unknown flag bits, interleave < 0, an unknown kv_format, fp8 pools with dtype other
  * than bf16, a descale that is not finite and positive or MLA with k_descale != v_descale, Hq % Hkv != 0, page_size % (I * P) != 0, a stripe range outside [0, P), negative sizes or
  * strides, bt_stride < max_pages, too small a workspace, MLA with Hkv != 1 or v_pool != k_pool.
  * EUNSUPPORTED: a (kind, dtype, head_dim, head_dim_v) with no kernel. Built: GQA f32/bf16 with (64, 64) and
- * (128, 128), bf16 queries over fp8 pools for both; MLA bf16 with (576, 512), also over fp8 latent pools (read by
- * the generic kernel, which decodes each code as it is read).
+ * (128, 128), bf16 queries over fp8 pools for both; MLA bf16 with (576, 512), also over fp8 latent pools.
  */
 int32_t cp_paged_attn_partial(const cp_paged_args* args, hipStream_t stream);
 
@@ -335,7 +335,9 @@ typedef struct cp_own_args {
  *
  * Query i of a row (0-based within the row) sees the row's keys 0..i. Keys and queries of padding tokens are never
  * read; padding tokens get out = 0 and lse = -inf (with CPATTN_FLAG_PAD_LSE_ONLY lse = -inf only, their out rows
- * untouched).
+ * untouched). Precision: fp32 scores and sums; bf16 calls at head_dim 128 weight the values by fp16-rounded
+ * probabilities with the values widened to fp16 (bf16 values must stay below 65504 in magnitude), normalised by the
+ * sum of those weights; other calls compute in fp32.
  * EINVAL: null pointers, negative sizes, Hq % Hkv != 0, unknown flag bits. EUNSUPPORTED: head_dim other than 64 or
  * 128.
  */

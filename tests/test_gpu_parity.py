@@ -113,6 +113,8 @@ FP8 = [
     ("llama8b", dict(batch=3, ctx_lengths=[17, 300, 2222], kv_dtype="fp8", interleave=4)),
     ("mixed", dict(batch=6, new_lengths=[1, 1, 5, 33, 1, 70], ctx_lengths=[0, 19, 0, 300, 1000, 2100], pad_rows=2,
                    kv_dtype="fp8")),
+    ("mixed", dict(batch=4, new_lengths=[17, 2, 130, 64], ctx_lengths=[5000, 33, 1, 2999], pad_rows=1,
+                   kv_dtype="fp8", interleave=2)),
     ("mla", dict(batch=4, ctx_lengths=[1, 3, 70, 700], kv_dtype="fp8")),
     ("mla", dict(batch=2, ctx_lengths=[65, 1500], kv_dtype="fp8", num_q_heads=16, interleave=2)),
     ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000], kv_dtype="fp8", num_q_heads=64)),
@@ -339,19 +341,22 @@ def test_mla_late_score_jump(heads):
     compare_rows(wl, batch, res, [0], DEV)                # the other row is untouched
 
 
-def test_extend_late_score_jump():
-    """A late key aligned with one query head scores over 200 (log2 units) above every key of its tile-0, once among a
-    row's context keys and once among its in-step keys. The bf16 extend kernel takes its softmax reference from a
-    unit's first tile, so p overflows here and the unit repeats with the exact maxima; partials, the own-token part
-    and the merge must still match the oracle."""
-    wl = workloads.make("mixed", batch=2, new_lengths=[40, 3], ctx_lengths=[3000, 500])
-    say("extend late score jump")
+@pytest.mark.parametrize("kv_dtype", ["same", "fp8"])
+def test_extend_late_score_jump(kv_dtype):
+    """A late key aligned with one query head scores far above every key of its tile-0 (over 200 log2 units in bf16,
+    about 100 over fp8 pools, whose largest code is 448 times the key descale), once among a row's context keys and
+    once among its in-step keys. The extend kernel takes its softmax reference from a unit's first tile, so p
+    overflows here and the unit repeats with the exact maxima; partials, the own-token part and the merge must still
+    match the oracle."""
+    wl = workloads.make("mixed", batch=2, new_lengths=[40, 3], ctx_lengths=[3000, 500], kv_dtype=kv_dtype)
+    say(f"extend late score jump {kv_dtype}")
     batch = pool.build_batch(wl, DEV)
     b, c, n, h = 0, 3000, 40, 5
     g = h // (wl.num_q_heads // wl.num_kv_heads)
     rv = workloads.row_values(wl, b, DEV)
     k_ctx = rv.k_ctx.clone()
-    k_ctx[c - 3, g] = (16.0 * torch.sign(rv.q[0, h].float())).to(k_ctx.dtype)     # context key 2997 (stripe 1)
+    big = 448.0 if kv_dtype == "fp8" else 16.0       # fp8: the largest E4M3 code, stored as the code itself
+    k_ctx[c - 3, g] = (big * torch.sign(rv.q[0, h].float())).to(k_ctx.dtype)     # context key 2997 (stripe 1)
     slots = pool.logical_slots(batch.block_table[b], c, wl.page_size)
     api.kv_write(slots, k_ctx, rv.v_ctx, batch.k_pool, batch.v_pool, wl.page_size, wl.partners)
     k_new = rv.k_new.clone()
@@ -360,8 +365,11 @@ def test_extend_late_score_jump():
     batch.k_new[t0:t0 + n] = k_new
     res = pool.run_step(batch)
     torch.cuda.synchronize()
-    parts, merged = oracle.row_partials(rv.q.cpu(), k_ctx.cpu(), rv.v_ctx.cpu(), wl.partners, wl.scale,
-                                        k_new.cpu(), rv.v_new.cpu())
+    kc, vc = k_ctx.cpu(), rv.v_ctx.cpu()
+    if kv_dtype == "fp8":               # what the codes stand for, by the oracle's own decoding
+        kc = oracle.dequantize_e4m3(kc.view(torch.uint8), wl.k_descale)
+        vc = oracle.dequantize_e4m3(vc.view(torch.uint8), wl.v_descale)
+    parts, merged = oracle.row_partials(rv.q.cpu(), kc, vc, wl.partners, wl.scale, k_new.cpu(), rv.v_new.cpu())
     for r in range(wl.partners):
         check_out(res[2][r, t0:t0 + n], parts[r][0], f"stripe {r} out")
         check_lse(res[3][r, t0:t0 + n], parts[r][1], f"stripe {r} lse")
@@ -452,6 +460,27 @@ def _sample_rows(wl, nsample, seed):
     rng = np.random.default_rng(seed)
     return sorted(set([int(order[0]), int(order[-1])] +
                       [int(x) for x in rng.choice(wl.batch, size=nsample - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("name,nsample", [("mixed", 6), ("llama8b", 4)])
+def test_full_size_fp8(name, nsample):
+    """Full-size workloads over fp8 pools (the extend kernel for mixed, the decode kernel for llama8b), as the
+    benchmark times them with --kv-dtype fp8: every row's merged result and sampled rows' partials against the
+    oracle."""
+    wl = workloads.make(name, kv_dtype="fp8")
+    say(f"full size fp8 {name}: B={wl.batch}")
+    batch = pool.build_batch(wl, DEV, fill=0.0)
+    plan = pool.StepPlan(batch, out_dtype=torch.bfloat16)
+    plan.run()
+    torch.cuda.synchronize()
+    own = (plan.own_out, plan.own_lse) if plan.own is not None else None
+    res = (plan.merged, plan.merged_lse, plan.out, plan.lse, own)
+    part_rows = _sample_rows(wl, nsample, 13)
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV, check_partials=part_rows)
+    check_padding(wl, res, partial_rows_written=False)
+    say(f"  partial rows {part_rows} worst {w}")
+    del plan, batch, res
+    torch.cuda.empty_cache()
 
 
 def test_full_size_interleaved_llama8b():
