@@ -144,13 +144,12 @@ __device__ __forceinline__ void sched_pipeline() {
     __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD / R, 0);
 }
 
-// Element offset (from the K or V base) of key j's row for kv head g.
+// Element offset (from the K or V base) of key j's row for kv head g (pool mode: the staged page ids are valid ones).
 template <int MODE>
 __device__ __forceinline__ int64_t key_row(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
                                            int32_t j) {
     if (MODE == kFromPool) {
-        int32_t page = s_pages[j >> p.geo.pp_shift];
-        page = (page >= 0 && page < p.geo.num_pages) ? page : 0;
+        const int32_t page = s_pages[j >> p.geo.pp_shift];
         return int64_t(r) * p.geo.s_stripe + int64_t(page) * p.geo.s_page + int64_t(j & (p.geo.pp - 1)) * p.geo.s_slot +
                int64_t(g) * p.geo.s_head;
     } else {
@@ -163,6 +162,18 @@ __device__ __forceinline__ int64_t key_row(const ExtParams& p, lds_i32_ptr s_pag
 // (l % 16) ^ f(t). Keys past the end take the last key's row (their scores are masked out). fp8 pools: one
 // instruction per wave for K and one for V, lane l loading codes [16 (l % 8), +16) of token l / 8, in token order
 // into the staging half of the wave's rows.
+// One 4-token group i of a bf16 tile, addressed lane by lane.
+template <int MODE>
+__device__ __forceinline__ void issue_group(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
+                                            int32_t tile0, int32_t last_key, lds_char_ptr tile, int32_t w, int lane,
+                                            int i) {
+    const int32_t t = kTokPerWave * w + 4 * i + (lane >> 4);
+    const int64_t off = key_row<MODE>(p, s_pages, r, g, tok0, min(tile0 + t, last_key)) + 8 * ((lane & 15) ^ swz(t));
+    const int32_t dst = kRowBytes * (kTokPerWave * w + 4 * i);
+    __builtin_amdgcn_global_load_lds((const void*)(p.kp + off), (lds_ptr)(tile + dst), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.vp + off), (lds_ptr)(tile + kVOff + dst), 16, 0, 0);
+}
+
 template <int MODE, bool KV8>
 __device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pages, int32_t r, int32_t g, int32_t tok0,
                                            int32_t tile0, int32_t last_key, lds_char_ptr tile, int32_t w, int lane) {
@@ -177,13 +188,7 @@ __device__ __forceinline__ void issue_tile(const ExtParams& p, lds_i32_ptr s_pag
         return;
     }
 #pragma unroll
-    for (int i = 0; i < kTokPerWave / 4; ++i) {
-        const int32_t t = kTokPerWave * w + 4 * i + (lane >> 4);
-        const int64_t off = key_row<MODE>(p, s_pages, r, g, tok0, min(tile0 + t, last_key)) + 8 * ((lane & 15) ^ swz(t));
-        const int32_t dst = kRowBytes * (kTokPerWave * w + 4 * i);
-        __builtin_amdgcn_global_load_lds((const void*)(p.kp + off), (lds_ptr)(tile + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(p.vp + off), (lds_ptr)(tile + kVOff + dst), 16, 0, 0);
-    }
+    for (int i = 0; i < kTokPerWave / 4; ++i) issue_group<MODE>(p, s_pages, r, g, tok0, tile0, last_key, tile, w, lane, i);
 }
 
 // Widen the V rows this wave loaded into a tile (tokens [kTokPerWave w, +kTokPerWave), 256 bytes each, pieces stored
@@ -271,9 +276,15 @@ __device__ __forceinline__ float group_sum(float x) {
 
 }  // namespace
 
-template <int MODE, bool KV8>
+// UPAGE (bf16 pools with pages of at least 4 slots): the 4 tokens of a load instruction share one page (the group's
+// first key, or the last key for a group past it), read from the staged ids a step ahead; each lane's address is the
+// row base plus page times page stride (a 32 x 32 -> 64-bit product) plus its clamped key's slot and its piece. The
+// scalar unit, shared by the CU's four SIMDs, is kept out of the 64-bit arithmetic: moved there it became the
+// bottleneck.
+template <int MODE, bool KV8, bool UPAGE>
 __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams p) {
     static_assert(MODE == kFromPool || !KV8, "fp8 codes come from the pools only");
+    static_assert(!UPAGE || (MODE == kFromPool && !KV8), "uniform pages: bf16 pools");
     constexpr int kLoadsPerTile = loads_per_tile<KV8>();
     // Four tile buffers as separate arrays: a read of one and a tile load into another then refer to different
     // objects, which the wait-count pass needs to see to leave the other tiles' loads in flight.
@@ -368,7 +379,10 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     if (MODE == kFromPool) {
         const int32_t npages = (last_key >> p.geo.pp_shift) + 1;
         const int32_t* bt_row = p.bt + int64_t(b) * p.bt_stride;
-        for (int32_t i = threadIdx.x; i < npages; i += blockDim.x) s_pages[i] = bt_row[i];
+        for (int32_t i = threadIdx.x; i < npages; i += blockDim.x) {
+            const int32_t pg = bt_row[i];
+            s_pages[i] = (pg >= 0 && pg < p.geo.num_pages) ? pg : 0;   // ids outside the pool read page 0
+        }
     }
     __syncthreads();
     const lds_i32_ptr pages = (lds_i32_ptr)s_pages;
@@ -393,6 +407,42 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         for (int db = 0; db < 8; ++db)
             vofs[rr][db] = kVOff + kRowBytes * t + 16 * ((2 * db + ((n16 >> 1) & 1)) ^ swz(t)) + 8 * (n16 & 1);
     }
+
+    // Uniform-page addressing: the row base of (stripe, kv head) and each lane's stored-piece offset, the same on
+    // every tile; V rows lie a fixed distance from K rows.
+    const uint64_t kbase =
+        reinterpret_cast<uint64_t>(p.kp + int64_t(r) * p.geo.s_stripe + int64_t(g) * p.geo.s_head);
+    const int64_t v_minus_k = (reinterpret_cast<const char*>(p.vp) - reinterpret_cast<const char*>(p.kp));
+    const uint32_t page_bytes = uint32_t(2 * p.geo.s_page);       // below 2^32 (launch condition)
+    const uint32_t slot_bytes = uint32_t(2 * p.geo.s_slot);       // slot_bytes * pp below 2^31 (launch condition)
+    uint32_t piece_off[kTokPerWave / 4];
+#pragma unroll
+    for (int i = 0; i < kTokPerWave / 4; ++i)
+        piece_off[i] = uint32_t(16 * ((lane & 15) ^ swz(kTokPerWave * w + 4 * i + (lane >> 4))));
+    // Page ids of this wave's groups of the tile starting at key tile0 (uniform pages only).
+    auto tile_pages = [&](int32_t tile0, int32_t (&pg)[kTokPerWave / 4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kTokPerWave / 4; ++i)
+            pg[i] = UPAGE ? pages[min(tile0 + kTokPerWave * w + 4 * i, last_key) >> p.geo.pp_shift] : 0;
+    };
+    auto issue = [&](int32_t tile0, lds_char_ptr tile, const int32_t (&pg)[kTokPerWave / 4])
+        __attribute__((always_inline)) {
+        if constexpr (UPAGE) {
+#pragma unroll
+            for (int i = 0; i < kTokPerWave / 4; ++i) {
+                // the lane's key, clamped to the last one: on the group's page (pg[i]) whichever way it is clamped
+                const int32_t j = min(tile0 + kTokPerWave * w + 4 * i + (lane >> 4), last_key);
+                const uint64_t ka = uint64_t(uint32_t(pg[i])) * page_bytes + kbase +
+                                    (uint32_t(j & (p.geo.pp - 1)) * slot_bytes + piece_off[i]);
+                const int32_t dst = kRowBytes * (kTokPerWave * w + 4 * i);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ka), (lds_ptr)(tile + dst), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ka + v_minus_k),
+                                                 (lds_ptr)(tile + kVOff + dst), 16, 0, 0);
+            }
+        } else {
+            issue_tile<MODE, KV8>(p, pages, r, g, tok0, tile0, last_key, tile, w, lane);
+        }
+    };
 
     auto tile_buf = [&](auto bc) __attribute__((always_inline)) -> lds_char_ptr {
         constexpr int bb = decltype(bc)::value % kBufs;
@@ -427,12 +477,13 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         return t;
     };
     auto prologue = [&]() __attribute__((always_inline)) {
-        issue_tile<MODE, KV8>(p, pages, r, g, tok0, 0, last_key, opaque(tile_buf(std::integral_constant<int, 0>{})), w,
-                              lane);
-        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min(kTile, (ntiles - 1) * kTile), last_key,
-                              opaque(tile_buf(std::integral_constant<int, 1>{})), w, lane);
-        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min(2 * kTile, (ntiles - 1) * kTile), last_key,
-                              opaque(tile_buf(std::integral_constant<int, 2>{})), w, lane);
+        int32_t pg[kTokPerWave / 4];
+        tile_pages(0, pg);
+        issue(0, opaque(tile_buf(std::integral_constant<int, 0>{})), pg);
+        tile_pages(min(kTile, (ntiles - 1) * kTile), pg);
+        issue(min(kTile, (ntiles - 1) * kTile), opaque(tile_buf(std::integral_constant<int, 1>{})), pg);
+        tile_pages(min(2 * kTile, (ntiles - 1) * kTile), pg);
+        issue(min(2 * kTile, (ntiles - 1) * kTile), opaque(tile_buf(std::integral_constant<int, 2>{})), pg);
         wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();         // this wave's pieces of tile 0 are in LDS
         asm volatile("" ::: "memory");                      // (the LDS reads below stay after the wait)
         widen_tile<KV8>(opaque(tile_buf(std::integral_constant<int, 0>{})), w, lane);
@@ -531,13 +582,16 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     // without the compute, as a separate copy so that no branch on liveness sits inside the pipelined loop.
     auto step = [&](auto bc, auto live, auto maxonly, int32_t kt) __attribute__((always_inline)) {
         constexpr int bb = decltype(bc)::value;
+        // The page ids of the tile issued below are read first; the wait for this step's LDS work covers them.
+        const int32_t tnext = min((kt + kAhead) * kTile, (ntiles - 1) * kTile);
+        int32_t pg[kTokPerWave / 4];
+        tile_pages(tnext, pg);
         // This wave's pieces of tiles kt and kt + 1 are in LDS (tile kt already widened by every wave before the
         // barrier below; tile kt + 1 is widened now, before the next step's barrier).
         wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
         wait_lgkm0();
         lds_barrier();                                      // every wave's too; tile kt - 1's buffer is free
-        issue_tile<MODE, KV8>(p, pages, r, g, tok0, min((kt + kAhead) * kTile, (ntiles - 1) * kTile), last_key,
-                              tile_buf(std::integral_constant<int, bb + kAhead>{}), w, lane);
+        issue(tnext, tile_buf(std::integral_constant<int, bb + kAhead>{}), pg);
         widen_tile<KV8>(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
         if constexpr (decltype(live)::value) {
             if constexpr (decltype(maxonly)::value) {
@@ -643,11 +697,14 @@ int32_t launch_extend(ExtParams& p, int mode, bool kv8, hipStream_t stream) {
     if (blocks == 0) return CPATTN_OK;
     const dim3 grid{uint32_t(blocks), 1, 1};
     if (mode == kFromPool && kv8)
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, true>), grid, dim3(64 * kNW), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, true, false>), grid, dim3(64 * kNW), 0, stream, p);
+    else if (mode == kFromPool && p.geo.pp_shift >= 2 && 2 * p.geo.s_page < (int64_t(1) << 32) &&
+             2 * p.geo.s_slot * p.geo.pp < (int64_t(1) << 31))
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, false, true>), grid, dim3(64 * kNW), 0, stream, p);
     else if (mode == kFromPool)
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, false>), grid, dim3(64 * kNW), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, false, false>), grid, dim3(64 * kNW), 0, stream, p);
     else
-        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn, false>), grid, dim3(64 * kNW), 0, stream, p);
+        hipLaunchKernelGGL((gqa_extend_kernel<kFromOwn, false, false>), grid, dim3(64 * kNW), 0, stream, p);
     return check_launch(mode == kFromPool ? "cp_paged_attn_partial (bf16 extend)" : "cp_own_token_attn (bf16)");
 }
 
