@@ -587,12 +587,12 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         int32_t pg[kTokPerWave / 4];
         tile_pages(tnext, pg);
         // This wave's pieces of tiles kt and kt + 1 are in LDS (tile kt already widened by every wave before the
-        // barrier below; tile kt + 1 is widened now, before the next step's barrier).
+        // barrier below; tile kt + 1 is widened at the end of this step, before the next step's barrier: after the
+        // compute, measured 2.5% faster than before it).
         wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
         wait_lgkm0();
         lds_barrier();                                      // every wave's too; tile kt - 1's buffer is free
         issue(tnext, tile_buf(std::integral_constant<int, bb + kAhead>{}), pg);
-        widen_tile<KV8>(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
         if constexpr (decltype(live)::value) {
             if constexpr (decltype(maxonly)::value) {
                 float sv[2][8];
@@ -603,6 +603,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
                 tile_compute(tile_buf(std::integral_constant<int, bb>{}), kt);
             }
         }
+        widen_tile<KV8>(tile_buf(std::integral_constant<int, bb + 1>{}), w, lane);
     };
     auto run = [&](auto live, auto maxonly) __attribute__((always_inline)) {
         for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
