@@ -643,7 +643,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
     }
     if (!REDO) {
         // A workgroup-wide decision, so that every wave takes the same path.
-        if (lane == 0) s_over[w] = __any(over) ? 1 : 0;
+        // The vote is taken by the whole wave, before the one-lane store: inside `lane == 0` it would see lane 0 only.
+        const bool wave_over = __any(over);
+        if (lane == 0) s_over[w] = wave_over ? 1 : 0;
         __syncthreads();
         int32_t any_over = 0;
 #pragma unroll

@@ -314,18 +314,21 @@ def test_mla_query_head_counts(heads):
     say(f"  worst errors {w}")
 
 
-@pytest.mark.parametrize("heads", [16, 128])
-def test_mla_late_score_jump(heads):
+@pytest.mark.parametrize("target", ["lane0", "lane10"])
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_mla_late_score_jump(heads, target):
     """A late latent row aligned with one query head scores far above everything in the stripe's first tile. The MLA
     kernel takes its softmax reference from a unit's first tile, so this case makes it repeat the unit with the exact
-    maximum; the partials must still match the oracle."""
+    maximum; the partials must still match the oracle. The aligned head is the first of a wave's 16 or one held by
+    another lane (the workgroup's vote must see every lane)."""
     wl = workloads.make("mla", batch=2, ctx_lengths=[300, 1000], num_q_heads=heads)
-    say(f"mla late score jump heads={heads}")
+    h = 0 if target == "lane0" else heads - 6
+    say(f"mla late score jump heads={heads} head={h}")
     batch = pool.build_batch(wl, DEV)
     b, c = 1, 1000
     rv = workloads.row_values(wl, b, DEV)
     lat = rv.k_ctx.clone()
-    lat[c - 3, 0] = (6.0 * torch.sign(rv.q[0, 0].float())).to(lat.dtype)   # about +100 in log2 units for head 0
+    lat[c - 3, 0] = (6.0 * torch.sign(rv.q[0, h].float())).to(lat.dtype)   # about +100 in log2 units for head h
     slots = pool.logical_slots(batch.block_table[b], c, wl.page_size)
     api.kv_write(slots, lat, None, batch.k_pool, None, wl.page_size, wl.partners, kind="mla")
     res = pool.run_step(batch)
