@@ -298,9 +298,6 @@ __device__ __forceinline__ void wait_tile() {
     wait_vmcnt<(kN < 63 ? kN : 63)>();
 }
 
-    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD / R, 0);
-}
-
 // Scheduling groups of the output product: AHEAD LDS reads, then G groups of M MFMAs, each but the last followed by R
 // reads.
 template <int M, int G, int AHEAD, int R>
