@@ -246,6 +246,30 @@ SMALL = [
 ]
 
 
+EXTEND_PAGES = [
+    # the extend kernel addresses keys a 4-token group at a time when pages hold 4 or more slots, else lane by lane
+    ("pp2", dict(batch=4, new_lengths=[1, 40, 7, 100], ctx_lengths=[500, 3000, 40, 9], partners=8, pad_rows=1)),
+    ("pp1", dict(batch=3, new_lengths=[33, 5, 64], ctx_lengths=[1000, 77, 2], partners=8, page_size=8)),
+    ("pp8-fp8", dict(batch=3, new_lengths=[70, 1, 20], ctx_lengths=[2000, 300, 31], partners=2, kv_dtype="fp8")),
+    ("pp16-i2", dict(batch=3, new_lengths=[9, 130, 2], ctx_lengths=[700, 2500, 65], partners=2, page_size=32,
+                     interleave=2)),
+]
+
+
+@pytest.mark.parametrize("case,kw", EXTEND_PAGES, ids=[c[0] for c in EXTEND_PAGES])
+def test_extend_page_geometries(case, kw):
+    """Multi-token rows over pools whose pages hold 1, 2, 8 or 16 slots (P = 8 or 2, pages of 8 to 32): the extend
+    kernel's lane-by-lane and grouped key addressing, against the oracle."""
+    wl = workloads.make("mixed", **kw)
+    say(f"extend page geometry {case}: P={wl.partners} page={wl.page_size} ctx={list(wl.ctx_len)}")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch)
+    torch.cuda.synchronize()
+    w = compare_rows(wl, batch, res, range(wl.batch), DEV)
+    check_padding(wl, res)
+    say(f"  worst errors {w}")
+
+
 @pytest.mark.parametrize("fixed_splits", [False, True], ids=["balanced", "fixed"])
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_step_parity_small(name, kw, fixed_splits):
