@@ -21,6 +21,9 @@ CASES = [
     ("longctx", dict(batch=4, ctx_lengths=[5, 100, 4097, 9001]), False),
     ("llama8b-p16", dict(batch=3, ctx_lengths=[5, 300, 2000], partners=16), False),   # more than 8 stripes: two calls
     ("mla", dict(batch=3, ctx_lengths=[7, 130, 2000]), False),
+    ("mla-fp8", dict(batch=3, ctx_lengths=[7, 130, 2000], kv_dtype="fp8"), False),
+    ("llama8b-ext", dict(batch=4, new_lengths=[1, 40, 7, 100], ctx_lengths=[500, 3000, 40, 9]), False),   # extend kernel
+    ("llama8b-ext8", dict(batch=4, new_lengths=[1, 40, 7, 100], ctx_lengths=[500, 3000, 40, 9], kv_dtype="fp8"), False),
     ("tiny", dict(), False),
 ]
 

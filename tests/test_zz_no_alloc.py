@@ -30,6 +30,9 @@ CASES = [
     ("mla", dict(batch=3, ctx_lengths=[7, 130, 5000]), dict(batch=2, ctx_lengths=[2, 64])),
     ("mixed", dict(batch=4, new_lengths=[1, 40, 3, 100], ctx_lengths=[0, 300, 2000, 50], pad_rows=1),
      dict(batch=2, new_lengths=[5, 1], ctx_lengths=[10, 0])),
+    ("llama8b-fp8", dict(batch=5, ctx_lengths=[3, 300, 2100, 8192, 77], kv_dtype="fp8"),
+     dict(batch=2, ctx_lengths=[900, 5], kv_dtype="fp8")),
+    ("mla-fp8", dict(batch=3, ctx_lengths=[7, 130, 5000], kv_dtype="fp8"), dict(batch=1, ctx_lengths=[64], kv_dtype="fp8")),
 ]
 
 
@@ -38,7 +41,7 @@ CASES = [
 def test_noalloc_matches_workspace_call(name, big, small, fixed_splits):
     print(f"noalloc {name} fixed_splits={fixed_splits}", flush=True)
     for kw in (big, small):                     # two calls in a row, the second with a smaller input
-        wl = workloads.make(name, **kw)
+        wl = workloads.make(name.split("-")[0], **kw)
         batch = pool.build_batch(wl, DEV)
         (ro, rl), (o, l) = _both(batch, wl, fixed_splits)
         assert torch.equal(o, ro) and torch.equal(l, rl)
