@@ -1,5 +1,5 @@
-// bf16 MLA per-stripe paged partial (one latent head: key = the 576-value latent row, value = its first 512 values),
-// built for gfx950 MFMA.
+// MLA per-stripe paged partial over bf16 or fp8 E4M3 latent pools (one latent head: key = the 576-value latent row,
+// value = its first 512 values), built for gfx950 MFMA.
 //
 // What it computes is the partial of one partner over the slots it holds, returned as (out, natural-log lse), with the
 // one latent head of MLA shared by all query heads (mstar PR #1124, "Context / Sequence Parallel 1/5", PR description:
