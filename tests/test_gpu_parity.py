@@ -419,6 +419,41 @@ def test_repeat_calls_are_deterministic(fixed_splits):
         assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
 
 
+@pytest.mark.parametrize("kv_dtype", ["same", "fp8"])
+def test_workspace_needs_no_initial_contents(kv_dtype):
+    """The balanced schedule (static shares, then small chunks claimed from a counter in the workspace) gives the same
+    bits whatever the workspace held before the call: zeros, all-ones bytes, random bytes, a NaN fill, or what the
+    previous call left."""
+    wl = workloads.make("llama8b", batch=6, ctx_lengths=[8192, 5000, 2000, 7777, 31, 12000], kv_dtype=kv_dtype)
+    say(f"workspace contents {kv_dtype}")
+    batch = pool.build_batch(wl, DEV)
+    args = (batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len, batch.block_table)
+    kw = dict(page_size=wl.page_size, partners=wl.partners, scale=wl.scale, kind=wl.kind,
+              max_ctx_len=batch.max_ctx_len, max_row_tokens=batch.max_row_tokens, interleave=wl.interleave,
+              k_descale=wl.k_descale, v_descale=wl.v_descale)
+    n = api.paged_attn_workspace_size(*args, **kw)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref_o, ref_l = api.paged_attn_partial(*args, workspace=ws, **kw)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    fills = {"ones": lambda: ws.fill_(255), "random": lambda: ws.copy_(torch.randint(0, 256, (n,), generator=g,
+             device=DEV, dtype=torch.uint8)), "nan": lambda: ws[: n // 4 * 4].view(torch.float32).fill_(float("nan")),
+             "leftover": lambda: None, "zeros": lambda: ws.zero_()}
+    for what, fill in fills.items():
+        fill()
+        o, l = api.paged_attn_partial(*args, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), what
+    mo = torch.empty(batch.q.shape[0], wl.num_q_heads, wl.head_dim_v, dtype=torch.float32, device=DEV)
+    ml = torch.empty(batch.q.shape[0], wl.num_q_heads, dtype=torch.float32, device=DEV)
+    api.paged_attn_merged(*args, merged=mo, merged_lse=ml, workspace=ws, **kw)
+    ref_mo, ref_ml = mo.clone(), ml.clone()
+    for what, fill in fills.items():
+        fill()
+        api.paged_attn_merged(*args, merged=mo, merged_lse=ml, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(mo, ref_mo) and torch.equal(ml, ref_ml), f"merged {what}"
+
+
 @pytest.mark.parametrize("ctx_lengths", [[32768, 30001, 20000], [32769, 64, 5000]], ids=["at_limit", "past_limit"])
 def test_extend_rows_at_page_staging_limit(ctx_lengths):
     """Multi-token rows whose stripes hold 2048 pages (the most the bf16 extend kernel stages in LDS), and a batch one
