@@ -66,7 +66,7 @@ constexpr int kMaxChunkPages = 512;            // page ids of one chunk staged i
 constexpr int kKSteps = kD / 32;               // k-steps of the score product
 constexpr int kMaxPlanUnits = 1024;            // units sorted by the plan kernel (block order above)
 constexpr int kTargetUnits = 512;              // about two units per compute unit before chunks are split
-constexpr int kFp8Off = kRowV - kD;            // fp8 tiles: a token's 576 codes land in [kFp8Off, kRowV) of its row
+constexpr int kFp8Off = kRowV - 1024;          // fp8 tiles: a token's 576 codes land at [kFp8Off, kFp8Off + 576) of its row
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -195,26 +195,26 @@ constexpr int kLatentCpol = CPATTN_MLA_NONTEMPORAL ? 2 : 0;     // 2: the nt bit
 //   * value dims [0, 512): wave w takes tokens [T w, T w + T) with T = 32 / NW, one instruction per token: 64 lanes x
 //     16 bytes = the token's 1024 bytes, written to its padded LDS row. The row address is moved to scalar registers
 //     with readlane, so each lane adds only its fixed 16-byte offset.
-//   * rope dims [512, 576): 4-byte loads, 32 lanes per token, two tokens per instruction (16 per tile, shared evenly
-//     by the waves, so every wave issues the same loads and no lane is masked); lane l fills dword l % 32 of its
-//     token's rope row, i.e. stored piece (l % 32) / 4, with the matching dword of logical piece ((l % 32) / 4) ^ g(t).
+//   * rope dims [512, 576): whole 128-byte rope rows, 16 bytes a lane (below).
 template <int NW, bool KV8>
 __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int32_t w, int lane) {
     constexpr int kTpw = kTile / NW;
     const uint32_t alo = uint32_t(rows), ahi = uint32_t(rows >> 32);
     if constexpr (KV8) {
-        // fp8 latent rows (576 one-byte codes): one instruction per token, lanes 0..35 loading 16 bytes each into
-        // the upper part [kFp8Off, kRowV) of the token's LDS row; widen_tile_fp8 turns them into the bf16 layout.
+        // fp8 latent rows (576 one-byte codes): one instruction per token, all 64 lanes loading 16 bytes each into
+        // [kFp8Off, kRowV) of the token's LDS row: lanes 0..35 the codes, lanes 36..63 a second copy of the row's
+        // first 448 bytes into the row's tail, which the widening overwrites (and whose last 32 bytes are padding).
+        // widen_tile_fp8 turns the codes into the bf16 layout. (Masking lanes 36..63 instead put the loads under a
+        // branch, and the compiler's wait-count pass then waited for every tile in flight at that point of the loop.)
 #pragma unroll
         for (int i = 0; i < kTpw; ++i) {
             const int32_t t = kTpw * w + i;                                      // wave-uniform
             const uint64_t base = (uint64_t(uint32_t(__builtin_amdgcn_readlane(ahi, t))) << 32) |
                                   uint32_t(__builtin_amdgcn_readlane(alo, t));
-            if (lane < kD / 16) {
-                const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * lane);
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t + kFp8Off), 16, 0,
-                                                 kLatentCpol);
-            }
+            const int32_t piece = lane < kD / 16 ? lane : lane - kD / 16;
+            const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * piece);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t + kFp8Off), 16, 0,
+                                             kLatentCpol);
         }
         return;
     }
@@ -226,25 +226,32 @@ __device__ __forceinline__ void issue_tile(uint64_t rows, lds_char_ptr tile, int
         const char* src = reinterpret_cast<const char*>(base) + uint32_t(16 * lane);
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRowV * t), 16, 0, kLatentCpol);
     }
-    constexpr int kRInstr = (kTile / 2) / NW;                                    // 256-byte instructions
+    // rope dims: 16-byte loads, 8 lanes per token (a 128-byte rope row), lane l of an instruction filling stored
+    // piece l % 8 of token first + l / 8 from the matching logical piece (l % 8) ^ g(t): 8 tokens per instruction, the
+    // tile's 4 instructions taken by the first waves (kRopeWaves of them, the same number each).
+    constexpr int kRopeWaves = NW < 4 ? NW : 4;
+    constexpr int kRInstr = 4 / kRopeWaves;
+    if (NW <= 4 || w < kRopeWaves) {                                            // (every wave when NW <= 4)
 #pragma unroll
-    for (int i = 0; i < kRInstr; ++i) {
-        const int32_t pair = kRInstr * w + i;                                    // tokens 2 pair, 2 pair + 1
-        const int32_t t = 2 * pair + (lane >> 5);
-        const int32_t q = lane & 31;                                             // dword of the 128-byte rope row
-        const uint64_t base = (uint64_t(uint32_t(__shfl(int32_t(ahi), t))) << 32) | uint32_t(__shfl(int32_t(alo), t));
-        const char* src = reinterpret_cast<const char*>(base) + 1024 + 16 * ((q >> 2) ^ swz(t)) + 4 * (q & 3);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRegionV + kRowR * 2 * pair), 4, 0, kLatentCpol);
+        for (int i = 0; i < kRInstr; ++i) {
+            const int32_t first = 8 * (kRInstr * w + i);                         // wave-uniform
+            const int32_t t = first + (lane >> 3);
+            const uint64_t base = (uint64_t(uint32_t(__shfl(int32_t(ahi), t))) << 32) | uint32_t(__shfl(int32_t(alo), t));
+            const char* src = reinterpret_cast<const char*>(base) + 1024 + 16 * ((lane & 7) ^ swz(t));
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tile + kRegionV + kRowR * first), 16, 0,
+                                             kLatentCpol);
+        }
     }
 }
 
-// Direct-to-LDS loads a wave issues per tile (the same for every wave).
+// Direct-to-LDS loads the waves with the fewest issue per tile: waits leave at most that many of a later tile in flight,
+// which for the waves issuing the rope loads as well waits for a little more than needed.
 template <int NW, bool KV8>
 __device__ __forceinline__ constexpr int tile_loads() {
-    return KV8 ? kTile / NW : kTile / NW + (kTile / 2) / NW;
+    return KV8 ? kTile / NW : kTile / NW + (NW <= 4 ? 4 / NW : 0);
 }
 
-// fp8 tiles: widen the rows this wave loaded (tokens [32 w / NW, +32 / NW)) from the E4M3 codes at [kFp8Off, kRowV)
+// fp8 tiles: widen the rows this wave loaded (tokens [32 w / NW, +32 / NW)) from the E4M3 codes at [kFp8Off, +576)
 // of each row to the bf16 layout the products read: value dims [0, 512) at the start of the row, rope dims in the
 // swizzled rope row. Sixteen lanes a token, each taking 32 value codes and 4 rope codes; every read of a pass is done
 // before its writes (they depend on the read data), so the in-place overlap of source and destination is safe. The
@@ -264,18 +271,16 @@ __device__ __forceinline__ void widen_tile_fp8(lds_char_ptr tile, int32_t w, int
             return (u32x2_t){__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true))};
         };
-        u32x4_t out[4];
+        // Each 16-byte piece is stored as soon as it is converted (the reads above all come first), so that only one
+        // piece's registers are live at a time.
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const u32x2_t a = wide(q < 2 ? c0[2 * q] : c1[2 * (q - 2)]);
             const u32x2_t b = wide(q < 2 ? c0[2 * q + 1] : c1[2 * (q - 2) + 1]);
-            out[q] = (u32x4_t){a[0], a[1], b[0], b[1]};
+            *(__attribute__((address_space(3))) u32x4_t*)(row + 64 * j + 16 * q) = (u32x4_t){a[0], a[1], b[0], b[1]};
         }
-        const u32x2_t rr = wide(cr);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *(__attribute__((address_space(3))) u32x4_t*)(row + 64 * j + 16 * q) = out[q];
         *(__attribute__((address_space(3))) u32x2_t*)(tile + kRegionV + kRowR * t + 16 * ((j >> 1) ^ swz(t)) +
-                                                      8 * (j & 1)) = rr;
+                                                      8 * (j & 1)) = wide(cr);
     }
 }
 
@@ -633,8 +638,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(const MlaParams 
             const int32_t tn0 = min(x.j0 + (kt + kAhead) * kTile, last_tile0);
             issue_tile<NW, KV8>(token_rows<KV8>(p, pages, pidx0, tn0, j_last, kv_r, lane),
                                 tile_buf(std::integral_constant<int, b + kAhead>{}), w, lane);
-            // fp8: widen this wave's rows of tile kt + 1 (loaded); the next step's barrier publishes them
-            if constexpr (KV8) widen_tile_fp8<NW>(tile_buf(std::integral_constant<int, b + 1>{}), w, lane);
+            // fp8: widen this wave's rows of tile kt + 1 (loaded); the next step's barrier publishes them. Fenced from
+            // the compute in the instruction schedule: interleaved, both sets of temporaries are live and spill.
+            if constexpr (KV8) {
+                widen_tile_fp8<NW>(tile_buf(std::integral_constant<int, b + 1>{}), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             tile_compute(tile_buf(std::integral_constant<int, b>{}), kt);
         };
         for (int32_t kt = 0; kt < ntiles; kt += kBufs) {
