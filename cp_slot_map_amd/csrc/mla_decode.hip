@@ -263,7 +263,13 @@ __device__ __forceinline__ void widen_tile_fp8(lds_char_ptr tile, int32_t w, int
 #pragma unroll
     for (int pass = 0; pass < kTpw / 4; ++pass) {
         const int32_t t = kTpw * w + 4 * pass + (lane >> 4);
-        const lds_char_ptr row = tile + kRowV * t;
+        // The lane's offsets inside a tile go through an empty asm statement: the compiler then keeps one copy of
+        // them and adds each buffer's address where it is used, instead of holding (buffer + offset) for each of the
+        // loop's four buffers across the loop (registers that made the 128-head kernel spill, and the spill reloads
+        // inside the loop waited for every tile in flight).
+        int32_t row_off = kRowV * t, rope_off = kRegionV + kRowR * t + 16 * ((j >> 1) ^ swz(t)) + 8 * (j & 1);
+        asm volatile("" : "+v"(row_off), "+v"(rope_off));
+        const lds_char_ptr row = tile + row_off;
         const u32x4_t c0 = *(const __attribute__((address_space(3))) u32x4_t*)(row + kFp8Off + 32 * j);
         const u32x4_t c1 = *(const __attribute__((address_space(3))) u32x4_t*)(row + kFp8Off + 32 * j + 16);
         const uint32_t cr = *(const __attribute__((address_space(3))) uint32_t*)(row + kFp8Off + kDv + 4 * j);
@@ -279,8 +285,7 @@ __device__ __forceinline__ void widen_tile_fp8(lds_char_ptr tile, int32_t w, int
             const u32x2_t b = wide(q < 2 ? c0[2 * q + 1] : c1[2 * (q - 2) + 1]);
             *(__attribute__((address_space(3))) u32x4_t*)(row + 64 * j + 16 * q) = (u32x4_t){a[0], a[1], b[0], b[1]};
         }
-        *(__attribute__((address_space(3))) u32x2_t*)(tile + kRegionV + kRowR * t + 16 * ((j >> 1) ^ swz(t)) +
-                                                      8 * (j & 1)) = wide(cr);
+        *(__attribute__((address_space(3))) u32x2_t*)(tile + rope_off) = wide(cr);
     }
 }
 
