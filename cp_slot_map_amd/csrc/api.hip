@@ -105,7 +105,7 @@ static int32_t check_paged_pointers(const cp_paged_args& a) {
 }
 
 static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
-    if (extend_bf16_eligible(a, geo)) return 0;
+    if (extend_bf16_eligible(a, geo)) return extend_bf16_workspace_bytes(a);
     if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes(a);
     if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
     return 0;
@@ -113,7 +113,7 @@ static int64_t paged_workspace(const cp_paged_args& a, const PoolGeom& geo) {
 
 // Scratch bytes a call touches on the current device (at most paged_workspace()).
 static int64_t paged_workspace_on_device(const cp_paged_args& a, const PoolGeom& geo) {
-    if (extend_bf16_eligible(a, geo)) return 0;
+    if (extend_bf16_eligible(a, geo)) return extend_bf16_workspace_bytes(a);
     if (decode_bf16_eligible(a, geo)) return decode_bf16_workspace_bytes_on_device(a, geo);
     if (mla_decode_eligible(a, geo)) return mla_decode_workspace_bytes(a);
     return 0;

@@ -186,4 +186,35 @@ __device__ __forceinline__ void fill_excess_tokens(float* out, int64_t o_st, int
     if (t_begin < tok1) fill_padding(out, 0, o_st, o_sh, lse, 0, l_st, 1, Hq, Dv, t_begin, tok1, lane, nlanes, lse_only);
 }
 
+// Plans of the unit kernels: order[rank] = i for the n items whose keys (work estimates) sit in LDS, rank = the number
+// of items with a larger key, or an equal key and a smaller index (longest first, ties in index order). s_key holds
+// n16 = n rounded up to 16 entries, those past n set to -1 (below every real key). Workgroup b of 256 threads ranks
+// items [64 b, 64 b + 64): four threads share an item, each comparing it with a quarter of the keys, four at a time,
+// and the quarters' counts are summed through s_part (256 entries). Spread over n / 64 workgroups, the n^2 comparisons
+// take a few microseconds for a few thousand items.
+__device__ __forceinline__ void rank_longest_first(const int32_t* s_key, int32_t* s_part, int32_t n, int32_t* order) {
+    const int32_t tid = threadIdx.x;
+    const int32_t n16 = (n + 15) & ~15;
+    const int32_t u = int32_t(blockIdx.x) * 64 + (tid & 63);
+    const int32_t quarter = tid >> 6;
+    int32_t rank = 0;
+    if (u < n) {
+        const int32_t mine = s_key[u];
+        const int4* key4 = reinterpret_cast<const int4*>(s_key);
+        const int32_t q4 = n16 / 16;                        // int4 entries per quarter
+#pragma unroll 4
+        for (int32_t v4 = quarter * q4; v4 < (quarter + 1) * q4; ++v4) {
+            const int4 o = key4[v4];
+            const int32_t v = 4 * v4;
+            rank += (o.x > mine) || (o.x == mine && v < u);
+            rank += (o.y > mine) || (o.y == mine && v + 1 < u);
+            rank += (o.z > mine) || (o.z == mine && v + 2 < u);
+            rank += (o.w > mine) || (o.w == mine && v + 3 < u);
+        }
+    }
+    s_part[tid] = rank;
+    __syncthreads();
+    if (tid < 64 && u < n) order[s_part[tid] + s_part[tid + 64] + s_part[tid + 128] + s_part[tid + 192]] = u;
+}
+
 }  // namespace cpattn

@@ -58,6 +58,7 @@ constexpr int kNW = 4;                          // waves per workgroup (two work
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockRows = kNW * kRowsPerWave;  // query rows per unit
 constexpr int kMaxPages = 2048;                 // page ids of a stripe staged in LDS
+constexpr int kMaxPlanTriples = 8192;           // (row, stripe, query block) triples the plan kernel ranks
 constexpr int kTokPerWave = kTile / kNW;        // tokens of a tile each wave loads
 // Direct-to-LDS instructions per wave and tile (K and V): 1 KB each, so four tokens of bf16 rows or eight of fp8 rows.
 template <bool KV8>
@@ -80,6 +81,7 @@ struct ExtParams {
     PoolGeom geo;                  // pool mode
     int64_t kv_st, kv_sh;          // own mode: token and head strides of k and v
     const int32_t* row_start;      // q_row_start (pool mode) or cu_seqlens (own mode)
+    int32_t* order;                // pool mode with a plan: triples by rank, longest stripe first (null: grid order)
     const int32_t* ctx_len;        // pool mode
     const int32_t* bt;
     int64_t bt_stride;
@@ -274,7 +276,33 @@ __device__ __forceinline__ float group_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Plan key of triple v = (row b, stripe s, query block qb), v = (b S + s) n_qblocks + qb: the stripe length when the
+// block holds query rows, -1 when it lies past the row's rows (such workgroups only return, so they go last).
+__device__ int32_t triple_key(const ExtParams& p, int32_t v) {
+    const int32_t qb = v % p.n_qblocks;
+    v /= p.n_qblocks;
+    const int32_t s = v % p.S, b = v / p.S;
+    const int32_t tok0 = min(max(p.row_start[b], 0), p.T);
+    const int32_t tok1 = min(max(p.row_start[b + 1], tok0), p.T);
+    if (qb * kBlockRows >= min(tok1 - tok0, p.max_row_tokens) * p.G) return -1;
+    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
+    return stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
+}
+
 }  // namespace
+
+// Plan of the context part: the triples ranked by stripe length, longest first, into p.order. Rows bring very
+// different amounts of work (context and in-step lengths both vary), and the hardware hands out workgroups in grid
+// order as slots free up: run in row order, the last rows' long units set the end of the launch while most CUs idle.
+__global__ __launch_bounds__(256) void gqa_extend_plan_kernel(const ExtParams p) {
+    __shared__ __attribute__((aligned(16))) int32_t s_key[kMaxPlanTriples];
+    __shared__ int32_t s_part[256];
+    const int32_t n = p.n_units / p.Hkv;
+    const int32_t n16 = (n + 15) & ~15;
+    for (int32_t v = threadIdx.x; v < n16; v += blockDim.x) s_key[v] = v < n ? triple_key(p, v) : -1;
+    __syncthreads();
+    rank_longest_first(s_key, s_part, n, p.order);
+}
 
 // UPAGE (bf16 pools with pages of at least 4 slots): the 4 tokens of a load instruction share one page (the group's
 // first key, or the last key for a group past it), read from the staged ids a step ahead; each lane's address is the
@@ -308,13 +336,15 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         return;
     }
 
-    // Unit order: kv head fastest, then query block, stripe, row. The hardware hands block i to XCD i mod 8, so with
-    // 8 kv heads (or a multiple) every XCD gets one head of every (row, stripe, block): equal work per XCD whatever
-    // the mix of row lengths, and the query blocks of one (row, stripe, kv head), which read the same K/V tiles, run
-    // on one XCD close together in time and share its L2.
+    // Unit order: kv head fastest, then the (row, stripe, query block) triple: with a plan the triples by rank
+    // (longest stripe first; a row's blocks of one stripe stay adjacent), else query block, stripe, row. The hardware
+    // hands block i to XCD i mod 8, so with 8 kv heads (or a multiple) every XCD gets one head of every triple: equal
+    // work per XCD whatever the mix of row lengths, and the query blocks of one (row, stripe, kv head), which read the
+    // same K/V tiles, run on one XCD close together in time and share its L2.
     int32_t v = blk;
     const int32_t g = v % p.Hkv;
     v /= p.Hkv;
+    if (MODE == kFromPool && p.order) v = ((const_i32_ptr)p.order)[v];
     const int32_t qb = v % p.n_qblocks;
     v /= p.n_qblocks;
     const int32_t s = v % p.S;
@@ -696,6 +726,10 @@ int32_t launch_extend(ExtParams& p, int mode, bool kv8, hipStream_t stream) {
     p.pad_tokens_per_block = 4;
     const int64_t blocks = units + (p.T + 3) / 4;
     if (blocks == 0) return CPATTN_OK;
+    if (p.order && units > 0) {
+        hipLaunchKernelGGL(gqa_extend_plan_kernel, dim3(uint32_t((units / p.Hkv + 63) / 64)), dim3(256), 0, stream, p);
+        if (int32_t st = check_launch("cp_paged_attn_partial (extend plan)")) return st;
+    }
     const dim3 grid{uint32_t(blocks), 1, 1};
     if (mode == kFromPool && kv8)
         hipLaunchKernelGGL((gqa_extend_kernel<kFromPool, true, false>), grid, dim3(64 * kNW), 0, stream, p);
@@ -735,8 +769,21 @@ bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo) {
     return true;
 }
 
+// (row, stripe, query block) triples of a context-part launch, and the workspace of its plan: one int32 rank entry a
+// triple, when there are at least two and at most kMaxPlanTriples (otherwise the units run in grid order).
+int64_t extend_triples(const cp_paged_args& a) {
+    const int64_t G = a.num_q_heads / a.num_kv_heads;
+    return int64_t(a.num_rows) * a.stripe_count * ((int64_t(std::max(1, a.max_row_tokens)) * G + kBlockRows - 1) / kBlockRows);
+}
+
+int64_t extend_bf16_workspace_bytes(const cp_paged_args& a) {
+    const int64_t n = extend_triples(a);
+    return n >= 2 && n <= kMaxPlanTriples ? (4 * n + 255) / 256 * 256 : 0;
+}
+
 int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream) {
     ExtParams p{};
+    p.order = extend_bf16_workspace_bytes(a) > 0 ? static_cast<int32_t*>(a.workspace) : nullptr;
     p.q = static_cast<const uint16_t*>(a.q);
     p.q_st = a.q_stride_token;
     p.q_sh = a.q_stride_head;

@@ -38,6 +38,7 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
 // workgroup, K/V tiles staged in LDS, MFMA score and value products. The same kernel serves the own-token part.
 bool extend_bf16_eligible(const cp_paged_args& a, const PoolGeom& geo);
 int32_t launch_paged_extend_bf16(const cp_paged_args& a, const PoolGeom& geo, hipStream_t stream);
+int64_t extend_bf16_workspace_bytes(const cp_paged_args& a);
 bool own_bf16_eligible(const cp_own_args& a);
 int32_t launch_own_token_bf16(const cp_own_args& a, hipStream_t stream);
 

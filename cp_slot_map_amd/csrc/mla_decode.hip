@@ -332,39 +332,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
-// Plan: rank every unit by its token count, longest first (ties in unit order), into p.order. Workgroup b ranks units
-// [64 b, 64 b + 64): each workgroup loads all n lengths into LDS (entries past n hold -1, below every real length, so
-// they never count), four threads share a unit and each compares it with a quarter of the others, reading four
-// lengths at a time; the quarter counts are summed through LDS. Spread over n / 64 workgroups, the n^2 comparisons take
-// a few microseconds instead of the ~16 us one workgroup needed.
+// Plan: every unit ranked by its token count, longest first (ties in unit order), into p.order.
 __global__ __launch_bounds__(256) void mla_plan_kernel(const MlaParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_len[kMaxPlanUnits];
     __shared__ int32_t s_part[256];
-    const int32_t tid = threadIdx.x;
     const int32_t n = p.n_units;
-    const int32_t n16 = (n + 15) & ~15;                  // a multiple of 16: four quarters of whole int4 reads
-    for (int32_t v = tid; v < n16; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, v) : -1;
+    const int32_t n16 = (n + 15) & ~15;
+    for (int32_t v = threadIdx.x; v < n16; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, v) : -1;
     __syncthreads();
-    const int32_t u = int32_t(blockIdx.x) * 64 + (tid & 63);
-    const int32_t quarter = tid >> 6;
-    int32_t rank = 0;
-    if (u < n) {
-        const int32_t mine = s_len[u];
-        const int4* s_len4 = reinterpret_cast<const int4*>(s_len);
-        const int32_t q4 = n16 / 16;                     // int4 entries per quarter
-#pragma unroll 4
-        for (int32_t v4 = quarter * q4; v4 < (quarter + 1) * q4; ++v4) {
-            const int4 o = s_len4[v4];
-            const int32_t v = 4 * v4;
-            rank += (o.x > mine) || (o.x == mine && v < u);
-            rank += (o.y > mine) || (o.y == mine && v + 1 < u);
-            rank += (o.z > mine) || (o.z == mine && v + 2 < u);
-            rank += (o.w > mine) || (o.w == mine && v + 3 < u);
-        }
-    }
-    s_part[tid] = rank;
-    __syncthreads();
-    if (tid < 64 && u < n) p.order[s_part[tid] + s_part[tid + 64] + s_part[tid + 128] + s_part[tid + 192]] = u;
+    rank_longest_first(s_len, s_part, n, p.order);
 }
 
 // One workgroup per (unit, group of 16 NW heads); wave w of group hg owns heads hg 16 NW + 16 w + [0, 16).

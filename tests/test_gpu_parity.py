@@ -419,13 +419,20 @@ def test_repeat_calls_are_deterministic(fixed_splits):
         assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
 
 
+WORKSPACE_CASES = [
+    ("llama8b", dict(batch=6, ctx_lengths=[8192, 5000, 2000, 7777, 31, 12000])),
+    ("mixed", dict(batch=5, new_lengths=[1, 200, 37, 3, 90], ctx_lengths=[5000, 2100, 0, 777, 64], pad_rows=1)),
+]
+
+
 @pytest.mark.parametrize("kv_dtype", ["same", "fp8"])
-def test_workspace_needs_no_initial_contents(kv_dtype):
-    """The balanced schedule (static shares, then small chunks claimed from a counter in the workspace) gives the same
-    bits whatever the workspace held before the call: zeros, all-ones bytes, random bytes, a NaN fill, or what the
-    previous call left."""
-    wl = workloads.make("llama8b", batch=6, ctx_lengths=[8192, 5000, 2000, 7777, 31, 12000], kv_dtype=kv_dtype)
-    say(f"workspace contents {kv_dtype}")
+@pytest.mark.parametrize("name,kw", WORKSPACE_CASES, ids=[c[0] for c in WORKSPACE_CASES])
+def test_workspace_needs_no_initial_contents(name, kw, kv_dtype):
+    """The calls give the same bits whatever the workspace held before: zeros, all-ones bytes, random bytes, a NaN
+    fill, or what the previous call left. It holds the decode kernel's balanced schedule (static shares, then small
+    chunks claimed from a counter) and the extend kernel's plan (the units' order, every entry written before use)."""
+    wl = workloads.make(name, kv_dtype=kv_dtype, **kw)
+    say(f"workspace contents {name} {kv_dtype}")
     batch = pool.build_batch(wl, DEV)
     args = (batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len, batch.block_table)
     kw = dict(page_size=wl.page_size, partners=wl.partners, scale=wl.scale, kind=wl.kind,
@@ -452,6 +459,32 @@ def test_workspace_needs_no_initial_contents(kv_dtype):
         api.paged_attn_merged(*args, merged=mo, merged_lse=ml, workspace=ws, **kw)
         torch.cuda.synchronize()
         assert torch.equal(mo, ref_mo) and torch.equal(ml, ref_ml), f"merged {what}"
+
+
+def test_extend_plan_and_grid_order_give_the_same_bits():
+    """The context part runs its units longest stripe first when the launch has at most 8192 (row, stripe, query
+    block) triples (a plan kernel ranks them), in grid order beyond that. 70 rows with one of 1000 tokens make 8960
+    triples over four stripes (grid order) and 2240 for one stripe (planned): each stripe's share equals the same
+    stripe of the all-stripes call to the bit, and sampled rows match the oracle."""
+    rng = np.random.default_rng(11)
+    new = [int(x) for x in rng.integers(1, 4, size=70)]
+    new[17] = 1000
+    ctx = [int(x) for x in rng.integers(0, 200, size=70)]
+    wl = workloads.make("mixed", batch=70, new_lengths=new, ctx_lengths=ctx)
+    say(f"extend plan vs grid order: {sum(new)} tokens")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch)
+    _, _, po, pl, _ = res
+    t = int(sum(new))
+    for r in range(wl.partners):
+        o, l = api.paged_attn_partial(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
+                                      batch.block_table, page_size=wl.page_size, partners=wl.partners,
+                                      scale=wl.scale, stripe_begin=r, stripe_count=1, max_ctx_len=batch.max_ctx_len,
+                                      max_row_tokens=batch.max_row_tokens)
+        torch.cuda.synchronize()
+        assert torch.equal(o[0, :t], po[r, :t]) and torch.equal(l[0, :t], pl[r, :t]), f"stripe {r}"
+    w = compare_rows(wl, batch, res, [0, 17, 40, 69], DEV, check_partials=True)
+    say(f"  worst errors {w}")
 
 
 @pytest.mark.parametrize("ctx_lengths", [[32768, 30001, 20000], [32769, 64, 5000]], ids=["at_limit", "past_limit"])
