@@ -186,24 +186,46 @@ __device__ __forceinline__ void fill_excess_tokens(float* out, int64_t o_st, int
     if (t_begin < tok1) fill_padding(out, 0, o_st, o_sh, lse, 0, l_st, 1, Hq, Dv, t_begin, tok1, lane, nlanes, lse_only);
 }
 
+// Per-(row, stripe) inputs of the plans' keys, staged in LDS by a workgroup: for pair bs = b S + s,
+// s_ntok[bs] = row b's query tokens that are attended (at most max_row_tokens) and s_lr[bs] = the length of stripe
+// stripe_begin + s of its context (clamped to [0, ctx_cap]). The pairs' loads are independent of one another, so a
+// workgroup gathers its first blockDim.x pairs in the time of one load.
+__device__ __forceinline__ void stage_plan_pairs(const int32_t* row_start, const int32_t* ctx_len, int32_t B, int32_t S,
+                                                 int32_t T, int32_t max_row_tokens, int32_t ctx_cap,
+                                                 int32_t stripe_begin, int32_t P, int32_t I, int32_t* s_ntok,
+                                                 int32_t* s_lr) {
+    for (int32_t bs = threadIdx.x; bs < B * S; bs += blockDim.x) {
+        const int32_t b = bs / S;
+        const int32_t tok0 = min(max(row_start[b], 0), T);
+        const int32_t tok1 = min(max(row_start[b + 1], tok0), T);
+        s_ntok[bs] = min(tok1 - tok0, max_row_tokens);
+        s_lr[bs] = stripe_length(min(max(ctx_len[b], 0), ctx_cap), stripe_begin + bs % S, P, I);
+    }
+}
+
 // Plans of the unit kernels: order[rank] = i for the n items whose keys (work estimates) sit in LDS, rank = the number
 // of items with a larger key, or an equal key and a smaller index (longest first, ties in index order). s_key holds
-// n16 = n rounded up to 16 entries, those past n set to -1 (below every real key). Workgroup b of 256 threads ranks
-// items [64 b, 64 b + 64): four threads share an item, each comparing it with a quarter of the keys, four at a time,
-// and the quarters' counts are summed through s_part (256 entries). Spread over n / 64 workgroups, the n^2 comparisons
-// take a few microseconds for a few thousand items.
+// rank_padded(n) entries, those past n set to -1 (below every real key). A workgroup of 256 threads ranks kRankItems
+// items: kRankThreads threads share an item, each comparing it with its part of the keys, four at a time, and the
+// parts' counts are summed through s_part (256 entries). Many small workgroups spread the n^2 comparisons over the
+// whole chip.
+constexpr int kRankThreads = 16;
+constexpr int kRankItems = 256 / kRankThreads;
+__host__ __device__ __forceinline__ int32_t rank_padded(int32_t n) {
+    return (n + 4 * kRankThreads - 1) & ~(4 * kRankThreads - 1);
+}
+
 __device__ __forceinline__ void rank_longest_first(const int32_t* s_key, int32_t* s_part, int32_t n, int32_t* order) {
     const int32_t tid = threadIdx.x;
-    const int32_t n16 = (n + 15) & ~15;
-    const int32_t u = int32_t(blockIdx.x) * 64 + (tid & 63);
-    const int32_t quarter = tid >> 6;
+    const int32_t u = int32_t(blockIdx.x) * kRankItems + tid % kRankItems;
+    const int32_t part = tid / kRankItems;
     int32_t rank = 0;
     if (u < n) {
         const int32_t mine = s_key[u];
         const int4* key4 = reinterpret_cast<const int4*>(s_key);
-        const int32_t q4 = n16 / 16;                        // int4 entries per quarter
+        const int32_t per = rank_padded(n) / (4 * kRankThreads);   // int4 entries of a part
 #pragma unroll 4
-        for (int32_t v4 = quarter * q4; v4 < (quarter + 1) * q4; ++v4) {
+        for (int32_t v4 = part * per; v4 < (part + 1) * per; ++v4) {
             const int4 o = key4[v4];
             const int32_t v = 4 * v4;
             rank += (o.x > mine) || (o.x == mine && v < u);
@@ -214,7 +236,12 @@ __device__ __forceinline__ void rank_longest_first(const int32_t* s_key, int32_t
     }
     s_part[tid] = rank;
     __syncthreads();
-    if (tid < 64 && u < n) order[s_part[tid] + s_part[tid + 64] + s_part[tid + 128] + s_part[tid + 192]] = u;
+    if (tid < kRankItems && u < n) {
+        int32_t r = 0;
+#pragma unroll
+        for (int k = 0; k < kRankThreads; ++k) r += s_part[k * kRankItems + tid];
+        order[r] = u;
+    }
 }
 
 }  // namespace cpattn

@@ -276,17 +276,13 @@ __device__ __forceinline__ float group_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Plan key of triple v = (row b, stripe s, query block qb), v = (b S + s) n_qblocks + qb: the stripe length when the
-// block holds query rows, -1 when it lies past the row's rows (such workgroups only return, so they go last).
-__device__ int32_t triple_key(const ExtParams& p, int32_t v) {
-    const int32_t qb = v % p.n_qblocks;
-    v /= p.n_qblocks;
-    const int32_t s = v % p.S, b = v / p.S;
-    const int32_t tok0 = min(max(p.row_start[b], 0), p.T);
-    const int32_t tok1 = min(max(p.row_start[b + 1], tok0), p.T);
-    if (qb * kBlockRows >= min(tok1 - tok0, p.max_row_tokens) * p.G) return -1;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
-    return stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
+// Plan key of triple v = (row b, stripe s, query block qb), v = (b S + s) n_qblocks + qb, from the staged pairs: the
+// stripe length when the block holds query rows, -1 when it lies past the row's rows (such workgroups only return, so
+// they go last).
+__device__ __forceinline__ int32_t triple_key(const ExtParams& p, const int32_t* s_ntok, const int32_t* s_lr,
+                                              int32_t v) {
+    const int32_t bs = v / p.n_qblocks, qb = v - bs * p.n_qblocks;
+    return qb * kBlockRows < s_ntok[bs] * p.G ? s_lr[bs] : -1;
 }
 
 }  // namespace
@@ -296,10 +292,14 @@ __device__ int32_t triple_key(const ExtParams& p, int32_t v) {
 // order as slots free up: run in row order, the last rows' long units set the end of the launch while most CUs idle.
 __global__ __launch_bounds__(256) void gqa_extend_plan_kernel(const ExtParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_key[kMaxPlanTriples];
+    __shared__ int32_t s_ntok[kMaxPlanTriples], s_lr[kMaxPlanTriples];    // (row, stripe) pairs: B S <= triples
     __shared__ int32_t s_part[256];
     const int32_t n = p.n_units / p.Hkv;
-    const int32_t n16 = (n + 15) & ~15;
-    for (int32_t v = threadIdx.x; v < n16; v += blockDim.x) s_key[v] = v < n ? triple_key(p, v) : -1;
+    const int32_t npad = rank_padded(n);
+    stage_plan_pairs(p.row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
+                     p.geo.interleave, s_ntok, s_lr);
+    __syncthreads();
+    for (int32_t v = threadIdx.x; v < npad; v += blockDim.x) s_key[v] = v < n ? triple_key(p, s_ntok, s_lr, v) : -1;
     __syncthreads();
     rank_longest_first(s_key, s_part, n, p.order);
 }
@@ -340,12 +340,13 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     // (longest stripe first; a row's blocks of one stripe stay adjacent), else query block, stripe, row. The hardware
     // hands block i to XCD i mod 8, so with 8 kv heads (or a multiple) every XCD gets one head of every triple: equal
     // work per XCD whatever the mix of row lengths, and the query blocks of one (row, stripe, kv head), which read the
-    // same K/V tiles, run on one XCD close together in time and share its L2.
+    // same K/V tiles, run on one XCD close together in time and share its L2. In the own-token part a row's query
+    // blocks run last block first: a block attends the keys up to its last token, so the long ones start early.
     int32_t v = blk;
     const int32_t g = v % p.Hkv;
     v /= p.Hkv;
     if (MODE == kFromPool && p.order) v = ((const_i32_ptr)p.order)[v];
-    const int32_t qb = v % p.n_qblocks;
+    const int32_t qb = MODE == kFromOwn ? p.n_qblocks - 1 - v % p.n_qblocks : v % p.n_qblocks;
     v /= p.n_qblocks;
     const int32_t s = v % p.S;
     const int32_t b = v / p.S;
@@ -727,7 +728,8 @@ int32_t launch_extend(ExtParams& p, int mode, bool kv8, hipStream_t stream) {
     const int64_t blocks = units + (p.T + 3) / 4;
     if (blocks == 0) return CPATTN_OK;
     if (p.order && units > 0) {
-        hipLaunchKernelGGL(gqa_extend_plan_kernel, dim3(uint32_t((units / p.Hkv + 63) / 64)), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(gqa_extend_plan_kernel, dim3(uint32_t((units / p.Hkv + kRankItems - 1) / kRankItems)), dim3(256),
+                           0, stream, p);
         if (int32_t st = check_launch("cp_paged_attn_partial (extend plan)")) return st;
     }
     const dim3 grid{uint32_t(blocks), 1, 1};

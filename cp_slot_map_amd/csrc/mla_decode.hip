@@ -156,20 +156,14 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     return x;
 }
 
-// Tokens of unit u (0 when it does no attention work): the sort key of the plan kernel.
-__device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, int32_t u) {
-    const int32_t c = u % p.n_chunks;
-    int32_t v = u / p.n_chunks;
-    const int32_t qtok = v % p.unit_tokens;
-    v /= p.unit_tokens;
-    const int32_t s = v % p.S;
-    const int32_t b = v / p.S;
-    const int32_t tok0 = min(max(p.q_row_start[b], 0), p.T);
-    const int32_t tok1 = min(max(p.q_row_start[b + 1], tok0), p.T);
-    if (qtok >= min(tok1 - tok0, p.max_row_tokens)) return 0;
-    const int32_t L = min(max(p.ctx_len[b], 0), p.ctx_cap);
-    const int32_t Lr = stripe_length(L, p.stripe_begin + s, p.P, p.geo.interleave);
-    return max(0, min(Lr - c * p.chunk_tokens, p.chunk_tokens));
+// Tokens of unit u (0 when it does no attention work), from the staged (row, stripe) pairs: the sort key of the plan
+// kernel.
+__device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, const int32_t* s_ntok, const int32_t* s_lr,
+                                               int32_t u) {
+    const int32_t v = u / p.n_chunks, c = u - v * p.n_chunks;
+    const int32_t bs = v / p.unit_tokens, qtok = v - bs * p.unit_tokens;
+    if (qtok >= s_ntok[bs]) return 0;
+    return max(0, min(s_lr[bs] - c * p.chunk_tokens, p.chunk_tokens));
 }
 
 // Byte address of tile token L % 32's latent row in lane L, from the chunk's page ids staged in LDS (tokens past the
@@ -335,10 +329,14 @@ __device__ __forceinline__ void lds_barrier() {
 // Plan: every unit ranked by its token count, longest first (ties in unit order), into p.order.
 __global__ __launch_bounds__(256) void mla_plan_kernel(const MlaParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_len[kMaxPlanUnits];
+    __shared__ int32_t s_ntok[kMaxPlanUnits], s_lr[kMaxPlanUnits];      // (row, stripe) pairs: B S <= units
     __shared__ int32_t s_part[256];
     const int32_t n = p.n_units;
-    const int32_t n16 = (n + 15) & ~15;
-    for (int32_t v = threadIdx.x; v < n16; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, v) : -1;
+    const int32_t npad = rank_padded(n);
+    stage_plan_pairs(p.q_row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
+                     p.geo.interleave, s_ntok, s_lr);
+    __syncthreads();
+    for (int32_t v = threadIdx.x; v < npad; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, s_ntok, s_lr, v) : -1;
     __syncthreads();
     rank_longest_first(s_len, s_part, n, p.order);
 }
@@ -864,7 +862,8 @@ int32_t launch_mla_decode(const cp_paged_args& a, const PoolGeom& geo, hipStream
     p.pad_lse_only = (a.flags & CPATTN_FLAG_PAD_LSE_ONLY) ? 1 : 0;
 
     if (p.order) {
-        hipLaunchKernelGGL(mla_plan_kernel, dim3(uint32_t((d.n_units + 63) / 64)), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(mla_plan_kernel, dim3(uint32_t((d.n_units + kRankItems - 1) / kRankItems)), dim3(256), 0, stream,
+                           p);
         if (int32_t st = check_launch("cp_paged_attn_partial (MLA plan)")) return st;
     }
     const int64_t blocks = d.work_blocks + p.pad_blocks;

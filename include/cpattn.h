@@ -286,8 +286,9 @@ int32_t cp_paged_attn_merged(const cp_paged_args* args, const cp_merge_out* merg
  * overlap on one device (different streams without ordering between them) race and give undefined results; calls
  * ordered on one stream are safe.
  * EINVAL: as cp_paged_attn_partial, and a call whose workspace would exceed the static scratch (see
- * cp_paged_attn_workspace_size; the bf16 decode schedule needs about 4-17 MB on MI355X, MLA up to a few hundred MB
- * for small batches whose stripes are split into many chunks). ELAUNCH: the scratch address could not be obtained.
+ * cp_paged_attn_workspace_size; the bf16 decode schedule needs about 4-17 MB on MI355X, the bf16 extend kernel's
+ * unit order at most 32 KB, MLA up to a few hundred MB for small batches whose stripes are split into many chunks).
+ * ELAUNCH: the scratch address could not be obtained.
  */
 int32_t cp_paged_attn_partial_noalloc(const cp_paged_args* args, hipStream_t stream);
 
