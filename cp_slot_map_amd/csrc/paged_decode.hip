@@ -1059,12 +1059,17 @@ __device__ __forceinline__ void merge_records(const DecodeParams& p, int64_t A, 
     }
 }
 
+// The fix-up and finish kernels run one independent wave per item, kFinishWaves of them a workgroup: fewer, larger
+// workgroups start sooner than one single-wave workgroup per item.
+constexpr int kFinishWaves = 4;
+
 // Items split over several waves are merged from their records; tiles with query rows but no context get (0, -inf);
-// extra blocks write padding tokens. One wave per (tile, kv head).
-__global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams p) {
-    const int lane = threadIdx.x;
-    const int32_t idx = blockIdx.x;
+// extra waves write padding tokens. One wave per (tile, kv head).
+__global__ __launch_bounds__(64 * kFinishWaves) void gqa_decode_fixup_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int32_t idx = int32_t(blockIdx.x) * kFinishWaves + int32_t(threadIdx.x >> 6);
     const int32_t n_items = p.num_tiles * p.Hkv;
+    if (idx >= n_items + p.pad_blocks) return;
     if (idx >= n_items) {
         const int32_t k = idx - n_items;
         const int32_t first = min(max(p.q_row_start[p.B], 0), p.T);
@@ -1126,10 +1131,11 @@ __global__ __launch_bounds__(64) void gqa_decode_fixup_kernel(const DecodeParams
 // also writes the split items' and empty stripes' partials, so the partial buffer ends as after cp_paged_attn_partial.
 // Extra blocks write padding tokens: (0, -inf) in every partial and in the merged output.
 template <bool BF16OUT, int SMAX>
-__global__ __launch_bounds__(64) void gqa_decode_finish_kernel(const DecodeParams p) {
-    const int lane = threadIdx.x;
-    const int32_t idx = blockIdx.x;
+__global__ __launch_bounds__(64 * kFinishWaves) void gqa_decode_finish_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int32_t idx = int32_t(blockIdx.x) * kFinishWaves + int32_t(threadIdx.x >> 6);
     const int32_t n_items = p.B * p.n_qtiles * p.Hkv;
+    if (idx >= n_items + p.pad_blocks) return;
     const int32_t d8 = lane & 15, rsub = lane >> 4;
     auto merged_row = [&](int32_t t, int32_t h, const f32x4_t (&acc)[2]) __attribute__((always_inline)) {
         const int64_t off = int64_t(t) * p.m_st + int64_t(h) * p.m_sh + 8 * d8;
@@ -1454,22 +1460,24 @@ int32_t launch_paged_decode_bf16(const cp_paged_args& a, const PoolGeom& geo, hi
             p.m_sh = m->out_stride_head;
             p.m_lse = m->lse;
             p.m_lst = m->lse_stride_token;
-            const int64_t blocks = int64_t(a.num_rows) * d.n_qtiles * a.num_kv_heads + p.pad_blocks;
-            if (blocks == 0) return CPATTN_OK;
-            const dim3 grid{uint32_t(blocks), 1, 1};
+            const int64_t waves = int64_t(a.num_rows) * d.n_qtiles * a.num_kv_heads + p.pad_blocks;
+            if (waves == 0) return CPATTN_OK;
+            const dim3 grid{uint32_t((waves + kFinishWaves - 1) / kFinishWaves), 1, 1};
+            const dim3 block{64 * kFinishWaves, 1, 1};
             const bool bf = m->out_dtype == CPATTN_BF16;
             if (a.stripe_count <= 4) {
-                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 4>), grid, dim3(64), 0, stream, p);
-                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 4>), grid, dim3(64), 0, stream, p);
+                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 4>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 4>), grid, block, 0, stream, p);
             } else {
-                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 8>), grid, dim3(64), 0, stream, p);
-                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 8>), grid, dim3(64), 0, stream, p);
+                if (bf) hipLaunchKernelGGL((gqa_decode_finish_kernel<true, 8>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gqa_decode_finish_kernel<false, 8>), grid, block, 0, stream, p);
             }
             return check_launch("cp_paged_attn_merged (finish)");
         }
-        const int64_t fix_blocks = d.num_tiles * a.num_kv_heads + p.pad_blocks;
-        if (fix_blocks > 0) {
-            hipLaunchKernelGGL(gqa_decode_fixup_kernel, dim3(uint32_t(fix_blocks)), dim3(64), 0, stream, p);
+        const int64_t fix_waves = d.num_tiles * a.num_kv_heads + p.pad_blocks;
+        if (fix_waves > 0) {
+            hipLaunchKernelGGL(gqa_decode_fixup_kernel, dim3(uint32_t((fix_waves + kFinishWaves - 1) / kFinishWaves)),
+                               dim3(64 * kFinishWaves), 0, stream, p);
             return check_launch("cp_paged_attn_partial (fix-up)");
         }
         return CPATTN_OK;
