@@ -429,8 +429,8 @@ WORKSPACE_CASES = [
 @pytest.mark.parametrize("name,kw", WORKSPACE_CASES, ids=[c[0] for c in WORKSPACE_CASES])
 def test_workspace_needs_no_initial_contents(name, kw, kv_dtype):
     """The calls give the same bits whatever the workspace held before: zeros, all-ones bytes, random bytes, a NaN
-    fill, or what the previous call left. It holds the decode kernel's balanced schedule (static shares, then small
-    chunks claimed from a counter) and the extend kernel's plan (the units' order, every entry written before use)."""
+    fill, or what the previous call left. It holds the decode kernel's row offsets and split-item records and the
+    extend kernel's plan (the units' order); every entry is written before it is read."""
     wl = workloads.make(name, kv_dtype=kv_dtype, **kw)
     say(f"workspace contents {name} {kv_dtype}")
     batch = pool.build_batch(wl, DEV)
