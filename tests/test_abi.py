@@ -176,6 +176,24 @@ def test_paged_workspace_size_is_host_only(lib):
     assert lib.cp_paged_attn_workspace_size(C.byref(f), C.byref(n)) == _lib.CPATTN_OK and n.value > 0
 
 
+def test_extend_workspace_holds_the_plan(lib):
+    """bf16 rows with more than 16 query rows per kv head run the extend kernel, whose plan (one int32 per (row, stripe,
+    query block of 128 rows) triple, ranked longest stripe first) lives in the workspace, rounded up to 256 bytes; past
+    8192 triples the units run in grid order and need none."""
+    strides = dict(kv_stride_slot=128, kv_stride_head=512, kv_stride_page=4096, kv_stride_stripe=40960,
+                   q_stride_token=4096, q_stride_head=128, out_stride_stripe=8192, out_stride_token=4096,
+                   out_stride_head=128, lse_stride_stripe=64, lse_stride_token=32)
+    n = C.c_int64(-1)
+    for kw, want in [(dict(max_row_tokens=40, num_tokens=80), 256),                      # 2 rows x 4 stripes x 2 blocks
+                     (dict(max_row_tokens=40, num_tokens=80, kv_format=1, k_descale=0.5, v_descale=0.5), 256),
+                     (dict(num_rows=1024, max_row_tokens=64, num_tokens=1024), 4 * 8192),  # 8192 triples
+                     (dict(num_rows=1024, max_row_tokens=65, num_tokens=1024), 0),         # 12288: grid order
+                     (dict(num_rows=1, stripe_count=1, max_row_tokens=20, num_tokens=20), 0)]:  # one triple
+        a = _paged(**strides, **kw)
+        assert lib.cp_paged_attn_workspace_size(C.byref(a), C.byref(n)) == _lib.CPATTN_OK, _err(lib)
+        assert n.value == want, (kw, n.value)
+
+
 def test_own_token_refusals(lib):
     a = _lib.OwnArgs()
     a.dtype, a.num_rows, a.bucket_tokens, a.num_q_heads, a.num_kv_heads, a.head_dim = 1, 2, 16, 32, 8, 96
