@@ -487,6 +487,30 @@ def test_extend_plan_and_grid_order_give_the_same_bits():
     say(f"  worst errors {w}")
 
 
+def test_mla_plan_and_grid_order_give_the_same_bits():
+    """The MLA kernel runs its units longest first when a launch has at most 1024 of them (a plan kernel ranks them),
+    in grid order beyond that. 260 rows over four stripes make 1040 units (grid order), one stripe 260 (planned): each
+    stripe's share equals the same stripe of the all-stripes call to the bit, and sampled rows match the oracle."""
+    rng = np.random.default_rng(12)
+    ctx = [int(x) for x in rng.integers(0, 96, size=260)]
+    ctx[100] = 760                              # stripes of at most 190 tokens: one chunk in both calls
+    wl = workloads.make("mla", batch=260, ctx_lengths=ctx)
+    say(f"mla plan vs grid order: {sum(ctx)} context tokens")
+    batch = pool.build_batch(wl, DEV)
+    res = pool.run_step(batch)
+    _, _, po, pl, _ = res
+    t = wl.num_tokens
+    for r in range(wl.partners):
+        o, l = api.paged_attn_partial(batch.q, batch.k_pool, batch.v_pool, batch.q_row_start, batch.ctx_len,
+                                      batch.block_table, page_size=wl.page_size, partners=wl.partners,
+                                      scale=wl.scale, kind="mla", stripe_begin=r, stripe_count=1,
+                                      max_ctx_len=batch.max_ctx_len, max_row_tokens=batch.max_row_tokens)
+        torch.cuda.synchronize()
+        assert torch.equal(o[0, :t], po[r, :t]) and torch.equal(l[0, :t], pl[r, :t]), f"stripe {r}"
+    w = compare_rows(wl, batch, res, [0, 100, 259], DEV, check_partials=True)
+    say(f"  worst errors {w}")
+
+
 @pytest.mark.parametrize("ctx_lengths", [[32768, 30001, 20000], [32769, 64, 5000]], ids=["at_limit", "past_limit"])
 def test_extend_rows_at_page_staging_limit(ctx_lengths):
     """Multi-token rows whose stripes hold 2048 pages (the most the bf16 extend kernel stages in LDS), and a batch one
