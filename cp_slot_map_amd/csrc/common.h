@@ -186,20 +186,33 @@ __device__ __forceinline__ void fill_excess_tokens(float* out, int64_t o_st, int
     if (t_begin < tok1) fill_padding(out, 0, o_st, o_sh, lse, 0, l_st, 1, Hq, Dv, t_begin, tok1, lane, nlanes, lse_only);
 }
 
-// Per-(row, stripe) inputs of the plans' keys, staged in LDS by a workgroup: for pair bs = b S + s,
-// s_ntok[bs] = row b's query tokens that are attended (at most max_row_tokens) and s_lr[bs] = the length of stripe
-// stripe_begin + s of its context (clamped to [0, ctx_cap]). The pairs' loads are independent of one another, so a
-// workgroup gathers its first blockDim.x pairs in the time of one load.
-__device__ __forceinline__ void stage_plan_pairs(const int32_t* row_start, const int32_t* ctx_len, int32_t B, int32_t S,
-                                                 int32_t T, int32_t max_row_tokens, int32_t ctx_cap,
-                                                 int32_t stripe_begin, int32_t P, int32_t I, int32_t* s_ntok,
-                                                 int32_t* s_lr) {
-    for (int32_t bs = threadIdx.x; bs < B * S; bs += blockDim.x) {
-        const int32_t b = bs / S;
-        const int32_t tok0 = min(max(row_start[b], 0), T);
-        const int32_t tok1 = min(max(row_start[b + 1], tok0), T);
-        s_ntok[bs] = min(tok1 - tok0, max_row_tokens);
-        s_lr[bs] = stripe_length(min(max(ctx_len[b], 0), ctx_cap), stripe_begin + bs % S, P, I);
+// The plans' per-(row, stripe) inputs: for every pair bs = b S + s of a workgroup's share, f(bs, ntok, lr) with ntok =
+// row b's query tokens that are attended (at most max_row_tokens) and lr = the length of stripe stripe_begin + s of
+// its context (clamped to [0, ctx_cap]). A thread takes four pairs at a time and issues their loads before using any,
+// so a workgroup gathers 4 blockDim.x pairs in the time of one load.
+template <class F>
+__device__ __forceinline__ void for_each_plan_pair(const int32_t* row_start, const int32_t* ctx_len, int32_t B,
+                                                   int32_t S, int32_t T, int32_t max_row_tokens, int32_t ctx_cap,
+                                                   int32_t stripe_begin, int32_t P, int32_t I, F&& f) {
+    const int32_t n = B * S;
+    for (int32_t bs0 = threadIdx.x; bs0 < n; bs0 += 4 * blockDim.x) {
+        int32_t q0[4], q1[4], cl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int32_t b = min(bs0 + u * int32_t(blockDim.x), n - 1) / S;
+            q0[u] = row_start[b];
+            q1[u] = row_start[b + 1];
+            cl[u] = ctx_len[b];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int32_t bs = bs0 + u * int32_t(blockDim.x);
+            if (bs >= n) break;
+            const int32_t tok0 = min(max(q0[u], 0), T);
+            const int32_t tok1 = min(max(q1[u], tok0), T);
+            f(bs, min(tok1 - tok0, max_row_tokens),
+              stripe_length(min(max(cl[u], 0), ctx_cap), stripe_begin + bs % S, P, I));
+        }
     }
 }
 

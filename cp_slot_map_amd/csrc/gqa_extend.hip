@@ -276,15 +276,6 @@ __device__ __forceinline__ float group_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Plan key of triple v = (row b, stripe s, query block qb), v = (b S + s) n_qblocks + qb, from the staged pairs: the
-// stripe length when the block holds query rows, -1 when it lies past the row's rows (such workgroups only return, so
-// they go last).
-__device__ __forceinline__ int32_t triple_key(const ExtParams& p, const int32_t* s_ntok, const int32_t* s_lr,
-                                              int32_t v) {
-    const int32_t bs = v / p.n_qblocks, qb = v - bs * p.n_qblocks;
-    return qb * kBlockRows < s_ntok[bs] * p.G ? s_lr[bs] : -1;
-}
-
 }  // namespace
 
 // Plan of the context part: the triples ranked by stripe length, longest first, into p.order. Rows bring very
@@ -292,14 +283,17 @@ __device__ __forceinline__ int32_t triple_key(const ExtParams& p, const int32_t*
 // order as slots free up: run in row order, the last rows' long units set the end of the launch while most CUs idle.
 __global__ __launch_bounds__(256) void gqa_extend_plan_kernel(const ExtParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_key[kMaxPlanTriples];
-    __shared__ int32_t s_ntok[kMaxPlanTriples], s_lr[kMaxPlanTriples];    // (row, stripe) pairs: B S <= triples
     __shared__ int32_t s_part[256];
     const int32_t n = p.n_units / p.Hkv;
     const int32_t npad = rank_padded(n);
-    stage_plan_pairs(p.row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
-                     p.geo.interleave, s_ntok, s_lr);
-    __syncthreads();
-    for (int32_t v = threadIdx.x; v < npad; v += blockDim.x) s_key[v] = v < n ? triple_key(p, s_ntok, s_lr, v) : -1;
+    // Key of triple v = (row b, stripe s, query block qb), v = (b S + s) n_qblocks + qb: the stripe length when the
+    // block holds query rows, -1 when it lies past the row's rows (such workgroups only return, so they go last).
+    const int32_t nq = p.n_qblocks;
+    for_each_plan_pair(p.row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
+                       p.geo.interleave, [&](int32_t bs, int32_t ntok, int32_t lr) {
+                           for (int32_t qb = 0; qb < nq; ++qb) s_key[bs * nq + qb] = qb * kBlockRows < ntok * p.G ? lr : -1;
+                       });
+    for (int32_t v = n + int32_t(threadIdx.x); v < npad; v += blockDim.x) s_key[v] = -1;
     __syncthreads();
     rank_longest_first(s_key, s_part, n, p.order);
 }

@@ -156,16 +156,6 @@ __device__ __forceinline__ Unit decode_unit(const MlaParams& p, int32_t u) {
     return x;
 }
 
-// Tokens of unit u (0 when it does no attention work), from the staged (row, stripe) pairs: the sort key of the plan
-// kernel.
-__device__ __forceinline__ int32_t unit_tokens(const MlaParams& p, const int32_t* s_ntok, const int32_t* s_lr,
-                                               int32_t u) {
-    const int32_t v = u / p.n_chunks, c = u - v * p.n_chunks;
-    const int32_t bs = v / p.unit_tokens, qtok = v - bs * p.unit_tokens;
-    if (qtok >= s_ntok[bs]) return 0;
-    return max(0, min(s_lr[bs] - c * p.chunk_tokens, p.chunk_tokens));
-}
-
 // Byte address of tile token L % 32's latent row in lane L, from the chunk's page ids staged in LDS (tokens past the
 // chunk end take its last token, whose values are masked out; invalid page ids read page 0).
 template <bool KV8>
@@ -329,14 +319,19 @@ __device__ __forceinline__ void lds_barrier() {
 // Plan: every unit ranked by its token count, longest first (ties in unit order), into p.order.
 __global__ __launch_bounds__(256) void mla_plan_kernel(const MlaParams p) {
     __shared__ __attribute__((aligned(16))) int32_t s_len[kMaxPlanUnits];
-    __shared__ int32_t s_ntok[kMaxPlanUnits], s_lr[kMaxPlanUnits];      // (row, stripe) pairs: B S <= units
     __shared__ int32_t s_part[256];
     const int32_t n = p.n_units;
     const int32_t npad = rank_padded(n);
-    stage_plan_pairs(p.q_row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
-                     p.geo.interleave, s_ntok, s_lr);
-    __syncthreads();
-    for (int32_t v = threadIdx.x; v < npad; v += blockDim.x) s_len[v] = v < n ? unit_tokens(p, s_ntok, s_lr, v) : -1;
+    // Tokens of unit u = ((b S + s) unit_tokens + qtok) n_chunks + c: its chunk's share of the stripe, 0 when the row
+    // has no query token qtok (no attention work).
+    const int32_t ut = p.unit_tokens, nch = p.n_chunks, ch = p.chunk_tokens;
+    for_each_plan_pair(p.q_row_start, p.ctx_len, p.B, p.S, p.T, p.max_row_tokens, p.ctx_cap, p.stripe_begin, p.P,
+                       p.geo.interleave, [&](int32_t bs, int32_t ntok, int32_t lr) {
+                           for (int32_t qtok = 0; qtok < ut; ++qtok)
+                               for (int32_t c = 0; c < nch; ++c)
+                                   s_len[(bs * ut + qtok) * nch + c] = qtok < ntok ? max(0, min(lr - c * ch, ch)) : 0;
+                       });
+    for (int32_t v = n + int32_t(threadIdx.x); v < npad; v += blockDim.x) s_len[v] = -1;
     __syncthreads();
     rank_longest_first(s_len, s_part, n, p.order);
 }
