@@ -545,10 +545,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
 #pragma unroll
             for (int e = 0; e < 8; ++e) sv[rb][e] = sacc[rb][e >> 2][e & 3];
             if (mask) {
+                // key j = tile0 + off + 4 c4 with off = 16 (e / 4) + e % 4: the lane's part 4 c4 is compared with
+                // wave-uniform bounds, so unmasked tiles carry no per-key index arithmetic
+                const int32_t kleft = nkeys - tile0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int32_t j = tile0 + 16 * (e >> 2) + 4 * c4 + (e & 3);
-                    if (j >= nkeys || (MODE == kFromOwn && j > qtok[rb])) sv[rb][e] = neg_inf();
+                    const int32_t off = 16 * (e >> 2) + (e & 3);
+                    if (4 * c4 >= kleft - off || (MODE == kFromOwn && 4 * c4 - qtok[rb] > -(tile0 + off)))
+                        sv[rb][e] = neg_inf();
                 }
             }
         }
