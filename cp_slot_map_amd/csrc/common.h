@@ -217,7 +217,8 @@ __device__ __forceinline__ void for_each_plan_pair(const int32_t* row_start, con
 }
 
 // Plans of the unit kernels: order[rank] = i for the n items whose keys (work estimates) sit in LDS, rank = the number
-// of items with a larger key, or an equal key and a smaller index (longest first, ties in index order). s_key holds
+// of items with a larger key, or an equal key and a smaller index (longest first, ties in index order); an item whose
+// key is negative (no work at all) is entered as -1, so its workgroup returns without looking at anything else. s_key holds
 // rank_padded(n) entries, those past n set to -1 (below every real key). A workgroup of 256 threads ranks kRankItems
 // items: kRankThreads threads share an item, each comparing it with its part of the keys, four at a time, and the
 // parts' counts are summed through s_part (256 entries). Many small workgroups spread the n^2 comparisons over the
@@ -253,7 +254,7 @@ __device__ __forceinline__ void rank_longest_first(const int32_t* s_key, int32_t
         int32_t r = 0;
 #pragma unroll
         for (int k = 0; k < kRankThreads; ++k) r += s_part[k * kRankItems + tid];
-        order[r] = u;
+        order[r] = s_key[u] < 0 ? -1 : u;
     }
 }
 

@@ -340,6 +340,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
     const int32_t g = v % p.Hkv;
     v /= p.Hkv;
     if (MODE == kFromPool && p.order) v = ((const_i32_ptr)p.order)[v];
+    if (v < 0) return;                                      // a block past its row's rows (plan key -1)
     const int32_t qb = MODE == kFromOwn ? p.n_qblocks - 1 - v % p.n_qblocks : v % p.n_qblocks;
     v /= p.n_qblocks;
     const int32_t s = v % p.S;
