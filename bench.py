@@ -275,9 +275,13 @@ def summarize(wl, m, traffic=None):
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     part_avg = float(np.mean(m["part_ms"]))
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
-    # Algorithmic flops of the partial: every (query token, context token) pair costs Hq * 2 * (D + Dv).
-    flops = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64)) * wl.num_q_heads * 2 * (
-        wl.head_dim + wl.head_dim_v)
+    # Algorithmic flops of the timed calls: every (query token, context token) pair costs Hq * 2 * (D + Dv), and so does
+    # every (query token, visible in-step key) pair of the own-token call when the step has one (n (n + 1) / 2 a row).
+    pairs = float(wl.ctx_len.astype(np.int64) @ wl.new_len.astype(np.int64))
+    if wl.own_token:
+        n = wl.new_len.astype(np.int64)
+        pairs += float((n * (n + 1) // 2).sum())
+    flops = pairs * wl.num_q_heads * 2 * (wl.head_dim + wl.head_dim_v)
     kernel = KERNEL_NAMES.get(wl.name, "cp_paged_attn_partial")
     if wl.kind == "mla" and wl.kv_dtype == "fp8":
         kernel = "cp_paged_attn_partial (mla_plan_kernel + mla_decode_kernel over the fp8 latent pool)"
