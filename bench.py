@@ -315,7 +315,7 @@ def summarize(wl, m, traffic=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs the whole striped path on a single MI355X "
+        print(f"bench.py measures one GPU only: the whole striped path runs on a single MI355X "
               f"(all P stripes resident); --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
     import numpy as np

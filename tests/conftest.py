@@ -33,7 +33,7 @@ def pytest_collection_modifyitems(config, items):
 def pytest_terminal_summary(terminalreporter):
     """Print the worst GPU-vs-oracle errors each parity test recorded (tests/gpu_helpers.py), so that the session's
     output keeps the margins to the bounds: one line per test function (worst over its parameters), then the overall
-    worst. The per-case figures also go to gpurun_out/parity_margins.json when that folder can be written."""
+    worst. The per-case figures also go to parity_margins.json in the run's output folder when it can be written."""
     try:
         from tests.gpu_helpers import MARGINS
     except Exception:
