@@ -591,7 +591,10 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
         }
 
         // Values: 8 output tiles of 16 dims per row block, each B operand from two transposed reads, widened from bf16
-        // to fp16 in registers.
+        // to fp16 in registers. The wave issues them at raised priority: with two waves a SIMD, the other wave's
+        // softmax then fills the gaps between these MFMAs instead of delaying them (measured 0.8% faster on bf16 pools,
+        // 1.5% on fp8 pools).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + vofs[0][db]));
@@ -604,6 +607,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void gqa_extend_kernel(const ExtParams
                                                                   0, 0, 0);
         }
         sched_pipeline<16, 1, 8>();
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // One iteration with buffer bb (compile time): wait for tile kt, issue the loads of tile kt + kAhead into buffer
